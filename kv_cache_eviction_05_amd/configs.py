@@ -1,0 +1,101 @@
+"""Workload shapes of the eviction round.
+
+Five synthetic workloads, each a single-GPU share at its real shape:
+
+  tiny      1 layer x 2 KV heads, D=128, n=1088 (K=1024 + r=64), prot=32,
+            per-head random draw, contiguous storage.
+  batch     128 requests x 36 layers x 8 KV heads, D=128, n=1088, K=1024,
+            prot=128, per-head random draw, contiguous storage (decode-time
+            round over a full batch).
+  paged     64 requests x 36 layers x 8 KV heads, D=128, n=2112, K=2048,
+            prot=1024, 16-token pages behind seed-shuffled page tables,
+            per-head draw ("paged") or one draw per layer ("paged_shared"),
+            compacted into freshly allocated pages.
+  global    16 attention layers x 4 KV heads, D=256, n=32768, prot=256, p=0.25:
+            weighted GDN-signal scores over the up-to-six preceding GDN layers
+            x 48 heads, then one model-wide top-B (GateSight-shaped).
+  longgen   128 x 36 x 8, D=128, K=3072, r=64, prot=557: 30 consecutive rounds,
+            64 fresh tokens appended between rounds, rescored every round.
+
+Budget and trigger follow the Random Attention blog summary (persistent budget
+K, recent buffer r=64, evict when the buffer is full) and the GateSight
+problem statement (B = L*H*round(p*(n-prot)), prot <= 256).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+
+
+@dataclass(frozen=True)
+class RoundConfig:
+    name: str
+    R: int            # requests
+    L: int            # attention layers
+    H: int            # KV heads per layer
+    D: int            # head dim (bf16 elements per row)
+    K: int            # kept entries per head (top-K mode, prompt included)
+    r: int            # recent buffer; a round fires at n = K + r
+    prot: int         # protected prompt prefix
+    layout: str = "contig"     # "contig" or "paged"
+    page_size: int = 16
+    scorer: str = "random"     # "random" or "weighted"
+    select: str = "topk"       # "topk" or "global"
+    shared: bool = False       # one draw per (request, layer), applied to all heads
+    p: float = 0.0             # kept fraction for the global budget
+    rounds: int = 1
+    seed: int = 0
+    G: int = 48                # GDN layers (weighted scorer)
+    Hg: int = 48               # GDN heads per layer
+    win_width: int = 6         # GDN layers read by one attention layer
+    n_override: int = 0        # n when it is not K + r (global mode)
+
+    @property
+    def n(self) -> int:
+        return self.n_override if self.n_override else self.K + self.r
+
+    @property
+    def groups(self) -> int:
+        return self.R * self.L
+
+    @property
+    def lists(self) -> int:
+        """Number of score/index lists: one per (request, layer, head), or per layer if shared."""
+        return self.groups if self.shared else self.groups * self.H
+
+    @property
+    def row_bytes(self) -> int:
+        return self.D * 2
+
+    def small(self, **kw) -> "RoundConfig":
+        return replace(self, **kw)
+
+
+def gdn_windows(L: int, G: int, width: int = 6):
+    """GDN layers read by each attention layer, as (begin, count) lists.
+
+    Hybrid stack of 64 layers with full attention at every fourth layer
+    (GateSight, model paragraph): attention layer a follows GDN layers
+    3a-3 .. 3a+2 (GDN numbering), i.e. the up-to-six preceding GDN layers, and
+    only three for the first attention layer (Sec. 4.1).  ``width`` is the
+    window size; the begin is clipped at 0.
+    """
+    per = G // L if L else 0  # GDN layers between consecutive attention layers
+    begins, counts = [], []
+    for a in range(L):
+        end = per * (a + 1)
+        b = max(0, end - width)
+        begins.append(b)
+        counts.append(end - b)
+    return begins, counts
+
+
+TINY = RoundConfig("tiny", R=1, L=1, H=2, D=128, K=1024, r=64, prot=32)
+BATCH = RoundConfig("batch", R=128, L=36, H=8, D=128, K=1024, r=64, prot=128)
+PAGED = RoundConfig("paged", R=64, L=36, H=8, D=128, K=2048, r=64, prot=1024, layout="paged")
+PAGED_SHARED = replace(PAGED, name="paged_shared", shared=True)
+GLOBAL = RoundConfig("global", R=1, L=16, H=4, D=256, K=0, r=0, prot=256, scorer="weighted",
+                     select="global", p=0.25, n_override=32768)
+LONGGEN = RoundConfig("longgen", R=128, L=36, H=8, D=128, K=3072, r=64, prot=557, rounds=30)
+
+ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN)}

@@ -1,0 +1,196 @@
+"""CPU oracle for the KV-cache eviction round (ctypes wrapper over oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and never imports it; the two meet only through the seeded
+input generators, which hold none of the method's arithmetic.
+
+Every function states the passage it follows; the C++ file carries the
+definitions.  Arrays are numpy; bf16 rows are handled as ``uint16`` bytes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_LIB = None
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
+_u64 = ctypes.c_uint64
+_dbl = ctypes.c_double
+_p = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.cpp with g++ into liboracle.so (no GPU code involved)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_philox4x64_10.argtypes = [_p, _p, _p]
+        lib.oracle_philox4x64_10.restype = None
+        lib.oracle_random_draw.argtypes = [_u64, _u64, _u64, _u64, _u64, _i64]
+        lib.oracle_random_draw.restype = ctypes.c_float
+        lib.oracle_score_random.argtypes = [_p, _i64, _i32, _i32, _i32, _i32, _u64, _u32, _i32,
+                                            _i64, _i64]
+        lib.oracle_score_random.restype = None
+        lib.oracle_score_weighted.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i64, _p, _i32, _p,
+                                              _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+        lib.oracle_score_weighted.restype = None
+        lib.oracle_select_topk.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _i32]
+        lib.oracle_select_topk.restype = None
+        lib.oracle_budget.argtypes = [_i64, _i32, _i32, _dbl]
+        lib.oracle_budget.restype = _i64
+        lib.oracle_select_global.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i32, _i32, _dbl]
+        lib.oracle_select_global.restype = _i64
+        lib.oracle_compact.argtypes = [_i32, _p, _p, _i64, _p, _i64,
+                                       _i32, _p, _p, _i64, _p, _i64,
+                                       _i32, _i32, _i32, _p, _i64, _p, _i32, _i64, _i64, _i32]
+        lib.oracle_compact.restype = None
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------------------
+# Random Attention scores (blog summary, Algorithm 1; shared-draw paragraph)
+# ---------------------------------------------------------------------------
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """Philox4x64-10 block (Salmon et al., SC 2011) of a 4-word counter, 2-word key."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint64))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64))
+    out = np.zeros(4, dtype=np.uint64)
+    _lib().oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def random_draw(seed, request, layer, head, round_id, i) -> float:
+    """Score of slot i: top 24 bits of Philox word i%4 at counter (i//4, head, layer, req<<32|round)."""
+    return float(_lib().oracle_random_draw(seed, request, layer, head, round_id, i))
+
+
+def score_random(L, H, n, prot, seed, round_id, shared_draw, list_begin, list_end,
+                 out: np.ndarray | None = None) -> np.ndarray:
+    """Scores of lists [list_begin, list_end) as float32 [lists][n]; slots < prot are +inf."""
+    rows = list_end - list_begin
+    if out is None:
+        out = np.empty((rows, n), dtype=np.float32)
+    _lib().oracle_score_random(_ptr(out), out.shape[1], L, H, n, prot, seed, round_id,
+                               1 if shared_draw else 0, list_begin, list_end)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# GateSight-style weighted score (Sec. 4.1 window; log effective write)
+# ---------------------------------------------------------------------------
+
+def score_weighted(beta: np.ndarray, vnorm: np.ndarray, w: np.ndarray, win_begin, win_count,
+                   prot: int, t_begin: int = 0, t_end: int | None = None) -> np.ndarray:
+    """Weighted scores float32 [L*H][n] from planar signals [G][n][Hg] and weights [L][H][S][Hg]."""
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    vnorm = np.ascontiguousarray(vnorm, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    G, n, Hg = beta.shape
+    L, H, S, Hg2 = w.shape
+    assert Hg2 == Hg and vnorm.shape == beta.shape
+    wb = np.ascontiguousarray(np.asarray(win_begin, dtype=np.int32))
+    wc = np.ascontiguousarray(np.asarray(win_count, dtype=np.int32))
+    assert wb.shape == (L,) and wc.shape == (L,)
+    assert np.all(wc <= S) and np.all(wb >= 0) and np.all(wb + wc <= G)
+    if t_end is None:
+        t_end = n
+    out = np.full((L * H, n), np.nan, dtype=np.float32)
+    _lib().oracle_score_weighted(_ptr(out), n, _ptr(beta), _ptr(vnorm), n * Hg, Hg, 1, _ptr(w),
+                                 S, _ptr(wb), _ptr(wc), L, H, Hg, n, prot, t_begin, t_end)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Selection (Algorithm 1 top-K; GateSight budget B and KVzip-style global top-B)
+# ---------------------------------------------------------------------------
+
+def select_topk(scores: np.ndarray, K: int, prot: int) -> np.ndarray:
+    """Ascending kept indices int32 [lists][K]: prompt plus the K-prot best other slots."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    lists, n = scores.shape
+    assert 0 <= prot <= K <= n
+    kept = np.zeros((lists, max(K, 1)), dtype=np.int32)
+    _lib().oracle_select_topk(_ptr(kept), kept.shape[1], _ptr(scores), n, lists, n, K, prot)
+    return kept[:, :K]
+
+
+def budget(num_lists: int, n: int, prot: int, p: float) -> int:
+    """B = num_lists * round(p*(n-prot)), ties to even."""
+    return int(_lib().oracle_budget(num_lists, n, prot, p))
+
+
+def select_global(scores: np.ndarray, prot: int, p: float):
+    """Global top-B: returns (kept int32 [lists][n] with -1 padding, counts int32 [lists], B)."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    lists, n = scores.shape
+    kept = np.full((lists, n), -1, dtype=np.int32)
+    counts = np.zeros(lists, dtype=np.int32)
+    B = _lib().oracle_select_global(_ptr(kept), n, _ptr(counts), _ptr(scores), n, lists, n,
+                                    prot, p)
+    return kept, counts, int(B)
+
+
+# ---------------------------------------------------------------------------
+# Chronological compaction (blog summary: per-KV-head physical eviction with
+# chronological compaction; GateSight Sec. 4.3: kept entries to the front of
+# the layer's pages)
+# ---------------------------------------------------------------------------
+
+def compact(src: dict, k_src: np.ndarray, v_src: np.ndarray, dst: dict, k_dst: np.ndarray,
+            v_dst: np.ndarray, kept: np.ndarray, K: int, D: int, H: int,
+            group_begin: int, group_end: int, ipg: int, kept_count: np.ndarray | None = None,
+            page_size: int = 16) -> None:
+    """Copy kept rows src -> dst in place on the numpy arrays.
+
+    ``src``/``dst`` describe a store: ``{"paged": bool, "list_stride": int}`` or
+    ``{"paged": True, "page_table": int32 [groups][pt_ld]}``.  K/V arrays are
+    uint16 views of bf16 data, flat or shaped.
+    """
+    kept = np.ascontiguousarray(kept, dtype=np.int32)
+    kc = None if kept_count is None else np.ascontiguousarray(kept_count, dtype=np.int32)
+
+    def desc(d):
+        if d.get("paged"):
+            pt = np.ascontiguousarray(d["page_table"], dtype=np.int32)
+            return 1, 0, pt, pt.shape[1]
+        return 0, int(d["list_stride"]), None, 0
+
+    sp, sls, spt, sld = desc(src)
+    dp, dls, dpt, dld = desc(dst)
+    for a in (k_src, v_src, k_dst, v_dst):
+        assert a.dtype == np.uint16 and a.flags["C_CONTIGUOUS"]
+    _lib().oracle_compact(sp, _ptr(k_src), _ptr(v_src), sls, _ptr(spt), sld,
+                          dp, _ptr(k_dst), _ptr(v_dst), dls, _ptr(dpt), dld,
+                          D, H, page_size, _ptr(kept), kept.shape[1], _ptr(kc), K,
+                          group_begin, group_end, ipg)

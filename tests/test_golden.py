@@ -1,0 +1,67 @@
+"""Golden fixtures: numbers the pages print, and frozen oracle draws.
+
+page_facts.json holds values printed on the pages (each with its citation);
+the workload definitions and the oracle must reproduce them.  random_kat.json
+holds oracle draws written by tests/golden/make_random_kat.py (which calls only
+the oracle); it freezes the draw's definition against accidental change.
+"""
+
+import json
+import os
+
+import numpy as np
+
+import oracle
+from kv_cache_eviction_05_amd import configs
+
+HERE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load(name):
+    with open(os.path.join(HERE, name)) as f:
+        return json.load(f)
+
+
+def test_page_facts():
+    f = load("page_facts.json")
+    s = f["kib_per_token"]["shape"]
+    bytes_per_token = s["layers"] * s["kv_heads"] * s["k_and_v"] * s["head_dim"] * s["bytes_per_value"]
+    assert bytes_per_token == f["kib_per_token"]["value"] * 1024
+    g = configs.GLOBAL
+    # the global workload carries the page's model shape: 16 layers x 4 KV heads x D=256
+    assert (g.L, g.H, g.D) == (s["layers"], s["kv_heads"], s["head_dim"])
+    assert g.prot <= f["max_protected_prefix"]["value"]
+
+    e = f["estimator_inputs"]
+    begins, counts = configs.gdn_windows(g.L, g.G, g.win_width)
+    assert max(counts) == e["window_layers"] and counts[0] == e["first_window_layers"]
+    per_head = e["gdn_heads"] * e["signals_per_head"]
+    assert counts[1] * per_head + e["age_features"] == e["value"]
+    assert counts[0] * per_head + e["age_features"] == e["first_layer"]
+    assert counts[1] * e["gdn_heads"] == f["window_cells"]["value"]
+    p = f["estimator_params_millions"]
+    params = sum(g.H * ((c * per_head + e["age_features"]) * p["hidden"] + 2 * p["hidden"] + 1)
+                 for c in counts)
+    assert g.L * g.H == p["mlps"] and round(params / 1e6, 1) == p["value"]
+
+    sv = f["survival_per_round"]
+    assert round(sv["K"] / (sv["K"] + sv["r"]), 2) == sv["value"]
+    assert configs.BATCH.r == configs.LONGGEN.r == f["recent_buffer"]["value"]
+
+    ev = f["compression_events"]
+    events = ev["requests"] * (ev["generation"] - ev["K"]) // ev["every_tokens"]
+    # the page says "about 62k"; 128 * (32768 - 2048) / 64 = 61,440 is within 1%
+    assert abs(events / 1000 - ev["value_thousands"]) / ev["value_thousands"] < 0.02
+
+
+def test_random_kat():
+    for c in load("random_kat.json")["cases"]:
+        u = oracle.random_draw(c["seed"], c["request"], c["layer"], c["head"], c["round"], c["i"])
+        assert u == c["u24"] / float(1 << 24), c
+        assert 0.0 <= u < 1.0
+
+
+def test_global_budget_of_workload():
+    g = configs.GLOBAL
+    B = oracle.budget(g.L * g.H, g.n, g.prot, g.p)
+    assert B == g.L * g.H * int(np.round(g.p * (g.n - g.prot))) == 520192
