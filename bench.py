@@ -1,0 +1,313 @@
+"""Benchmark of the eviction round on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workloads batch,paged,...] [--no-cpu-baseline]
+
+A step is one whole eviction round (score -> pin + select -> compact) over one
+batch of synthetic inputs resident in HBM.  The headline workload is the
+decode-time batch round (128 requests x 36 layers x 8 KV heads, D=128,
+n=1088, K=1024, prot=128, contiguous storage, per-head random draw).  Other
+workloads, if requested, are reported under "workloads".  Prints ONE JSON line.
+
+Timing: W untimed rounds, then exactly K rounds between two synchronisations;
+HIP events on the launch stream bracket every kernel launch of the round, so
+each step of the round gets its own average duration.  The roofline entry
+prices the dominant kernel (the K/V gather) at its algorithmic bytes: the
+kept K and V rows, each read once and written once.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "eviction rounds/sec and achieved HBM GB/s (fraction of peak) per MI355X"
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "compact_batch_traffic.json")
+COMPACT_SRC = os.path.join(HERE, "kv_cache_eviction_05_amd", "csrc", "compact.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="batch",
+                    help="comma list of batch,paged,paged_shared,global,longgen (or 'all')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for PMC scaling)")
+    return ap.parse_args()
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def describe(cfg) -> str:
+    layout = "paged 16-token pages" if cfg.layout == "paged" else "contiguous"
+    if cfg.select == "global":
+        return (f"{cfg.name}: {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, n={cfg.n}, "
+                f"prot={cfg.prot}, p={cfg.p}, weighted GDN score over 48 GDN layers x 48 heads, "
+                f"global top-B, {layout}")
+    draw = "shared draw per layer" if cfg.shared else "per-head random draw"
+    return (f"{cfg.name}: {cfg.R} requests x {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, "
+            f"n={cfg.n}, K={cfg.K}, prot={cfg.prot}, {layout}, {draw}"
+            + (f", {cfg.rounds} rounds with r={cfg.r} appended" if cfg.rounds > 1 else ""))
+
+
+class Timer:
+    """HIP events on the launch stream around each step of the round."""
+
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.marks = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append(e)
+
+    def per_step_ms(self, steps):
+        """Average duration of each named interval over `steps` rounds."""
+        k = len(self.names)
+        tot = [0.0] * k
+        for s in range(steps):
+            base = s * (k + 1)
+            for i in range(k):
+                tot[i] += self.marks[base + i].elapsed_time(self.marks[base + i + 1])
+        return {n: t / steps for n, t in zip(self.names, tot)}
+
+
+def time_workload(torch, rounds, cfg, steps, warmup):
+    st = rounds.make_state(cfg, "cuda")
+    torch.cuda.synchronize()
+    round_id = 0
+    if cfg.rounds > 1:
+        # repeated rounds: each step is one round of the persistent-budget loop; the
+        # append of r fresh tokens between rounds is input synthesis and stays untimed
+        for _ in range(warmup):
+            rounds.run_round(st, round_id)
+            rounds.append_tokens(st, round_id)
+            rounds.swap(st)
+            round_id += 1
+        torch.cuda.synchronize()
+        timer = Timer(torch, ["score", "select", "compact"])
+        total_ms = 0.0
+        for _ in range(steps):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            timer.mark()
+            rounds.score(st, round_id)
+            timer.mark()
+            rounds.select(st)
+            timer.mark()
+            rounds.compact(st)
+            timer.mark()
+            t1.record()
+            st.applied_rounds += 1
+            rounds.append_tokens(st, round_id)
+            rounds.swap(st)
+            round_id += 1
+            torch.cuda.synchronize()
+            total_ms += t0.elapsed_time(t1)
+        ms_per = total_ms / steps
+    else:
+        for _ in range(warmup):
+            rounds.run_round(st, 0)
+        torch.cuda.synchronize()
+        timer = Timer(torch, ["score", "select", "compact"])
+        t_start = time.perf_counter()
+        for s in range(steps):
+            timer.mark()
+            rounds.score(st, s)
+            timer.mark()
+            rounds.select(st)
+            timer.mark()
+            rounds.compact(st)
+            timer.mark()
+            st.applied_rounds += 1
+        torch.cuda.synchronize()
+        ms_per = (time.perf_counter() - t_start) * 1e3 / steps
+    kern = timer.per_step_ms(steps)
+    kv_bytes = st.kv_bytes_moved()
+    errors = int(st.errors.item())
+    out = {"state": st, "ms_per_step": ms_per, "kernels_ms": kern, "kv_bytes": kv_bytes,
+           "errors": errors, "applied_rounds": st.applied_rounds - warmup,
+           "budget": st.budget}
+    return out
+
+
+def traffic_for(kv_bytes):
+    """Measured HBM bytes per launch of the gather, if the counters match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash(COMPACT_SRC):
+        return None  # the kernel changed since the counters were taken
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(torch, cfg, st, seconds):
+    """The oracle timed on the host cores over a bounded sample of the same workload."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    req = max(1, min(cfg.R, 16))
+    lists = req * cfg.L * cfg.H
+    ks = st.k_src[:lists].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    vs = st.v_src[:lists].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    kd = np.zeros((lists, cfg.K, cfg.D), np.uint16)
+    vd = np.zeros_like(kd)
+    groups = lists // cfg.H
+    bounds = [groups * t // threads for t in range(threads + 1)]
+
+    def part(t):
+        g0, g1 = bounds[t], bounds[t + 1]
+        if g1 <= g0:
+            return
+        l0, l1 = g0 * cfg.H, g1 * cfg.H
+        s = oracle.score_random(cfg.L, cfg.H, cfg.n, cfg.prot, cfg.seed, 0, False, l0, l1)
+        kept = oracle.select_topk(s, cfg.K, cfg.prot)
+        # the slices [l0, l1) are whole groups of H lists, addressed from their own base
+        oracle.compact({"list_stride": cfg.n * cfg.D}, ks[l0:l1], vs[l0:l1],
+                       {"list_stride": cfg.K * cfg.D}, kd[l0:l1], vd[l0:l1], kept, cfg.K, cfg.D,
+                       cfg.H, 0, g1 - g0, ipg=cfg.H)
+
+    reps = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(part, range(threads)))
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    frac = lists / cfg.lists
+    return {"value": reps * frac / el, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{req} of {cfg.R} requests ({lists} of {cfg.lists} lists: score, select, "
+                      f"compact) x {reps} repetitions in {el:.1f} s on {threads} threads"}
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of 4 GiB: reference for scaling FETCH/WRITE counters."""
+    n = 4 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(every list is independent, so throughput at N GPUs is N x the one-GPU value "
+              f"under request sharding)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    from kv_cache_eviction_05_amd import binding, configs, rounds
+
+    binding.load()
+    names = [w for w in args.workloads.split(",") if w]
+    if names == ["all"]:
+        names = ["batch", "paged", "paged_shared", "global", "longgen"]
+    if "batch" not in names:
+        names = ["batch"] + names
+    head = None
+    extra = {}
+    for name in names:
+        cfg = configs.ALL[name]
+        print(f"# timing {name}", file=sys.stderr, flush=True)
+        steps = args.steps if cfg.rounds == 1 else min(args.steps, cfg.rounds)
+        r = time_workload(torch, rounds, cfg, steps, args.warmup)
+        comp_ms = r["kernels_ms"]["compact"]
+        achieved = r["kv_bytes"] / (comp_ms * 1e-3) / 1e9
+        entry = {
+            "workload": describe(cfg),
+            "rounds_per_s": 1e3 / r["ms_per_step"],
+            "ms_per_round": r["ms_per_step"],
+            "kernel_ms": {k: round(v, 4) for k, v in r["kernels_ms"].items()},
+            "kv_bytes_per_round": r["kv_bytes"],
+            "kv_gbps_round": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+            "compact_gbps": achieved,
+            "compact_frac_of_peak": achieved / PEAK_HBM_GBPS,
+            "applied_rounds": r["applied_rounds"],
+            "bad_rows": r["errors"],
+        }
+        if cfg.select == "global":
+            entry["budget"] = r["budget"]
+        if name == "batch":
+            head = (cfg, r, entry)
+            if not args.no_cpu_baseline:
+                print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+                head[2]["cpu"] = cpu_baseline(torch, cfg, r["state"], args.cpu_seconds)
+        else:
+            extra[name] = entry
+        del r["state"]
+        r.clear()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    cfg, r, e = head
+    comp_ms = e["kernel_ms"]["compact"]
+    line = {
+        "metric": METRIC,
+        "value": e["rounds_per_s"],
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": e["ms_per_round"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": e["workload"], "lists": cfg.lists, "n": cfg.n, "K": cfg.K,
+                   "prot": cfg.prot, "head_dim": cfg.D},
+        "kv_gbps": e["kv_gbps_round"],
+        "kernel_ms": e["kernel_ms"],
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "compact (K/V gather)",
+            "achieved": e["compact_gbps"],
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": e["compact_gbps"] / PEAK_HBM_GBPS,
+            "traffic": traffic_for(e["kv_bytes_per_round"]),
+            "algorithmic_bytes": e["kv_bytes_per_round"],
+        },
+        "cpu_baseline": e.get("cpu"),
+        "bad_rows": e["bad_rows"],
+    }
+    if extra:
+        line["workloads"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

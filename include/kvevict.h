@@ -1,0 +1,202 @@
+/*
+ * kvevict.h -- C ABI of the MI355X (gfx950) KV-cache eviction round.
+ *
+ * One eviction round, run for every (layer, KV head) list of a batch:
+ *   1. score every cache entry            kvevict_score_random / kvevict_score_weighted
+ *   2. pin the protected prompt prefix    (part of every scorer and selector)
+ *   3. select the entries to keep         kvevict_select_topk / kvevict_select_global
+ *   4. compact the kept bf16 K/V rows     kvevict_compact
+ *
+ * Sources of the definitions:
+ *   [RA]  "Random Attention" blog summary (sungsoo.github.io, 2026-09-05):
+ *         Algorithm 1 (random score, prompt = +inf, top-K per KV head, return
+ *         the keep set); persistent budget K and recent buffer r = 64; the
+ *         shared draw (one keep set for all heads); the engine's per-KV-head
+ *         physical eviction with chronological compaction.
+ *   [GS]  "GateSight" (signal-papers 2610.14754): problem statement (model-wide
+ *         budget B = L*H*round(p*(n-prot)) exclusive of a protected prefix);
+ *         Sec. 4.1 (signals of the up-to-six preceding GDN layers; log
+ *         effective write log(beta*|v|)); Sec. 4.3 and Appendix G (kept
+ *         entries moved to the front of each layer's pages); baselines
+ *         paragraph (KVzip's global top-B over (layer, head, token) scores).
+ *
+ * Readings where the pages leave a step open (each function repeats its own):
+ *   - rand: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011), key
+ *     (seed, 0), counter (i/4, head, layer, request*2^32 + round); the score
+ *     of slot i is the top 24 bits of output word i%4 times 2^-24, in [0, 1).
+ *   - ranking: score descending; NaN ranks as -inf; -0 equals +0; among equal
+ *     scores the lower position wins (global: the lower list*n + i).
+ *   - round(): binary64 product, round half to even.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library allocates nothing, frees nothing and keeps no state between
+ *     calls.  Host arrays are read during the call only.
+ *   - All work is enqueued on `stream` (NULL = the default stream); nothing is
+ *     synchronised; outputs are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error status nothing has been enqueued and no output is touched.
+ *     KVEVICT_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - Empty batches (zero lists or groups) are valid and enqueue nothing.
+ */
+#ifndef KVEVICT_H
+#define KVEVICT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVEVICT_ABI_VERSION 1
+
+typedef enum kvevict_status {
+  KVEVICT_OK = 0,
+  KVEVICT_ERR_INVALID_ARG = 1, /* a size, count or pointer is out of its documented range */
+  KVEVICT_ERR_ALIGNMENT = 2,   /* a K/V base or stride is not 16-byte aligned */
+  KVEVICT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  KVEVICT_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement */
+  KVEVICT_ERR_HIP = 5          /* the HIP runtime reported an error */
+} kvevict_status;
+
+typedef enum kvevict_layout {
+  KVEVICT_LAYOUT_CONTIG = 0, /* one dense [capacity][D] slab per (group, head) list */
+  KVEVICT_LAYOUT_PAGED = 1   /* a page pool [pages][page_size][H][D] and a page table */
+} kvevict_layout;
+
+/*
+ * Describes one K or V store (K and V use the same description).  A group is
+ * one (request, layer); a list is one (group, KV head), list = group*H + head.
+ * Rows are D bf16 elements (2*D bytes, moved verbatim).
+ *
+ *   CONTIG: row t of list l at element  l*list_stride + t*D,  t < capacity.
+ *   PAGED:  row t of (group g, head h) at element
+ *             ((page_table[g*pt_ld + t/page_size]*page_size + t%page_size)*H + h)*D,
+ *           t < pt_ld*page_size, page ids in [0, capacity).
+ * [GS] Sec. 4.3: one block table per attention layer over a shared pool.
+ */
+typedef struct kvevict_kv_desc {
+  int32_t layout;            /* kvevict_layout */
+  int32_t head_dim;          /* D: elements per row, multiple of 8 (16-byte rows) */
+  int32_t heads;             /* H: KV heads per group */
+  int32_t page_size;         /* PAGED: tokens per page (>= 1); ignored for CONTIG */
+  int64_t capacity;          /* CONTIG: rows per list; PAGED: pages in the pool */
+  int64_t list_stride;       /* CONTIG: elements between lists, >= capacity*D, multiple of 8 */
+  const int32_t* page_table; /* PAGED: device [num_groups][pt_ld] physical page ids */
+  int64_t pt_ld;             /* PAGED: page-table entries per group (>= 1) */
+} kvevict_kv_desc;
+
+/*
+ * Random Attention scores ([RA] Algorithm 1 "rand" and "prompt = +inf"; shared
+ * draw paragraph).
+ *
+ * scores  device fp32, row `list` at scores + list*ld, ld >= n.
+ *         Per-head draw: num_requests*L*H rows, list = (req*L + layer)*H + head.
+ *         Shared draw (shared_draw != 0): num_requests*L rows, list = req*L + layer,
+ *         drawn from the head-0 stream, so it equals head 0's per-head draw.
+ * Row entries i < prot are +inf; entries prot <= i < n get the Philox draw of
+ * (seed, req, layer, head, round, i) described above; entries >= n untouched.
+ * Requires 0 <= prot <= n, num_requests < 2^32, L >= 1, H >= 1.
+ */
+kvevict_status kvevict_score_random(float* scores, int64_t ld, int64_t num_requests, int32_t L,
+                                    int32_t H, int32_t n, int32_t prot, uint64_t seed,
+                                    uint32_t round, int32_t shared_draw, hipStream_t stream);
+
+/*
+ * GateSight-style weighted scores ([GS] Sec. 4.1; log effective write).
+ *
+ *   s[l][h][t] = sum_{slot < win_count[l]} sum_{j < Hg}
+ *                  w[((l*H + h)*w_slots + slot)*Hg + j] * ln(beta[e] * vnorm[e]),
+ *   e = (win_begin[l] + slot)*sig_stride_g + t*sig_stride_t + j*sig_stride_j,
+ *
+ * for prot <= t < n, written to scores[(l*H + h)*ld + t]; +inf for t < prot.
+ * Logs and the sum are taken in binary64 and rounded once to fp32.
+ * beta, vnorm  device fp32 GDN signals (write gate, write magnitude); the
+ *              planar layout [G][n][Hg] (strides n*Hg, Hg, 1) is the fast one.
+ * w            device fp32 [L][H][w_slots][Hg] fixed per-GDN-head weights.
+ * win_begin, win_count  HOST int32 [L]: the GDN layers read by attention
+ *              layer l are [win_begin[l], win_begin[l] + win_count[l]) within
+ *              [0, G); win_count[l] <= w_slots <= 64.
+ * Requires L <= 64, H >= 1, Hg >= 1, 0 <= prot <= n, ld >= n.
+ */
+kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* beta,
+                                      const float* vnorm, int64_t sig_stride_g,
+                                      int64_t sig_stride_t, int64_t sig_stride_j, const float* w,
+                                      int32_t w_slots, const int32_t* win_begin,
+                                      const int32_t* win_count, int32_t L, int32_t H, int32_t G,
+                                      int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
+
+/*
+ * Pin + per-head top-K ([RA] Algorithm 1: prompt = +inf, topk, return keep).
+ *
+ * For each of num_lists lists (row at scores + list*ld): keeps [0, prot) and
+ * the K - prot best of [prot, n) in the ranking above, and writes the K kept
+ * indices in increasing order to kept_idx[list*kept_ld + j], j < K.  The
+ * result does not depend on the scores stored at [0, prot).
+ * Requires 0 <= prot <= K <= n, ld >= n, kept_ld >= K.
+ */
+kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const float* scores,
+                                   int64_t ld, int64_t num_lists, int32_t n, int32_t K,
+                                   int32_t prot, hipStream_t stream);
+
+/*
+ * Pin + model-wide top-B ([GS] problem statement: B = L*H*round(p*(n-prot))
+ * exclusive of the protected prefix; KVzip-style global top-B).
+ *
+ * B = num_lists * round_half_even(p * (n - prot)).  Keeps [0, prot) of every
+ * list plus the B best non-prompt entries over all lists (ties: lower
+ * list*n + i), then writes kept_count[list] and the kept indices of each list
+ * in increasing order to kept_idx[list*kept_ld + j], j < kept_count[list];
+ * entries beyond the count are untouched.
+ * budget_out  optional HOST pointer receiving B.
+ * workspace   device scratch.  Two-phase protocol: with workspace == NULL the
+ *             call writes the required size to *workspace_bytes and returns
+ *             KVEVICT_OK without enqueuing anything; otherwise *workspace_bytes
+ *             must hold at least that size.  The workspace is overwritten.
+ * Requires 0 <= prot <= n, 0 <= p <= 1, ld >= n, kept_ld >= n, num_lists*n < 2^31.
+ */
+kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                     int64_t* budget_out, const float* scores, int64_t ld,
+                                     int64_t num_lists, int32_t n, int32_t prot, double p,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * Chronological compaction ([RA] per-KV-head physical eviction, chronological
+ * compaction; [GS] Sec. 4.3 kept entries to the front of the layer's pages).
+ *
+ * For every group g < num_groups, head h < H and j < count:
+ *     K_dst row (g, h, j) = K_src row (g, h, idx[j])   and the same for V,
+ * with idx = kept_idx + (g*idx_lists_per_group + (idx_lists_per_group == 1 ? 0 : h))*kept_ld
+ * and count = kept_count ? kept_count[that index list] : K.
+ * idx_lists_per_group is H (one index list per KV head) or 1 (shared draw:
+ * one list applied to every head of the group).  Out of place: source and
+ * destination must not overlap.  Destination rows >= count are untouched.
+ * src, dst     host descriptors (see kvevict_kv_desc), same D and H.
+ * k_src ...    device bf16 stores, 16-byte aligned.
+ * errors       optional device uint32 counter; each row whose index or page
+ *              id falls outside its store (or whose count is outside [0, K])
+ *              is skipped and adds 1.  May be NULL.
+ * Requires K <= dst rows per list, kept_ld >= K.
+ */
+kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,
+                               const kvevict_kv_desc* dst, void* k_dst, void* v_dst,
+                               const int32_t* kept_idx, int64_t kept_ld,
+                               const int32_t* kept_count, int32_t K, int64_t num_groups,
+                               int32_t idx_lists_per_group, uint32_t* errors,
+                               hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* kvevict_status_string(kvevict_status status);
+
+/* KVEVICT_ABI_VERSION of the built library. */
+int32_t kvevict_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVEVICT_H */

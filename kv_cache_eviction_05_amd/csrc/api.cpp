@@ -1,0 +1,191 @@
+// C ABI of the eviction round: host-side validation and dispatch.
+//
+// Every entry point checks its arguments completely before enqueuing any
+// work, so an error status means nothing was launched and no output touched.
+// The library holds no state and allocates no memory.
+#include <hip/hip_runtime.h>
+
+#include <cfenv>
+#include <cmath>
+#include <cstdint>
+
+#include "kvevict.h"
+#include "kvevict_launch.hpp"
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+kvevict_status hip_status(hipError_t e) { return e == hipSuccess ? KVEVICT_OK : KVEVICT_ERR_HIP; }
+
+int log2_exact(int32_t v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+// Validates one store description; fills the kernel's view of it.
+kvevict_status check_store(const kvevict_kv_desc* d, const void* k, const void* v,
+                           int64_t num_groups, kvevict::StoreView* out) {
+  if (!d) return KVEVICT_ERR_INVALID_ARG;
+  if (d->head_dim <= 0 || d->heads <= 0) return KVEVICT_ERR_INVALID_ARG;
+  if (d->head_dim % 8 != 0) return KVEVICT_ERR_ALIGNMENT;
+  if (num_groups > 0 && (!k || !v)) return KVEVICT_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return KVEVICT_ERR_ALIGNMENT;
+  out->page_table = nullptr;
+  out->pt_ld = 0;
+  out->page_shift = 0;
+  out->list_stride_v = 0;
+  out->capacity = d->capacity;
+  if (d->capacity < 0) return KVEVICT_ERR_INVALID_ARG;
+  if (d->layout == KVEVICT_LAYOUT_CONTIG) {
+    out->paged = 0;
+    if (d->list_stride < d->capacity * d->head_dim) return KVEVICT_ERR_INVALID_ARG;
+    if (d->list_stride % 8 != 0) return KVEVICT_ERR_ALIGNMENT;
+    out->list_stride_v = d->list_stride / 8;
+    out->max_rows = d->capacity;
+  } else if (d->layout == KVEVICT_LAYOUT_PAGED) {
+    out->paged = 1;
+    if (d->page_size <= 0 || d->pt_ld <= 0) return KVEVICT_ERR_INVALID_ARG;
+    const int shift = log2_exact(d->page_size);
+    if (shift < 0) return KVEVICT_ERR_UNSUPPORTED;  // page sizes are powers of two
+    if (num_groups > 0 && !d->page_table) return KVEVICT_ERR_INVALID_ARG;
+    if (d->pt_ld > (kInt32Max >> shift)) return KVEVICT_ERR_INVALID_ARG;
+    out->page_shift = shift;
+    out->page_table = d->page_table;
+    out->pt_ld = d->pt_ld;
+    out->max_rows = d->pt_ld << shift;
+  } else {
+    return KVEVICT_ERR_INVALID_ARG;
+  }
+  return KVEVICT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvevict_status kvevict_score_random(float* scores, int64_t ld, int64_t num_requests, int32_t L,
+                                    int32_t H, int32_t n, int32_t prot, uint64_t seed,
+                                    uint32_t round, int32_t shared_draw, hipStream_t stream) {
+  if (num_requests < 0 || num_requests > 0xffffffffll || L < 1 || H < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_requests * L * (shared_draw ? 1 : H);
+  if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
+  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_score_random(scores, ld, lists, L, H, n, prot, seed, round,
+                                                 shared_draw != 0, stream));
+}
+
+kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* beta,
+                                      const float* vnorm, int64_t sig_stride_g,
+                                      int64_t sig_stride_t, int64_t sig_stride_j, const float* w,
+                                      int32_t w_slots, const int32_t* win_begin,
+                                      const int32_t* win_count, int32_t L, int32_t H, int32_t G,
+                                      int32_t Hg, int32_t n, int32_t prot, hipStream_t stream) {
+  if (L < 1 || L > kvevict::kMaxWeightedLayers || H < 1 || G < 1 || Hg < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
+  if (w_slots < 1 || w_slots > 64) return KVEVICT_ERR_INVALID_ARG;
+  if (!win_begin || !win_count) return KVEVICT_ERR_INVALID_ARG;
+  if (sig_stride_g < 0 || sig_stride_t < 0 || sig_stride_j < 0) return KVEVICT_ERR_INVALID_ARG;
+  kvevict::WindowTable win;
+  for (int32_t l = 0; l < L; ++l) {
+    if (win_count[l] < 0 || win_count[l] > w_slots) return KVEVICT_ERR_INVALID_ARG;
+    if (win_begin[l] < 0 || win_begin[l] + (int64_t)win_count[l] > G) return KVEVICT_ERR_INVALID_ARG;
+    win.begin[l] = win_begin[l];
+    win.count[l] = win_count[l];
+  }
+  if (n > 0 && (!scores || !beta || !vnorm || !w)) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_score_weighted(scores, ld, beta, vnorm, sig_stride_g,
+                                                   sig_stride_t, sig_stride_j, w, w_slots, win, L,
+                                                   H, Hg, n, prot, stream));
+}
+
+kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const float* scores,
+                                   int64_t ld, int64_t num_lists, int32_t n, int32_t K,
+                                   int32_t prot, hipStream_t stream) {
+  if (num_lists < 0 || num_lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (prot < 0 || K < prot || n < K || ld < n || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
+  if (num_lists > 0 && K > 0 && (!kept_idx || !scores)) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(
+      kvevict::launch_select_topk(kept_idx, kept_ld, scores, ld, num_lists, n, K, prot, stream));
+}
+
+kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                     int64_t* budget_out, const float* scores, int64_t ld,
+                                     int64_t num_lists, int32_t n, int32_t prot, double p,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  if (!workspace_bytes) return KVEVICT_ERR_INVALID_ARG;
+  if (num_lists < 0 || n < 0 || prot < 0 || prot > n || ld < n || kept_ld < n) return KVEVICT_ERR_INVALID_ARG;
+  if (!(p >= 0.0 && p <= 1.0)) return KVEVICT_ERR_INVALID_ARG;  // also rejects NaN
+  if (num_lists * (int64_t)n > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  const size_t need = kvevict::select_global_workspace_bytes(num_lists, n, prot);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return KVEVICT_OK;
+  }
+  if (*workspace_bytes < need) return KVEVICT_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return KVEVICT_ERR_ALIGNMENT;
+  if (num_lists > 0 && (!kept_idx || !kept_count || !scores)) return KVEVICT_ERR_INVALID_ARG;
+  // B = lists * round(p * (n - prot)): binary64 product, ties to even.
+  const int saved = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  const double per_list = std::nearbyint(p * (double)(n - prot));
+  std::fesetround(saved);
+  const int64_t budget = num_lists * (int64_t)per_list;
+  if (budget_out) *budget_out = budget;
+  return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
+                                                  num_lists, n, prot, budget, workspace, stream));
+}
+
+kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,
+                               const kvevict_kv_desc* dst, void* k_dst, void* v_dst,
+                               const int32_t* kept_idx, int64_t kept_ld,
+                               const int32_t* kept_count, int32_t K, int64_t num_groups,
+                               int32_t idx_lists_per_group, uint32_t* errors,
+                               hipStream_t stream) {
+  if (!src || !dst) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups < 0 || K < 0 || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
+  if (src->head_dim != dst->head_dim || src->heads != dst->heads) return KVEVICT_ERR_INVALID_ARG;
+  const int32_t H = src->heads;
+  if (idx_lists_per_group != 1 && idx_lists_per_group != H) return KVEVICT_ERR_INVALID_ARG;
+  kvevict::StoreView sv, dv;
+  kvevict_status st = check_store(src, k_src, v_src, num_groups, &sv);
+  if (st != KVEVICT_OK) return st;
+  st = check_store(dst, k_dst, v_dst, num_groups, &dv);
+  if (st != KVEVICT_OK) return st;
+  if (K > dv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
+  const int32_t D = src->head_dim;
+  if (num_groups > 0 && K > 0) {
+    // the workgroup grid must fit 31 bits
+    if (kvevict::compact_workgroups(D, K, num_groups * H) > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+    // out of place: K/V destinations must not overlap the sources
+    const uintptr_t ks = (uintptr_t)k_src, vs = (uintptr_t)v_src;
+    const uintptr_t kd = (uintptr_t)k_dst, vd = (uintptr_t)v_dst;
+    if (ks == kd || vs == vd || ks == vd || vs == kd) return KVEVICT_ERR_INVALID_ARG;
+  }
+  return hip_status(kvevict::launch_compact(sv, k_src, v_src, dv, k_dst, v_dst, D, H, kept_idx,
+                                            kept_ld, kept_count, K, num_groups,
+                                            idx_lists_per_group, errors, stream));
+}
+
+const char* kvevict_status_string(kvevict_status status) {
+  switch (status) {
+    case KVEVICT_OK: return "ok";
+    case KVEVICT_ERR_INVALID_ARG: return "invalid argument";
+    case KVEVICT_ERR_ALIGNMENT: return "misaligned K/V base, stride or head_dim";
+    case KVEVICT_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVEVICT_ERR_UNSUPPORTED: return "unsupported request";
+    case KVEVICT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t kvevict_abi_version(void) { return KVEVICT_ABI_VERSION; }
+
+}  // extern "C"

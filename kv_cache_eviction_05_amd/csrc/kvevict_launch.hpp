@@ -1,0 +1,56 @@
+// Host-side launch interfaces between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvevict {
+
+hipError_t launch_score_random(float* scores, int64_t ld, int64_t num_lists, int32_t L, int32_t H,
+                               int32_t n, int32_t prot, uint64_t seed, uint32_t round,
+                               bool shared_draw, hipStream_t stream);
+
+constexpr int kMaxWeightedLayers = 64;
+struct WindowTable {
+  int32_t begin[kMaxWeightedLayers];
+  int32_t count[kMaxWeightedLayers];
+};
+
+hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, const float* vnorm,
+                                 int64_t sg, int64_t st, int64_t sj, const float* w,
+                                 int32_t w_slots, const WindowTable& win, int32_t L, int32_t H,
+                                 int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
+
+hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, const float* scores, int64_t ld,
+                              int64_t num_lists, int32_t n, int32_t K, int32_t prot,
+                              hipStream_t stream);
+
+size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot);
+
+hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                const float* scores, int64_t ld, int64_t num_lists, int32_t n,
+                                int32_t prot, int64_t budget, void* workspace, hipStream_t stream);
+
+// One K/V store as the compaction kernels see it (units: 16-byte vectors).
+struct StoreView {
+  int32_t paged;
+  int32_t page_shift;      // log2(page_size) when paged
+  int64_t capacity;        // rows per list (contig) or pages in the pool (paged)
+  int64_t list_stride_v;   // contig: 16-byte vectors between lists
+  const int32_t* page_table;
+  int64_t pt_ld;
+  int64_t max_rows;        // rows addressable per list
+};
+
+// Workgroups launch_compact uses for `lists` index lists of up to K rows of D elements.
+int64_t compact_workgroups(int32_t D, int32_t K, int64_t lists);
+
+hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v_src,
+                          const StoreView& dst, void* k_dst, void* v_dst, int32_t D, int32_t H,
+                          const int32_t* kept_idx, int64_t kept_ld, const int32_t* kept_count,
+                          int32_t K, int64_t num_groups, int32_t ipg, uint32_t* errors,
+                          hipStream_t stream);
+
+}  // namespace kvevict

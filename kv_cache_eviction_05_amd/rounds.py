@@ -1,0 +1,177 @@
+"""Round driver: device buffers for a workload and one eviction round over them.
+
+A round is the sequence of C-ABI calls the pages describe ("Random Attention"
+blog summary, Algorithm 1 and the engine's chronological compaction; GateSight
+problem statement for the global budget):
+
+    random draw:   kvevict_score_random -> kvevict_select_topk -> kvevict_compact
+    weighted:      kvevict_score_weighted -> kvevict_select_global -> kvevict_compact
+
+Buffers are torch tensors used only as device memory; every step of the round
+runs in the HIP library.  The repeated-round driver (persistent budget K,
+recent buffer r, evict when n = K + r) ping-pongs two caches, appends r fresh
+tokens between rounds (input synthesis, outside the round) and counts the
+rounds it applied.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import binding as B
+from . import synth
+from .configs import RoundConfig, gdn_windows
+
+
+@dataclass
+class RoundState:
+    cfg: RoundConfig
+    device: torch.device
+    k_src: torch.Tensor
+    v_src: torch.Tensor
+    k_dst: torch.Tensor
+    v_dst: torch.Tensor
+    scores: torch.Tensor
+    kept: torch.Tensor
+    src_desc: B.KvDesc
+    dst_desc: B.KvDesc
+    errors: torch.Tensor
+    kept_count: torch.Tensor | None = None
+    workspace: torch.Tensor | None = None
+    workspace_bytes: int = 0
+    src_pt: torch.Tensor | None = None
+    dst_pt: torch.Tensor | None = None
+    beta: torch.Tensor | None = None
+    vnorm: torch.Tensor | None = None
+    weights: torch.Tensor | None = None
+    win_begin: list = field(default_factory=list)
+    win_count: list = field(default_factory=list)
+    n: int = 0
+    applied_rounds: int = 0
+    budget: int = 0
+
+    @property
+    def idx_lists(self) -> int:
+        return self.cfg.lists
+
+    def kv_bytes_moved(self) -> int:
+        """Read + write bytes of the kept K and V rows of one round."""
+        c = self.cfg
+        if c.select == "global":
+            rows = int(self.kept_count.sum().item())
+        else:
+            rows = c.groups * c.H * c.K
+        return rows * c.row_bytes * 2 * 2
+
+
+def _desc_pair(cfg: RoundConfig, n_src: int, cap_dst: int, device, seed: int):
+    """Allocate K/V source and destination stores and their descriptors."""
+    D, H, G = cfg.D, cfg.H, cfg.groups
+    if cfg.layout == "contig":
+        k_src = synth.kv_normal((G * H, n_src, D), seed, device)
+        v_src = synth.kv_normal((G * H, n_src, D), seed + 1000, device)
+        k_dst = torch.zeros((G * H, cap_dst, D), dtype=torch.bfloat16, device=device)
+        v_dst = torch.zeros_like(k_dst)
+        return (k_src, v_src, k_dst, v_dst, B.contig_desc(D, H, n_src),
+                B.contig_desc(D, H, cap_dst), None, None)
+    ps = cfg.page_size
+    src_pages = -(-n_src // ps)
+    dst_pages = -(-cap_dst // ps)
+    pool_src = G * src_pages
+    pool_dst = G * dst_pages
+    src_pt = synth.page_tables(G, src_pages, pool_src, synth.SEED_PAGES, device)
+    dst_pt = synth.page_tables(G, dst_pages, pool_dst, synth.SEED_PAGES + 1, device)
+    k_src = synth.kv_normal((pool_src, ps, H, D), seed, device)
+    v_src = synth.kv_normal((pool_src, ps, H, D), seed + 1000, device)
+    k_dst = torch.zeros((pool_dst, ps, H, D), dtype=torch.bfloat16, device=device)
+    v_dst = torch.zeros_like(k_dst)
+    return (k_src, v_src, k_dst, v_dst, B.paged_desc(D, H, ps, pool_src, src_pt),
+            B.paged_desc(D, H, ps, pool_dst, dst_pt), src_pt, dst_pt)
+
+
+def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) -> RoundState:
+    device = torch.device(device)
+    n = cfg.n
+    cap_dst = n if cfg.select == "global" else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
+    ks, vs, kd, vd, sd, dd, spt, dpt = _desc_pair(cfg, n, cap_dst, device, kv_seed)
+    lists = cfg.lists if cfg.select == "topk" else cfg.groups * cfg.H
+    scores = torch.empty((lists, n), dtype=torch.float32, device=device)
+    kept_cols = n if cfg.select == "global" else cfg.K
+    kept = torch.zeros((lists, kept_cols), dtype=torch.int32, device=device)
+    st = RoundState(cfg, device, ks, vs, kd, vd, scores, kept, sd, dd,
+                    torch.zeros(1, dtype=torch.int32, device=device), src_pt=spt, dst_pt=dpt, n=n)
+    if cfg.select == "global":
+        st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
+        st.workspace_bytes = B.kvevict_select_global_workspace(lists, n, cfg.prot, p=cfg.p)
+        st.workspace = torch.empty(max(st.workspace_bytes, 256), dtype=torch.uint8, device=device)
+    if cfg.scorer == "weighted":
+        st.beta, st.vnorm = synth.gdn_signals(cfg.G, n, cfg.Hg, synth.SEED_SIGNALS, device)
+        st.weights = synth.head_weights(cfg.L, cfg.H, cfg.win_width, cfg.Hg, synth.SEED_WEIGHTS,
+                                        device)
+        st.win_begin, st.win_count = gdn_windows(cfg.L, cfg.G, cfg.win_width)
+    return st
+
+
+# --- the steps of one round -------------------------------------------------------
+
+def score(st: RoundState, round_id: int, stream=None):
+    c = st.cfg
+    if c.scorer == "random":
+        B.kvevict_score_random(st.scores, st.scores.shape[1], c.R, c.L, c.H, st.n, c.prot, c.seed,
+                               round_id, c.shared, stream)
+    else:
+        n = st.n
+        B.kvevict_score_weighted(st.scores, st.scores.shape[1], st.beta, st.vnorm, n * c.Hg, c.Hg,
+                                 1, st.weights, c.win_width, st.win_begin, st.win_count, c.L, c.H,
+                                 c.G, c.Hg, n, c.prot, stream)
+
+
+def select(st: RoundState, stream=None):
+    c = st.cfg
+    lists = st.scores.shape[0]
+    if c.select == "topk":
+        B.kvevict_select_topk(st.kept, st.kept.shape[1], st.scores, st.scores.shape[1], lists, st.n,
+                              c.K, c.prot, stream)
+    else:
+        st.budget = B.kvevict_select_global(st.kept, st.kept.shape[1], st.kept_count, st.scores,
+                                            st.scores.shape[1], lists, st.n, c.prot, c.p,
+                                            st.workspace, st.workspace_bytes, stream)
+
+
+def compact(st: RoundState, stream=None):
+    c = st.cfg
+    if c.select == "topk":
+        K, count = c.K, None
+    else:
+        K, count = st.n, st.kept_count
+    ipg = 1 if c.shared else c.H
+    B.kvevict_compact(st.src_desc, st.k_src, st.v_src, st.dst_desc, st.k_dst, st.v_dst, st.kept,
+                      st.kept.shape[1], count, K, c.groups, ipg, st.errors, stream)
+
+
+def run_round(st: RoundState, round_id: int = 0, stream=None):
+    score(st, round_id, stream)
+    select(st, stream)
+    compact(st, stream)
+    st.applied_rounds += 1
+
+
+# --- repeated rounds (persistent budget K + recent buffer r) ------------------------
+
+def append_tokens(st: RoundState, round_id: int):
+    """Write r fresh N(0,1) tokens at rows [K, K+r) of the destination cache (input synthesis)."""
+    c = st.cfg
+    seed = synth.SEED_APPEND * 1_000_003 + round_id
+    st.k_dst[:, c.K:c.K + c.r].copy_(synth.kv_normal((st.k_dst.shape[0], c.r, c.D), seed,
+                                                     st.device))
+    st.v_dst[:, c.K:c.K + c.r].copy_(synth.kv_normal((st.v_dst.shape[0], c.r, c.D), seed + 7,
+                                                     st.device))
+
+
+def swap(st: RoundState):
+    """The compacted cache (K kept + r appended rows) becomes the next round's source."""
+    st.k_src, st.k_dst = st.k_dst, st.k_src
+    st.v_src, st.v_dst = st.v_dst, st.v_src
+    st.src_desc, st.dst_desc = st.dst_desc, st.src_desc
