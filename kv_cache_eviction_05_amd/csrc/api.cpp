@@ -161,9 +161,8 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
   if (K > dv.max_rows) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   const int32_t D = src->head_dim;
+  if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;  // one token row of all heads
   if (num_groups > 0 && K > 0) {
-    // the workgroup grid must fit 31 bits
-    if (kvevict::compact_workgroups(D, K, num_groups * H) > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
     // out of place: K/V destinations must not overlap the sources
     const uintptr_t ks = (uintptr_t)k_src, vs = (uintptr_t)v_src;
     const uintptr_t kd = (uintptr_t)k_dst, vd = (uintptr_t)v_dst;

@@ -4,13 +4,27 @@
 //
 //   dst row (g, h, j) = src row (g, h, idx[j])   for j < count, K and V.
 //
-// The work unit of a workgroup is (list = g*H + h, chunk of kRowsPerBlock
-// destination rows).  Rows are moved as 16-byte vectors: VPR = D/8 lanes
-// cover one row, so a wave moves 64/VPR whole rows per instruction with fully
-// coalesced 16-byte accesses on both sides.  Each thread issues kUnroll
-// K loads and kUnroll V loads before its stores, keeping 32 KiB per
-// workgroup in flight to cover HBM latency.  Source rows are streamed once
-// and destination rows written once, so both use nontemporal accesses.
+// Rows are moved as 16-byte vectors (VPR = D/8 vectors per row) with
+// nontemporal loads and stores: every source row is read once and every
+// destination row written once.  Two work decompositions, both measured on
+// MI355X against plain copies of the same bytes:
+//
+//  * list kernel (both stores contiguous).  A work item is one (list, chunk of
+//    rows), about 4 KiB of K or of V; even workgroups move the K rows of an
+//    item and odd ones the V rows.  Small items keep the set of workgroups in
+//    flight on a compact address range, which on this part is worth ~15% over
+//    large per-list chunks (6.2-6.7 TB/s vs 5.2-5.3 TB/s on 256-byte rows).
+//  * group kernel (either store paged).  A work item is one (group, a few
+//    destination tokens) over all H heads, K and V in the same thread, so a
+//    workgroup writes whole token rows of a destination page and reads the
+//    nearby source tokens of every head.  With seed-shuffled page tables the
+//    ceiling is the random 32 KiB page copy (~5.1 TB/s); this layout reaches it.
+//
+// Work items are visited by a grid-stride loop, so a one-shot grid (one item
+// per workgroup) and a grid capped below 2^32 work-items run the same code.
+// With per-list counts (kept_count, bounded only by K), a list is served by a
+// team of workgroups walking strided chunks up to its own count, so lists far
+// shorter than K do not launch mostly empty workgroups.
 //
 // Every indirect index (kept index, page id) is checked against its store
 // before it is used; a row that fails is skipped and counted in *errors.
@@ -20,9 +34,12 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kVecsPerBlock = 8192;  // 128 KiB of K (+ the same of V) per workgroup
+constexpr int kListThreads = 128;
+constexpr int kListVecs = 256;    // 16-byte vectors of K (or of V) per list item: 4 KiB
+constexpr int kGroupThreads = 256;
+constexpr int kGroupVecs = 256;   // vectors of K and of V per group item
+constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (work-items stay below 2^32)
+constexpr int32_t kVariableChunksPerPair = 4;
 
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
@@ -36,94 +53,145 @@ struct CompactArgs {
   int64_t kept_ld;
   const int32_t* kept_count;
   int32_t K, H, ipg;
-  int32_t rows_per_block, chunks_per_list;
-  int32_t vpr;  // runtime vectors per row (generic instantiation)
+  int32_t rows_per_item;  // rows of one work item
+  int32_t chunks;         // group kernel: items per group
+  int32_t team;           // list kernel: workgroup pairs per list
+  int64_t items;          // group items, or list workgroup pairs
+  int32_t vpr;                    // 16-byte vectors per row
   uint32_t* errors;
 };
 
 // Vector offset of row t of (group g, head h) in a store, or -1 if t or its
 // page id falls outside the store.
-template <int VPR>
 __device__ __forceinline__ int64_t row_vec_offset(const StoreView& s, int64_t g, int32_t h,
-                                                  int32_t H, int64_t list, int32_t t, int vpr) {
-  const int64_t vrow = VPR ? VPR : vpr;
+                                                  int32_t H, int64_t list, int32_t t,
+                                                  int32_t vpr) {
   if (t < 0 || (int64_t)t >= s.max_rows) return -1;
-  if (!s.paged) return list * s.list_stride_v + (int64_t)t * vrow;
+  if (!s.paged) return list * s.list_stride_v + (int64_t)t * vpr;
   const int32_t page = s.page_table[g * s.pt_ld + (t >> s.page_shift)];
   if (page < 0 || (int64_t)page >= s.capacity) return -1;
   const int64_t slot = ((int64_t)page << s.page_shift) + (t & ((1 << s.page_shift) - 1));
-  return (slot * H + h) * vrow;
+  return (slot * H + h) * vpr;
 }
 
-template <int VPR>
-__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
-  const int vpr = VPR ? VPR : a.vpr;
-  const int64_t list = blockIdx.x / a.chunks_per_list;
-  const int32_t chunk = blockIdx.x % a.chunks_per_list;
-  const int64_t g = list / a.H;
-  const int32_t h = (int32_t)(list % a.H);
-  const int64_t idx_list = g * a.ipg + (a.ipg == 1 ? 0 : h);
-
-  int32_t count = a.K;
-  if (a.kept_count) {
-    count = a.kept_count[idx_list];
-    if (count < 0 || count > a.K) {
-      if (chunk == 0 && threadIdx.x == 0 && a.errors) atomicAdd(a.errors, 1u);
-      count = count < 0 ? 0 : a.K;
-    }
+// Kept count of an index list, clamped to [0, K]; a count outside that range
+// is reported once (by the first item of the list).
+__device__ __forceinline__ int32_t list_count(const CompactArgs& a, int64_t idx_list,
+                                              bool report) {
+  if (!a.kept_count) return a.K;
+  const int32_t c = a.kept_count[idx_list];
+  if (c < 0 || c > a.K) {
+    if (report && a.errors) atomicAdd(a.errors, 1u);
+    return c < 0 ? 0 : a.K;
   }
-  const int32_t r0 = chunk * a.rows_per_block;
-  if (r0 >= count) return;
-  const int32_t r1 = min(count, r0 + a.rows_per_block);
-  const int32_t* idx = a.kept_idx + idx_list * a.kept_ld;
-  const int32_t nvec = (r1 - r0) * vpr;
+  return c;
+}
 
-  for (int32_t v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kUnroll) {
-    vec4u kr[kUnroll], vr[kUnroll];
-    int64_t doff[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int32_t v = v0 + u * kThreads;
-      doff[u] = -1;
-      if (v < nvec) {
+// VPR: vectors per row as a compile-time constant (0: a.vpr at run time).
+// Workgroup pair p (K: even, V: odd) serves list p / team and walks the chunks
+// p % team, p % team + team, ... below the list's count.
+template <int VPR>
+__global__ __launch_bounds__(kListThreads) void compact_list_kernel(CompactArgs a) {
+  const int32_t vpr = VPR ? VPR : a.vpr;
+  const bool is_v = blockIdx.x & 1;
+  const vec4u* __restrict__ src = is_v ? a.v_src : a.k_src;
+  vec4u* __restrict__ dst = is_v ? a.v_dst : a.k_dst;
+  for (int64_t pair = blockIdx.x >> 1; pair < a.items; pair += gridDim.x >> 1) {
+    const int64_t list = pair / a.team;
+    const int32_t first_chunk = (int32_t)(pair - list * a.team);
+    const int64_t g = list / a.H;
+    const int32_t h = (int32_t)(list - g * a.H);
+    const int64_t idx_list = g * a.ipg + (a.ipg == 1 ? 0 : h);
+    const int32_t count = list_count(
+        a, idx_list, first_chunk == 0 && !is_v && threadIdx.x == 0 && (a.ipg != 1 || h == 0));
+    const int32_t* idx = a.kept_idx + idx_list * a.kept_ld;
+    const int64_t step = (int64_t)a.team * a.rows_per_item;
+    for (int64_t r0l = (int64_t)first_chunk * a.rows_per_item; r0l < count; r0l += step) {
+      const int32_t r0 = (int32_t)r0l;
+      const int32_t r1 = min(count, r0 + a.rows_per_item);
+      const int32_t nvec = (r1 - r0) * vpr;
+      for (int32_t v = threadIdx.x; v < nvec; v += kListThreads) {
         const int32_t row = r0 + v / vpr;
         const int32_t col = v % vpr;
-        const int32_t t = idx[row];
-        const int64_t so = row_vec_offset<VPR>(a.src, g, h, a.H, list, t, vpr);
-        const int64_t dof = row_vec_offset<VPR>(a.dst, g, h, a.H, list, row, vpr);
+        const int64_t so = row_vec_offset(a.src, g, h, a.H, list, idx[row], vpr);
+        const int64_t dof = row_vec_offset(a.dst, g, h, a.H, list, row, vpr);
         if (so >= 0 && dof >= 0) {
-          kr[u] = __builtin_nontemporal_load(a.k_src + so + col);
-          vr[u] = __builtin_nontemporal_load(a.v_src + so + col);
-          doff[u] = dof + col;
-        } else if (col == 0 && a.errors) {
+          const vec4u x = __builtin_nontemporal_load(src + so + col);
+          __builtin_nontemporal_store(x, dst + dof + col);
+        } else if (col == 0 && !is_v && a.errors) {
           atomicAdd(a.errors, 1u);
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (doff[u] >= 0) {
-        __builtin_nontemporal_store(kr[u], a.k_dst + doff[u]);
-        __builtin_nontemporal_store(vr[u], a.v_dst + doff[u]);
+  }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void compact_group_kernel(CompactArgs a) {
+  const int32_t vpr = a.vpr;
+  const int32_t tok_vecs = a.H * vpr;  // vectors of one token row over all heads
+  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+    const int64_t g = item / a.chunks;
+    const int32_t chunk = (int32_t)(item - g * a.chunks);
+    const int32_t r0 = chunk * a.rows_per_item;
+    const int32_t r1 = min(a.K, r0 + a.rows_per_item);
+    const int32_t nvec = (r1 - r0) * tok_vecs;
+    for (int32_t v = threadIdx.x; v < nvec; v += kGroupThreads) {
+      const int32_t row = r0 + v / tok_vecs;
+      const int32_t rem = v % tok_vecs;
+      const int32_t h = rem / vpr;
+      const int32_t col = rem - h * vpr;
+      const int64_t list = g * a.H + h;
+      const int64_t idx_list = g * a.ipg + (a.ipg == 1 ? 0 : h);
+      const bool first = (chunk == 0 && row == r0 && col == 0 && (a.ipg != 1 || h == 0));
+      const int32_t count = list_count(a, idx_list, first);
+      if (row >= count) continue;
+      const int64_t so = row_vec_offset(a.src, g, h, a.H, list, a.kept_idx[idx_list * a.kept_ld + row], vpr);
+      const int64_t dof = row_vec_offset(a.dst, g, h, a.H, list, row, vpr);
+      if (so >= 0 && dof >= 0) {
+        const vec4u x = __builtin_nontemporal_load(a.k_src + so + col);
+        const vec4u y = __builtin_nontemporal_load(a.v_src + so + col);
+        __builtin_nontemporal_store(x, a.k_dst + dof + col);
+        __builtin_nontemporal_store(y, a.v_dst + dof + col);
+      } else if (col == 0 && a.errors) {
+        atomicAdd(a.errors, 1u);
       }
     }
   }
 }
 
-int32_t rows_per_block(int32_t D, int32_t K) {
-  int32_t rows = kVecsPerBlock / (D / 8);
-  if (rows < 1) rows = 1;
-  if (rows > K) rows = K;
-  return rows;
+struct Plan {
+  bool group;
+  int32_t rows_per_item, chunks, team;
+  int64_t items, grid;
+};
+
+Plan plan_compact(const StoreView& src, const StoreView& dst, int32_t D, int32_t H, int32_t K,
+                  int64_t num_groups, bool variable_counts) {
+  Plan p{};
+  const int32_t vpr = D / 8;
+  p.group = src.paged || dst.paged;
+  if (p.group) {
+    const int32_t tok_vecs = H * vpr;
+    p.rows_per_item = tok_vecs >= kGroupVecs ? 1 : kGroupVecs / tok_vecs;
+    p.chunks = (K + p.rows_per_item - 1) / p.rows_per_item;
+    p.items = num_groups * p.chunks;
+    p.grid = p.items < kMaxGrid ? p.items : kMaxGrid;
+  } else {
+    p.rows_per_item = vpr >= kListVecs ? 1 : kListVecs / vpr;
+    p.chunks = (K + p.rows_per_item - 1) / p.rows_per_item;
+    // Uniform counts: one chunk per workgroup pair.  Variable counts (K only
+    // bounds them): a quarter as many pairs, each walking up to four chunks,
+    // so lists far below K do not leave most workgroups empty.
+    p.team = variable_counts ? (p.chunks + kVariableChunksPerPair - 1) / kVariableChunksPerPair
+                             : p.chunks;
+    p.items = num_groups * H * p.team;
+    const int64_t pairs = p.items < kMaxGrid / 2 ? p.items : kMaxGrid / 2;
+    p.grid = 2 * pairs;  // even workgroups move K, odd ones V
+  }
+  return p;
 }
 
 }  // namespace
-
-int64_t compact_workgroups(int32_t D, int32_t K, int64_t lists) {
-  if (K <= 0) return 0;
-  const int32_t rows = rows_per_block(D, K);
-  return lists * ((K + rows - 1) / rows);
-}
 
 hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v_src,
                           const StoreView& dst, void* k_dst, void* v_dst, int32_t D, int32_t H,
@@ -131,8 +199,7 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
                           int32_t K, int64_t num_groups, int32_t ipg, uint32_t* errors,
                           hipStream_t stream) {
   if (num_groups == 0 || K == 0) return hipSuccess;
-  const int32_t vpr = D / 8;
-  const int32_t rows = rows_per_block(D, K);
+  const Plan p = plan_compact(src, dst, D, H, K, num_groups, kept_count != nullptr);
   CompactArgs a;
   a.src = src;
   a.dst = dst;
@@ -146,24 +213,27 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
   a.K = K;
   a.H = H;
   a.ipg = ipg;
-  a.rows_per_block = rows;
-  a.chunks_per_list = (K + rows - 1) / rows;
-  a.vpr = vpr;
+  a.rows_per_item = p.rows_per_item;
+  a.chunks = p.chunks;
+  a.team = p.team;
+  a.items = p.items;
+  a.vpr = D / 8;
   a.errors = errors;
-  const int64_t blocks = num_groups * H * a.chunks_per_list;
-  const dim3 grid((unsigned)blocks), block(kThreads);
-  switch (vpr) {
-    case 8:
-      hipLaunchKernelGGL(compact_kernel<8>, grid, block, 0, stream, a);
-      break;
+  if (p.group) {
+    hipLaunchKernelGGL(compact_group_kernel, dim3((unsigned)p.grid), dim3(kGroupThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)p.grid), block(kListThreads);
+  switch (a.vpr) {
     case 16:
-      hipLaunchKernelGGL(compact_kernel<16>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(compact_list_kernel<16>, grid, block, 0, stream, a);
       break;
     case 32:
-      hipLaunchKernelGGL(compact_kernel<32>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(compact_list_kernel<32>, grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL(compact_kernel<0>, grid, block, 0, stream, a);
+      hipLaunchKernelGGL(compact_list_kernel<0>, grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();

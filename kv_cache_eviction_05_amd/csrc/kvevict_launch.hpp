@@ -44,9 +44,6 @@ struct StoreView {
   int64_t max_rows;        // rows addressable per list
 };
 
-// Workgroups launch_compact uses for `lists` index lists of up to K rows of D elements.
-int64_t compact_workgroups(int32_t D, int32_t K, int64_t lists);
-
 hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v_src,
                           const StoreView& dst, void* k_dst, void* v_dst, int32_t D, int32_t H,
                           const int32_t* kept_idx, int64_t kept_ld, const int32_t* kept_count,
