@@ -10,15 +10,15 @@
 // MI355X against plain copies of the same bytes:
 //
 //  * list kernel (both stores contiguous).  A work item is one (list, chunk of
-//    rows), about 4 KiB of K or of V; even workgroups move the K rows of an
-//    item and odd ones the V rows.  Small items keep the set of workgroups in
-//    flight on a compact address range, which on this part is worth ~15% over
-//    large per-list chunks (6.2-6.7 TB/s vs 5.2-5.3 TB/s on 256-byte rows).
-//  * group kernel (either store paged).  A work item is one (group, a few
+//    rows), 8 KiB of K or of V; even workgroups move the K rows of an item and
+//    odd ones the V rows.  Small items keep the set of workgroups in flight on
+//    a compact address range: ~6.0-6.35 TB/s on 256-byte rows, against
+//    5.2-5.3 TB/s for 128 KiB per-list chunks moving K and V together.
+//  * group kernel (either store paged).  A work item is one (group, four
 //    destination tokens) over all H heads, K and V in the same thread, so a
 //    workgroup writes whole token rows of a destination page and reads the
-//    nearby source tokens of every head.  With seed-shuffled page tables the
-//    ceiling is the random 32 KiB page copy (~5.1 TB/s); this layout reaches it.
+//    nearby source tokens of every head: ~5.7-6.0 TB/s with seed-shuffled page
+//    tables, against ~4.5 TB/s for per-head chunks.
 //
 // Work items are visited by a grid-stride loop, so a one-shot grid (one item
 // per workgroup) and a grid capped below 2^32 work-items run the same code.
@@ -35,11 +35,11 @@ namespace kvevict {
 namespace {
 
 constexpr int kListThreads = 128;
-constexpr int kListVecs = 256;    // 16-byte vectors of K (or of V) per list item: 4 KiB
+constexpr int kListVecs = 512;    // 16-byte vectors of K (or of V) per list item: 8 KiB
 constexpr int kGroupThreads = 256;
-constexpr int kGroupVecs = 256;   // vectors of K and of V per group item
+constexpr int kGroupVecs = 512;   // vectors of K and of V per group item: 8 KiB each
 constexpr int64_t kMaxGrid = 1 << 24;  // workgroups per launch (work-items stay below 2^32)
-constexpr int32_t kVariableChunksPerPair = 4;
+constexpr int32_t kVariableChunksPerPair = 8;
 
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
@@ -180,7 +180,7 @@ Plan plan_compact(const StoreView& src, const StoreView& dst, int32_t D, int32_t
     p.rows_per_item = vpr >= kListVecs ? 1 : kListVecs / vpr;
     p.chunks = (K + p.rows_per_item - 1) / p.rows_per_item;
     // Uniform counts: one chunk per workgroup pair.  Variable counts (K only
-    // bounds them): a quarter as many pairs, each walking up to four chunks,
+    // bounds them): an eighth as many pairs, each walking up to eight chunks,
     // so lists far below K do not leave most workgroups empty.
     p.team = variable_counts ? (p.chunks + kVariableChunksPerPair - 1) / kVariableChunksPerPair
                              : p.chunks;

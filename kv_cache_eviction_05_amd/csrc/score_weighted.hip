@@ -5,16 +5,29 @@
 //   s[l][h][t] = sum_{slot} sum_j w[l][h][slot][j] * ln(beta[g][t][j] * vnorm[g][t][j]),
 //   g = win_begin[l] + slot,   +inf for t < prot.
 //
-// Layout of the work: a workgroup of 256 threads owns a tile of 64 tokens.
-// It walks the GDN layers g used by any window once; for each it loads the
-// tile's beta and |v| rows (coalesced along the GDN heads), takes one binary64
-// log per (t, j) into LDS (transposed, so lane = token reads are conflict
-// free), and every wave folds that layer into the accumulators of the
-// attention layers whose window contains g.  Wave w serves KV head h0 + w,
-// lane = token; the weights are wave-uniform and come through scalar loads.
-// Accumulation is binary64, rounded once to fp32 on the store, so the result
-// matches a binary64 evaluation of the sum up to the summation order.
+// Layout of the work.  A workgroup of eight waves owns a tile of 64 tokens
+// and walks the GDN layers g of its launch once, in order, in passes of 48
+// GDN heads.  For each (g, pass) the workgroup loads the tile of beta and |v|
+// with coalesced 8-byte loads (when the layout allows) and the pass's weights
+// of the active windows; every thread takes the binary64 logs of the six
+// products it loaded into a transposed LDS tile, and the weights go to LDS as
+// binary64.  The next tile's loads are issued before the current one is
+// folded.  Wave w then owns GDN heads [6w, 6w + 6) with lane = token: it folds
+// its six logs into partial sums, one per (KV head, accumulator slot).  A slot
+// holds the attention layer whose window contains g; the host assigns slots
+// so that layers with overlapping windows never share one (at most kSlots at
+// a time, else more launches) and passes, per GDN layer, each slot's weight
+// row and the windows that end there.  When a layer's window ends, the waves'
+// partial sums are added through LDS in a fixed order and the fp32 score is
+// stored.  The LDS tiles are double-buffered, so each step needs one barrier.
+//
+// Precision: the product beta*|v| of two floats is exact in binary64; its
+// natural log is taken in binary64 (table-driven reduction to [-2^-8, 2^-8]
+// and a degree-7 series, within a few binary64 ulps; zero, infinities, NaN
+// and negative products go through the library log); accumulation is
+// binary64 and the result is rounded once to fp32.
 #include <cmath>
+#include <type_traits>
 
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
@@ -22,97 +35,299 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTok = 64;            // tokens per tile (= lanes)
-constexpr int kHeadsPerBlock = 4;   // one KV head per wave
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTok = 64;                    // tokens per tile (= lanes)
+constexpr int kJW = 6;                      // GDN heads per wave per pass
+constexpr int kJPass = kWaves * kJW;        // GDN heads per pass
+constexpr int kHB = 4;                      // KV heads per launch
+constexpr int kSlots = 2;                   // accumulator slots
 constexpr int kLayersPerLaunch = 16;
-constexpr int kJChunk = 64;         // GDN heads staged per pass
-constexpr int kXStride = kTok + 1;  // doubles per staged GDN head (padding)
+constexpr int kPlanLayers = 64;             // GDN layers one launch spans
+constexpr int kLnTable = 128;               // ln table: centres of [1, 2) in steps of 1/128
+constexpr int kXStride = kTok + 1;          // doubles per staged GDN head (padding)
+constexpr int kElems = kTok * kJPass / kThreads;  // tile elements per thread
+constexpr int kWRow = kSlots * kHB * kJPass;      // weights of one (GDN layer, pass)
+static_assert(kTok * kJPass == kElems * kThreads, "the tile splits evenly over the threads");
+static_assert(kWRow <= kThreads, "one weight per thread");
 
 struct WeightedArgs {
-  float* scores;
   int64_t ld;
-  const float* beta;
-  const float* vnorm;
   int64_t sg, st, sj;
-  const float* w;
   int32_t w_slots, H, Hg, n, prot;
-  int32_t l0, nl;  // attention layers [l0, l0 + nl) of this launch
-  int32_t h0;      // first KV head of this launch
+  int32_t h0, hb;   // KV heads [h0, h0 + hb) of this launch
+  int32_t nl;       // attention layers of this launch
   int32_t g_lo, g_hi;
-  WindowTable win;
+  uint32_t empty_mask;                   // launch layers with an empty window
+  int32_t layer[kLayersPerLaunch];       // attention layer of each launch layer
+  int32_t slot[kLayersPerLaunch];        // its accumulator slot
+  int64_t woff[kPlanLayers][kSlots];     // weight row of (g, slot) for head h0, or -1
+  uint32_t end_mask[kPlanLayers];        // launch layers whose window ends at g
 };
 
-__global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a) {
-  __shared__ double s_x[kJChunk * kXStride];
+// ln(x) in binary64 for a positive normal x: x = 2^e * m, m in [1, 2);
+// c = 1 + (i + 1/2)/128 is the centre of m's slot, r = (m - c)/c with
+// |r| <= 2^-8, and ln x = e ln 2 + ln c + ln(1 + r) with
+// ln(1 + r) = r - r^2/2 + ... + r^7/7.  Only the high word of x carries e and
+// i, so m and c are built from it.  *special is set when x is not a positive
+// normal number (zero, subnormal, infinite, NaN or negative).
+__device__ __forceinline__ double ln_fast(double x, const double* lnc, const double* inv,
+                                          bool* special) {
+  const uint32_t hi = (uint32_t)__double2hiint(x);
+  const uint32_t ex = hi >> 20;  // sign and biased exponent
+  *special = ex - 1u >= 0x7feu;
+  const uint32_t i = (hi >> 13) & (kLnTable - 1);
+  const double m = __hiloint2double((int)((hi & 0x000fffffu) | 0x3ff00000u), __double2loint(x));
+  const double c = __hiloint2double((int)((hi & 0x000fe000u) | 0x3ff01000u), 0);
+  const double r = (m - c) * inv[i];
+  double p = 1.0 / 7.0;
+  p = fma(p, r, -1.0 / 6.0);
+  p = fma(p, r, 1.0 / 5.0);
+  p = fma(p, r, -0.25);
+  p = fma(p, r, 1.0 / 3.0);
+  p = fma(p, r, -0.5);
+  p = fma(p, r, 1.0);
+  return fma((double)((int32_t)ex - 1023), M_LN2, fma(p, r, lnc[i]));
+}
+
+// The library log, out of line, for the arguments ln_fast does not take.
+__device__ __attribute__((noinline)) double ln_special(double x) { return log(x); }
+
+// A thread's share of one (GDN layer, pass) tile: tokens [t0, t0 + 64) x GDN
+// heads [j0, j0 + jn), element e = token * jn + j; the thread holds the VW
+// consecutive heads of vectors q = tid + k * kThreads.
+template <int VW>
+struct Tile {
+  static constexpr int kVecs = kElems / VW;
+  float b[kVecs][VW];
+  float v[kVecs][VW];
+  float w;  // one weight of the (GDN layer, pass): [slot][head][j]
+};
+
+// Element position of vector k in a tile of width jn (kFull: jn == kJPass).
+template <int VW, bool kFull>
+__device__ __forceinline__ void tile_pos(int k, int32_t jn, int32_t* tok, int32_t* j) {
+  const int32_t q = threadIdx.x + k * kThreads;
+  const int32_t vpt = (kFull ? kJPass : jn) / VW;  // vectors per token
+  *tok = q / vpt;
+  *j = (q - *tok * vpt) * VW;
+}
+
+// Loads a tile and this thread's weight (1.0 signals outside the data, so
+// their log is 0; weight 0 outside the active rows).  VW = 2 needs sj == 1,
+// even jn and 8-byte aligned rows.
+template <int VW, bool kFull>
+__device__ __forceinline__ void load_tile(const WeightedArgs& a, const float* __restrict__ beta,
+                                          const float* __restrict__ vnorm,
+                                          const float* __restrict__ wts, int32_t g, int32_t p,
+                                          int32_t t0, Tile<VW>& r) {
+  const int32_t j0 = p * kJPass;
+  const int32_t jn = kFull ? kJPass : min(kJPass, a.Hg - j0);
+#pragma unroll
+  for (int k = 0; k < Tile<VW>::kVecs; ++k) {
+    int32_t tok, j;
+    tile_pos<VW, kFull>(k, jn, &tok, &j);
+#pragma unroll
+    for (int c = 0; c < VW; ++c) {
+      r.b[k][c] = 1.0f;
+      r.v[k][c] = 1.0f;
+    }
+    if ((!kFull && tok >= kTok) || t0 + tok >= a.n) continue;
+    const int64_t e = (int64_t)g * a.sg + (int64_t)(t0 + tok) * a.st + (int64_t)(j0 + j) * a.sj;
+    if (VW == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(beta + e);
+      const float2 y = *reinterpret_cast<const float2*>(vnorm + e);
+      r.b[k][0] = x.x;
+      r.b[k][VW - 1] = x.y;
+      r.v[k][0] = y.x;
+      r.v[k][VW - 1] = y.y;
+    } else {
+      r.b[k][0] = beta[e];
+      r.v[k][0] = vnorm[e];
+    }
+  }
+  r.w = 0.0f;
+  if (threadIdx.x < kWRow) {
+    const int32_t s = threadIdx.x / (kHB * kJPass);
+    const int32_t hh = (threadIdx.x / kJPass) % kHB;
+    const int32_t j = threadIdx.x % kJPass;
+    const int64_t wo = a.woff[g - a.g_lo][s];
+    if (wo >= 0 && hh < a.hb && j < jn)
+      r.w = wts[wo + (int64_t)hh * a.w_slots * a.Hg + j0 + j];
+  }
+}
+
+// Logs of a loaded tile into x[j][token] (transposed) and its weights, as
+// binary64, into w.
+template <int VW, bool kFull>
+__device__ __forceinline__ void stage_tile(const Tile<VW>& r, int32_t jn, double* x, double* w,
+                                           const double* lnc, const double* inv) {
+  double y[Tile<VW>::kVecs][VW];
+  bool any_special = false;
+#pragma unroll
+  for (int k = 0; k < Tile<VW>::kVecs; ++k)
+#pragma unroll
+    for (int c = 0; c < VW; ++c) {
+      bool sp;
+      y[k][c] = ln_fast((double)r.b[k][c] * (double)r.v[k][c], lnc, inv, &sp);
+      any_special |= sp;
+    }
+  if (any_special) {  // zero, infinite, NaN or negative signals: the library log
+#pragma unroll
+    for (int k = 0; k < Tile<VW>::kVecs; ++k)
+#pragma unroll
+      for (int c = 0; c < VW; ++c) {
+        const double xv = (double)r.b[k][c] * (double)r.v[k][c];
+        const uint32_t ex = (uint32_t)__double2hiint(xv) >> 20;
+        if (ex - 1u >= 0x7feu) y[k][c] = ln_special(xv);
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < Tile<VW>::kVecs; ++k) {
+    int32_t tok, j;
+    tile_pos<VW, kFull>(k, jn, &tok, &j);
+    if (!kFull && tok >= kTok) continue;
+#pragma unroll
+    for (int c = 0; c < VW; ++c) x[(j + c) * kXStride + tok] = y[k][c];
+  }
+  if (threadIdx.x < kWRow) w[threadIdx.x] = (double)r.w;
+}
+
+// The weights, signals and scores come as separate restrict-qualified
+// arguments: the kernel never writes what it reads.
+template <int VW>
+__global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a,
+                                                                  const float* __restrict__ wts,
+                                                                  const float* __restrict__ beta,
+                                                                  const float* __restrict__ vnorm,
+                                                                  float* __restrict__ scores) {
+  __shared__ double s_lnc[kLnTable];
+  __shared__ double s_inv[kLnTable];
+  __shared__ double s_x[2][kJPass * kXStride];
+  __shared__ double s_w[2][kWRow];
+  __shared__ double s_red[kWaves][kHB][kTok];
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int32_t t0 = blockIdx.x * kTok;
   const int32_t t = t0 + lane;
-  const int32_t h = a.h0 + wave;
-  const bool head_ok = h < a.H;
 
-  double acc[kLayersPerLaunch];
-#pragma unroll
-  for (int q = 0; q < kLayersPerLaunch; ++q) acc[q] = 0.0;
-
+  // stores the fp32 score of (layer index q of the launch, head h0 + hh) for the tile
+  auto store = [&](int q, int hh, int32_t tt, double v) {
+    if (hh < a.hb && tt < a.n)
+      scores[((int64_t)a.layer[q] * a.H + a.h0 + hh) * a.ld + tt] =
+          (tt < a.prot) ? INFINITY : (float)v;
+  };
+  // layers with an empty window score 0; a tile inside the prompt is all +inf
   const bool tile_in_prompt = (t0 + kTok <= a.prot);
-  if (!tile_in_prompt) {
-    for (int32_t g = a.g_lo; g < a.g_hi; ++g) {
-      for (int32_t j0 = 0; j0 < a.Hg; j0 += kJChunk) {
-        const int32_t jn = min(kJChunk, a.Hg - j0);
-        // stage ln(beta * |v|) of tokens [t0, t0+64) x heads [j0, j0+jn):
-        // every wave first issues its 16 row loads, then takes the logs
-        constexpr int kRows = kTok / kHeadsPerBlock;
-        float bv[kRows], vv[kRows];
-        const bool lane_ok = lane < jn;
-#pragma unroll
-        for (int k = 0; k < kRows; ++k) {
-          const int32_t tt = t0 + wave + k * kHeadsPerBlock;
-          bv[k] = 1.0f;
-          vv[k] = 1.0f;
-          if (lane_ok && tt < a.n) {
-            const int64_t e = (int64_t)g * a.sg + (int64_t)tt * a.st + (int64_t)(j0 + lane) * a.sj;
-            bv[k] = a.beta[e];
-            vv[k] = a.vnorm[e];
-          }
-        }
-        if (lane_ok) {
-#pragma unroll
-          for (int k = 0; k < kRows; ++k)
-            s_x[lane * kXStride + wave + k * kHeadsPerBlock] = log((double)bv[k] * (double)vv[k]);
-        }
-        __syncthreads();
-        if (head_ok) {
-#pragma unroll
-          for (int q = 0; q < kLayersPerLaunch; ++q) {
-            if (q < a.nl) {
-              const int32_t l = a.l0 + q;
-              const int32_t slot = g - a.win.begin[l];
-              if (slot >= 0 && slot < a.win.count[l]) {
-                const float* wr = a.w + (((int64_t)l * a.H + h) * a.w_slots + slot) * a.Hg + j0;
-                double s = acc[q];
-                for (int32_t j = 0; j < jn; ++j) s = fma((double)wr[j], s_x[j * kXStride + lane], s);
-                acc[q] = s;
-              }
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
+  if (wave < kHB) {
+    for (int q = 0; q < a.nl; ++q)
+      if (tile_in_prompt || ((a.empty_mask >> q) & 1u)) store(q, wave, t, 0.0);
   }
-  if (head_ok && t < a.n) {
+  if (tile_in_prompt || a.g_hi <= a.g_lo) return;
+
+  if (tid < kLnTable) {
+    const double c = 1.0 + ((double)tid + 0.5) * (1.0 / kLnTable);
+    s_lnc[tid] = log(c);
+    s_inv[tid] = 1.0 / c;
+  }
+
+  const int32_t passes = (a.Hg + kJPass - 1) / kJPass;
+  const bool full = a.Hg % kJPass == 0;  // every pass is kJPass heads wide
+  const int32_t steps = (a.g_hi - a.g_lo) * passes;
+  double acc[kHB][kSlots];
 #pragma unroll
-    for (int q = 0; q < kLayersPerLaunch; ++q) {
-      if (q < a.nl) {
-        const int32_t l = a.l0 + q;
-        a.scores[((int64_t)l * a.H + h) * a.ld + t] = (t < a.prot) ? INFINITY : (float)acc[q];
+  for (int hh = 0; hh < kHB; ++hh)
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) acc[hh][s] = 0.0;
+
+  Tile<VW> regs;
+  if (full)
+    load_tile<VW, true>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs);
+  else
+    load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs);
+  __syncthreads();  // the ln table
+  for (int32_t step = 0; step < steps; ++step) {
+    const int32_t g = a.g_lo + step / passes;
+    const int32_t p = step - (g - a.g_lo) * passes;
+    const int32_t jn = min(kJPass, a.Hg - p * kJPass);
+    double* x = s_x[step & 1];
+    double* w = s_w[step & 1];
+    if (full)
+      stage_tile<VW, true>(regs, jn, x, w, s_lnc, s_inv);
+    else
+      stage_tile<VW, false>(regs, jn, x, w, s_lnc, s_inv);
+    if (step + 1 < steps) {  // the next tile streams in while this one is folded
+      const int32_t g2 = a.g_lo + (step + 1) / passes;
+      const int32_t p2 = step + 1 - (g2 - a.g_lo) * passes;
+      if (full)
+        load_tile<VW, true>(a, beta, vnorm, wts, g2, p2, t0, regs);
+      else
+        load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs);
+    }
+    __syncthreads();
+
+    const int32_t jb = wave * kJW;  // this wave's heads [jb, je) of the tile
+    const int32_t je = min(jb + kJW, jn);
+    const int32_t gi = g - a.g_lo;
+    // folds logs [jb, je) into the partial sums; kFull: je - jb == kJW
+    auto fold = [&](auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;
+      double xv[kJW];
+#pragma unroll
+      for (int k = 0; k < kJW; ++k)
+        xv[k] = (kFull || jb + k < je) ? x[(jb + k) * kXStride + lane] : 0.0;
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        if (a.woff[gi][s] < 0) continue;
+#pragma unroll
+        for (int hh = 0; hh < kHB; ++hh) {
+          const double* wr = w + (s * kHB + hh) * kJPass + jb;
+          double v = acc[hh][s];
+#pragma unroll
+          for (int k = 0; k < kJW; ++k)
+            if (kFull || jb + k < je) v = fma(wr[k], xv[k], v);
+          acc[hh][s] = v;
+        }
       }
+    };
+    if (je - jb == kJW)
+      fold(std::true_type{});
+    else if (jb < je)
+      fold(std::false_type{});
+
+    if (p + 1 < passes) continue;
+    // windows ending at g: add the waves' partial sums in a fixed order and store
+    uint32_t ends = a.end_mask[gi];
+    while (ends) {
+      const int32_t q = __builtin_ctz(ends);
+      ends &= ends - 1u;
+      const int32_t s_q = a.slot[q];
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        if (s == s_q) {
+#pragma unroll
+          for (int hh = 0; hh < kHB; ++hh) {
+            s_red[wave][hh][lane] = acc[hh][s];
+            acc[hh][s] = 0.0;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < kHB * kTok) {
+        const int hh = tid / kTok;
+        double v = 0.0;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) v += s_red[w2][hh][lane];
+        store(q, hh, t, v);
+      }
+      __syncthreads();
     }
   }
 }
+
+static_assert(kThreads >= kHB * kTok, "one thread per (head, token) in the reduction");
+static_assert(kWaves >= kHB, "one wave per head for the direct stores");
 
 }  // namespace
 
@@ -122,37 +337,76 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
                                  int32_t Hg, int32_t n, int32_t prot, hipStream_t stream) {
   if (n == 0 || L == 0 || H == 0) return hipSuccess;
   const unsigned tiles = (unsigned)((n + kTok - 1) / kTok);
-  for (int32_t l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
-    const int32_t nl = (L - l0 < kLayersPerLaunch) ? L - l0 : kLayersPerLaunch;
-    int32_t g_lo = 0x7fffffff, g_hi = 0;
-    for (int32_t l = l0; l < l0 + nl; ++l) {
-      if (win.count[l] <= 0) continue;
-      g_lo = (win.begin[l] < g_lo) ? win.begin[l] : g_lo;
-      g_hi = (win.begin[l] + win.count[l] > g_hi) ? win.begin[l] + win.count[l] : g_hi;
+  const bool vec = sj == 1 && sg % 2 == 0 && st % 2 == 0 && Hg % 2 == 0 &&
+                   (reinterpret_cast<uintptr_t>(beta) & 7u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(vnorm) & 7u) == 0;
+  // Greedy grouping of layers into launches: a layer joins the current launch
+  // in the first slot whose layers' windows it does not overlap; when no slot
+  // is free, the launch is full or its GDN range would pass kPlanLayers, a
+  // new launch starts.
+  int32_t l = 0;
+  while (l < L) {
+    WeightedArgs a;
+    a.ld = ld;
+    a.sg = sg;
+    a.st = st;
+    a.sj = sj;
+    a.w_slots = w_slots;
+    a.H = H;
+    a.Hg = Hg;
+    a.n = n;
+    a.prot = prot;
+    a.nl = 0;
+    a.empty_mask = 0u;
+    int32_t lo = 0x7fffffff, hi = 0;
+    int32_t begin[kLayersPerLaunch], end[kLayersPerLaunch];
+    for (; l < L && a.nl < kLayersPerLaunch; ++l) {
+      const int32_t b = win.begin[l], e = win.begin[l] + win.count[l];
+      int32_t slot = 0;
+      if (e > b) {
+        const int32_t nlo = b < lo ? b : lo, nhi = e > hi ? e : hi;
+        if (nhi - nlo > kPlanLayers) break;
+        for (slot = 0; slot < kSlots; ++slot) {
+          bool free = true;
+          for (int32_t q = 0; q < a.nl; ++q)
+            if (a.slot[q] == slot && begin[q] < end[q] && begin[q] < e && b < end[q]) free = false;
+          if (free) break;
+        }
+        if (slot == kSlots) break;  // overlaps kSlots windows of this launch: next launch
+        lo = nlo;
+        hi = nhi;
+      } else {
+        a.empty_mask |= 1u << a.nl;
+      }
+      a.layer[a.nl] = l;
+      a.slot[a.nl] = slot;
+      begin[a.nl] = b;
+      end[a.nl] = e;
+      ++a.nl;
     }
-    if (g_hi <= g_lo) g_lo = g_hi = 0;  // empty windows: scores are 0 (or +inf in the prompt)
-    for (int32_t h0 = 0; h0 < H; h0 += kHeadsPerBlock) {
-      WeightedArgs a;
-      a.scores = scores;
-      a.ld = ld;
-      a.beta = beta;
-      a.vnorm = vnorm;
-      a.sg = sg;
-      a.st = st;
-      a.sj = sj;
-      a.w = w;
-      a.w_slots = w_slots;
-      a.H = H;
-      a.Hg = Hg;
-      a.n = n;
-      a.prot = prot;
-      a.l0 = l0;
-      a.nl = nl;
+    if (hi <= lo) lo = hi = 0;  // only empty windows
+    a.g_lo = lo;
+    a.g_hi = hi;
+    for (int32_t h0 = 0; h0 < H; h0 += kHB) {
       a.h0 = h0;
-      a.g_lo = g_lo;
-      a.g_hi = g_hi;
-      a.win = win;
-      hipLaunchKernelGGL(score_weighted_kernel, dim3(tiles), dim3(kThreads), 0, stream, a);
+      a.hb = (H - h0 < kHB) ? H - h0 : kHB;
+      for (int32_t gi = 0; gi < kPlanLayers; ++gi) {
+        a.end_mask[gi] = 0u;
+        for (int s = 0; s < kSlots; ++s) a.woff[gi][s] = -1;
+      }
+      for (int32_t q = 0; q < a.nl; ++q) {
+        if (begin[q] >= end[q]) continue;
+        for (int32_t g = begin[q]; g < end[q]; ++g)
+          a.woff[g - lo][a.slot[q]] =
+              (((int64_t)a.layer[q] * H + h0) * w_slots + (g - begin[q])) * Hg;
+        a.end_mask[end[q] - 1 - lo] |= 1u << q;
+      }
+      if (vec)
+        hipLaunchKernelGGL(score_weighted_kernel<2>, dim3(tiles), dim3(kThreads), 0, stream, a, w,
+                           beta, vnorm, scores);
+      else
+        hipLaunchKernelGGL(score_weighted_kernel<1>, dim3(tiles), dim3(kThreads), 0, stream, a, w,
+                           beta, vnorm, scores);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

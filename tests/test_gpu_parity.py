@@ -329,3 +329,49 @@ def test_score_weighted(G, L, H, Hg, n, prot, width):
     want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot)
     same = assert_weighted_close(got[:, :n], want, prot)
     say(f"  bit-identical fraction {same:.6f}")
+
+
+def test_score_weighted_interleaved_signals():
+    """The page's interleaved [G, n, Hg, 3] signal tensor (beta, g, |v|) through the stride arguments."""
+    G, L, H, Hg, n, prot, width = 12, 4, 4, 48, 333, 20, 6
+    say(f"score_weighted interleaved G={G} L={L} H={H} Hg={Hg} n={n} prot={prot}")
+    beta, vnorm, w, begins, counts = weighted_case(G, L, H, Hg, n, prot, width, seed=77)
+    sig = np.zeros((G, n, Hg, 3), dtype=np.float32)
+    sig[..., 0] = beta
+    sig[..., 1] = -1.0  # the log-decay channel, not read by the score
+    sig[..., 2] = vnorm
+    flat = torch.from_numpy(sig.reshape(-1)).to(DEV)
+    s = torch.full((L * H, n), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_weighted(s, n, flat[0:], flat[2:], n * Hg * 3, Hg * 3, 3,
+                             torch.from_numpy(w).to(DEV), width, begins, counts, L, H, G, Hg, n, prot)
+    torch.cuda.synchronize()
+    want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot)
+    same = assert_weighted_close(to_np(s), want, prot)
+    say(f"  bit-identical fraction {same:.6f}")
+
+
+def test_score_weighted_special_signals():
+    """Zero, infinite and NaN signals: the same infinities and NaNs as the oracle."""
+    G, L, H, Hg, n, prot, width = 6, 2, 4, 48, 200, 3, 6
+    say("score_weighted special signals")
+    beta, vnorm, w, begins, counts = weighted_case(G, L, H, Hg, n, prot, width, seed=5)
+    beta[1, 50, 7] = 0.0            # ln 0 = -inf
+    vnorm[2, 60, 3] = np.inf        # +inf
+    beta[0, 70, 0] = np.nan         # NaN
+    beta[3, 80, 5] = 0.0
+    vnorm[3, 80, 9] = np.inf        # opposite infinities in one sum: NaN for most weights
+    beta[4, 90, 1] = 1e-45          # subnormal float: an ordinary binary64 product
+    s = torch.full((L * H, n), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_weighted(s, n, torch.from_numpy(beta).to(DEV), torch.from_numpy(vnorm).to(DEV),
+                             n * Hg, Hg, 1, torch.from_numpy(w).to(DEV), width, begins, counts, L,
+                             H, G, Hg, n, prot)
+    torch.cuda.synchronize()
+    got = to_np(s).astype(np.float64)
+    want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(np.isposinf(got), np.isposinf(want))
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    fin = np.isfinite(want)
+    rel = np.abs(got[fin] - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30)
+    assert rel.max() <= 1e-5
+    assert np.isnan(want).any() and np.isinf(want[:, prot:]).any()  # the case is exercised
