@@ -2,19 +2,30 @@
 // entries beyond the protected prefix; KVzip-style global top-B over
 // (layer, head, token) scores).
 //
-// The candidates of each list ([prot, n)) are cut into chunks of kChunk
-// positions; one workgroup owns one (list, chunk) in every kernel below.
-//   init      prompt indices of every list; zero the histograms
+// The candidates of each list ([prot, n)) are cut into items of kChunk
+// positions, item f = list * chunks + chunk in flat order; one workgroup owns
+// one item in every kernel below.
+//   init      prompt indices and kept_count = prot for every list; zeroes the
+//             histograms, counters and state of the workspace
 //   hist x3   radix histograms of the 11/11/10-bit digits of rank_key(score),
-//             restricted to the keys matching the digits chosen so far;
-//             each workgroup resolves the earlier digits itself from the
-//             finished histograms (a 2048-bin scan), so no extra launches
-//   count     threshold key T and the number of keys equal to T to keep;
-//             per-chunk counts of keys > T and == T
-//   scan      one workgroup: exclusive scans over the chunks in flat order
-//             (ties at T go to the lowest list*n + i), per-list kept counts
-//   emit      ballot/mbcnt chronological emit of every chunk at its offset
+//             restricted to the keys matching the digits chosen so far; the
+//             last workgroup to finish resolves the digit from the finished
+//             histogram and stores it (later levels are skipped once a bucket
+//             is taken whole)
+//   count     per-item counts of keys > T and == T (T the threshold key)
+//   emit      the item's offset from the counts of the items before it in
+//             flat order (ties at T go to the lowest list*n + i), the per-list
+//             kept counts, and a ballot/mbcnt chronological emit of the item.
+//             With many items the last count workgroup scans the counts once
+//             instead and emit reads the offsets.
 // All counts are integer atomics or scans, so the result is deterministic.
+//
+// Every workspace word is written and read only with device-scope atomics
+// (ld_dev, st_dev, fetch-add), which take effect at the device's coherence
+// point: words passed between workgroups inside a kernel need no cache flush
+// (a device-scope fence would write back and invalidate every XCD's L2), and
+// no plain access can meet a stale copy of a word that an atomic wrote, in
+// this call or an earlier one on the same workspace.
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 
@@ -26,11 +37,12 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int32_t kChunk = 4096;
 
 // workspace layout (uint32 words)
-constexpr int64_t kHist0 = 0;      // 2048 bins, key bits [21, 32)
-constexpr int64_t kHist1 = 2048;   // 2048 bins, key bits [10, 21)
-constexpr int64_t kHist2 = 4096;   // 1024 bins, key bits [0, 10)
-constexpr int64_t kState = 5120;   // {T, need_eq}
-constexpr int64_t kArrays = 5128;  // gt[M], eq[M], eqx[M], S[M+1]
+constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
+constexpr int64_t kHist1 = 2048;    // 2048 bins, key bits [10, 21)
+constexpr int64_t kHist2 = 4096;    // 1024 bins, key bits [0, 10)
+constexpr int64_t kState = 5120;    // {prefix, mask, remaining, whole bucket}
+constexpr int64_t kDone = 5184;     // per-kernel counters of finished workgroups (4 words)
+constexpr int64_t kArrays = 5248;   // gt[M], eq[M], eqx[M], S[M+1]
 
 enum Mode : int32_t { kNormal = 0, kNone = 1, kAll = 2 };
 
@@ -45,54 +57,27 @@ __device__ __forceinline__ Level level_of(int lvl) {
   return {kHist2, 1024u, 0};
 }
 
-struct Resolved {
-  uint32_t prefix, mask, remaining;
-  bool whole_bucket;
-};
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Walks the finished histograms of levels [0, levels) from the top bin down
-// and returns the chosen digits.  Called by all threads of a workgroup.
-__device__ Resolved resolve(const uint32_t* ws, int levels, uint32_t budget, uint32_t* s_scan,
-                            uint32_t* s_pick) {
-  Resolved r{0u, 0u, budget, false};
-  const int tid = threadIdx.x;
-  for (int lvl = 0; lvl < levels; ++lvl) {
-    const Level L = level_of(lvl);
-    const uint32_t* hist = ws + L.off;
-    const uint32_t per = L.bins / kThreads;  // 8 or 4 bins per thread, top first
-    const uint32_t top = L.bins - per * (uint32_t)tid;  // exclusive upper bin
-    uint32_t c = 0u;
-    for (uint32_t b = 0; b < per; ++b) c += hist[top - 1u - b];
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
-    const uint32_t excl = incl - c;
-    if (excl < r.remaining && incl >= r.remaining) {
-      uint32_t acc = excl;
-      for (uint32_t b = 0; b < per; ++b) {
-        const uint32_t bin = top - 1u - b;
-        const uint32_t h = hist[bin];
-        if (acc + h >= r.remaining) {
-          s_pick[0] = bin;
-          s_pick[1] = r.remaining - acc;
-          s_pick[2] = h;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-    const uint32_t digit = s_pick[0];
-    const uint32_t cnt = s_pick[2];
-    r.remaining = s_pick[1];
-    r.prefix |= digit << L.shift;
-    r.mask |= (L.bins - 1u) << L.shift;
-    __syncthreads();
-    if (r.remaining == cnt) {
-      r.whole_bucket = true;
-      break;
-    }
-  }
-  return r;
+// True in every thread of the workgroup that finishes last among the grid's
+// workgroups (counter `done`).  Each wave first waits until all its memory
+// operations are acknowledged (s_waitcnt on every counter), so that the
+// device-scope atomics of every workgroup that has counted itself are
+// performed before the last one reads their words.  (A workgroup-scope fence
+// is not enough: it need not wait for global writes at all.)
+__device__ bool last_workgroup(uint32_t* done, uint32_t* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              gridDim.x - 1u;
+  __syncthreads();
+  return *s_flag != 0u;
 }
 
 struct GlobalArgs {
@@ -108,148 +93,236 @@ struct GlobalArgs {
   int32_t* kept_count;
 };
 
+__device__ __forceinline__ void item_range(const GlobalArgs& a, int64_t f, int64_t* list,
+                                           int32_t* i0, int32_t* i1) {
+  *list = f / a.chunks;
+  const int32_t chunk = (int32_t)(f - *list * a.chunks);
+  *i0 = a.prot + chunk * kChunk;
+  *i1 = min(a.n, *i0 + kChunk);
+}
+
+constexpr int kKeysPerThread = kChunk / kThreads;
+// Up to this many items, every emit workgroup sums the per-item counts before
+// its own item itself; beyond it, the last count workgroup scans them once.
+constexpr int64_t kDirectPrefixItems = 8192;
+
+// Loads the item's keys into registers, all loads in flight at once: key u of
+// the thread is position i0 + threadIdx.x + u * kThreads (valid if < i1).
+__device__ __forceinline__ void load_keys(const float* row, int32_t i0, int32_t i1,
+                                          uint32_t* keys) {
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const int32_t i = i0 + threadIdx.x + u * kThreads;
+    keys[u] = (i < i1) ? rank_key(row[i]) : 0u;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void global_init_kernel(GlobalArgs a) {
   const int64_t list = blockIdx.x;
   int32_t* out = a.kept_idx + list * a.kept_ld;
   for (int32_t j = threadIdx.x; j < a.prot; j += kThreads) out[j] = j;
-  if (list == 0)
-    for (int32_t b = threadIdx.x; b < (int32_t)kArrays; b += kThreads) a.ws[b] = 0u;
+  if (threadIdx.x == 0) a.kept_count[list] = a.prot;
+  if (list == 0) {
+    for (int32_t b = threadIdx.x; b < (int32_t)kArrays; b += kThreads)
+      st_dev(a.ws + b, (b == kState + 2) ? a.budget : 0u);  // remaining = B before level 0
+  }
+}
+
+// Resolves the digit of level lvl (run by one workgroup): walks the finished
+// histogram from the top bin down to the bin holding the remaining-th best key
+// among those matching the digits chosen so far, and stores the new state.
+__device__ void resolve_level(uint32_t* ws, int lvl, uint32_t prefix, uint32_t mask,
+                              uint32_t remaining, uint32_t* s_scan) {
+  const int tid = threadIdx.x;
+  const Level L = level_of(lvl);
+  const uint32_t* hist = ws + L.off;
+  const uint32_t per = L.bins / kThreads;             // 8 or 4 bins per thread, top first
+  const uint32_t top = L.bins - per * (uint32_t)tid;  // exclusive upper bin
+  uint32_t h[8];
+  uint32_t c = 0u;
+#pragma unroll
+  for (uint32_t b = 0; b < 8; ++b) {
+    h[b] = (b < per) ? ld_dev(hist + top - 1u - b) : 0u;
+    c += h[b];
+  }
+  uint32_t total;
+  const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
+  const uint32_t excl = incl - c;
+  if (excl < remaining && incl >= remaining) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (uint32_t b = 0; b < 8; ++b) {
+      if (b < per && acc < remaining && acc + h[b] >= remaining) {
+        const uint32_t digit = top - 1u - b;
+        const uint32_t left = remaining - acc;
+        st_dev(ws + kState + 0, prefix | (digit << L.shift));
+        st_dev(ws + kState + 1, mask | ((L.bins - 1u) << L.shift));
+        st_dev(ws + kState + 2, left);
+        st_dev(ws + kState + 3, left == h[b] ? 1u : 0u);  // the bucket is kept whole
+      }
+      acc += h[b];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void global_hist_kernel(GlobalArgs a, int lvl) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_pick[3];
-  const int64_t list = blockIdx.x / a.chunks;
-  const int32_t chunk = blockIdx.x % a.chunks;
-  const Resolved r = resolve(a.ws, lvl, a.budget, s_scan, s_pick);
-  if (lvl > 0 && r.whole_bucket) return;
+  __shared__ uint32_t s_flag;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, blockIdx.x, &list, &i0, &i1);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);  // in flight with the state loads
+  const uint32_t whole = ld_dev(a.ws + kState + 3);
+  const uint32_t prefix = ld_dev(a.ws + kState + 0), mask = ld_dev(a.ws + kState + 1);
+  if (whole) return;  // an earlier level took its bucket whole
   const Level L = level_of(lvl);
   for (uint32_t b = threadIdx.x; b < L.bins; b += kThreads) s_hist[b] = 0u;
   __syncthreads();
-  const float* row = a.scores + list * a.ld;
-  const int32_t i0 = a.prot + chunk * kChunk;
-  const int32_t i1 = min(a.n, i0 + kChunk);
-  for (int32_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    const uint32_t k = rank_key(row[i]);
-    if ((k & r.mask) == r.prefix) atomicAdd(&s_hist[(k >> L.shift) & (L.bins - 1u)], 1u);
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const uint32_t k = keys[u];
+    if (i0 + (int32_t)threadIdx.x + u * kThreads < i1 && (k & mask) == prefix)
+      atomicAdd(&s_hist[(k >> L.shift) & (L.bins - 1u)], 1u);
   }
   __syncthreads();
   for (uint32_t b = threadIdx.x; b < L.bins; b += kThreads) {
     const uint32_t h = s_hist[b];
-    if (h) atomicAdd(&a.ws[L.off + b], h);
+    if (h) __hip_atomic_fetch_add(a.ws + L.off + b, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (last_workgroup(a.ws + kDone + lvl, &s_flag))
+    resolve_level(a.ws, lvl, prefix, mask, ld_dev(a.ws + kState + 2), s_scan);
 }
 
-__device__ __forceinline__ void threshold(const GlobalArgs& a, uint32_t* s_scan, uint32_t* s_pick,
-                                          uint32_t* thr, uint32_t* need_eq) {
-  if (a.mode == kNone) {  // keep no candidate: no key exceeds or equals T with need_eq = 0
-    *thr = 0xffffffffu;
-    *need_eq = 0u;
-  } else if (a.mode == kAll) {
+// Threshold key T and how many keys equal to T are kept.
+__device__ __forceinline__ void threshold(const GlobalArgs& a, uint32_t* thr, uint32_t* need_eq) {
+  if (a.mode == kAll) {
     *thr = 0u;
     *need_eq = 0xffffffffu;
   } else {
-    const Resolved r = resolve(a.ws, 3, a.budget, s_scan, s_pick);
-    *thr = r.prefix;
-    *need_eq = r.whole_bucket ? 0xffffffffu : r.remaining;
+    *thr = ld_dev(a.ws + kState + 0);
+    *need_eq = ld_dev(a.ws + kState + 3) ? 0xffffffffu : ld_dev(a.ws + kState + 2);
   }
 }
 
 __global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a) {
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_pick[3];
-  const int64_t list = blockIdx.x / a.chunks;
-  const int32_t chunk = blockIdx.x % a.chunks;
+  __shared__ uint32_t s_flag;
   uint32_t thr, need_eq;
-  threshold(a, s_scan, s_pick, &thr, &need_eq);
-  const float* row = a.scores + list * a.ld;
-  const int32_t i0 = a.prot + chunk * kChunk;
-  const int32_t i1 = min(a.n, i0 + kChunk);
+  threshold(a, &thr, &need_eq);
+  const int64_t f = blockIdx.x;
+  const int64_t M = a.num_lists * a.chunks;
+  uint32_t* gt_arr = a.ws + kArrays;
+  uint32_t* eq_arr = gt_arr + M;
+  uint32_t* eqx = gt_arr + 2 * M;
+  uint32_t* S = gt_arr + 3 * M;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
   uint32_t gt = 0u, eq = 0u;
-  for (int32_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    const uint32_t k = rank_key(row[i]);
-    gt += (k > thr) ? 1u : 0u;
-    eq += (k == thr) ? 1u : 0u;
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const bool valid = i0 + (int32_t)threadIdx.x + u * kThreads < i1;
+    gt += (valid && keys[u] > thr) ? 1u : 0u;
+    eq += (valid && keys[u] == thr) ? 1u : 0u;
   }
   gt = block_sum<kThreads>(gt, s_scan);
   eq = block_sum<kThreads>(eq, s_scan);
-  const int64_t M = a.num_lists * a.chunks;
-  const int64_t f = (int64_t)blockIdx.x;
   if (threadIdx.x == 0) {
-    a.ws[kArrays + f] = gt;
-    a.ws[kArrays + M + f] = eq;
-    if (blockIdx.x == 0) {
-      a.ws[kState + 0] = thr;
-      a.ws[kState + 1] = need_eq;
-    }
+    st_dev(gt_arr + f, gt);
+    st_dev(eq_arr + f, eq);
   }
-}
+  if (M <= kDirectPrefixItems || !last_workgroup(a.ws + kDone + 3, &s_flag)) return;
 
-__global__ __launch_bounds__(1024) void global_scan_kernel(GlobalArgs a) {
-  constexpr int NT = 1024;
-  __shared__ uint32_t s_scan[NT / kWave];
-  const int64_t M = a.num_lists * a.chunks;
-  const uint32_t* gt = a.ws + kArrays;
-  const uint32_t* eq = gt + M;
-  uint32_t* eqx = a.ws + kArrays + 2 * M;
-  uint32_t* S = a.ws + kArrays + 3 * M;
-  const uint32_t need_eq = (M > 0) ? a.ws[kState + 1] : 0u;
+  // the last workgroup: scans in flat order and per-list counts
+  const int tid = threadIdx.x;
   uint32_t carry = 0u;
-  for (int64_t base = 0; base < M; base += NT) {
-    const int64_t f = base + threadIdx.x;
-    const uint32_t e = (f < M) ? eq[f] : 0u;
+  for (int64_t base = 0; base < M; base += kThreads) {
+    const int64_t g = base + tid;
+    const uint32_t e = (g < M) ? ld_dev(eq_arr + g) : 0u;
     uint32_t total;
-    const uint32_t incl = block_inclusive_scan<NT>(e, s_scan, &total);
-    if (f < M) eqx[f] = carry + incl - e;
+    const uint32_t incl = block_inclusive_scan<kThreads>(e, s_scan, &total);
+    if (g < M) st_dev(eqx + g, carry + incl - e);
     carry += total;
   }
   __syncthreads();
   carry = 0u;
-  for (int64_t base = 0; base < M; base += NT) {
-    const int64_t f = base + threadIdx.x;
+  for (int64_t base = 0; base < M; base += kThreads) {
+    const int64_t g = base + tid;
     uint32_t k = 0u;
-    if (f < M) {
-      const uint32_t x = eqx[f];
+    if (g < M) {
+      const uint32_t x = ld_dev(eqx + g);
       const uint32_t room = (need_eq > x) ? need_eq - x : 0u;
-      k = gt[f] + min(eq[f], room);
+      k = ld_dev(gt_arr + g) + min(ld_dev(eq_arr + g), room);
     }
     uint32_t total;
-    const uint32_t incl = block_inclusive_scan<NT>(k, s_scan, &total);
-    if (f < M) S[f] = carry + incl - k;
+    const uint32_t incl = block_inclusive_scan<kThreads>(k, s_scan, &total);
+    if (g < M) st_dev(S + g, carry + incl - k);
     carry += total;
   }
-  if (threadIdx.x == 0) S[M] = carry;
+  if (tid == 0) st_dev(S + M, carry);
   __syncthreads();
-  for (int64_t list = threadIdx.x; list < a.num_lists; list += NT) {
-    uint32_t kept = 0u;
-    if (a.chunks > 0) kept = S[(list + 1) * a.chunks] - S[list * a.chunks];
-    a.kept_count[list] = a.prot + (int32_t)kept;
-  }
+  for (int64_t l = tid; l < a.num_lists; l += kThreads)
+    a.kept_count[l] = a.prot + (int32_t)(ld_dev(S + (l + 1) * a.chunks) - ld_dev(S + l * a.chunks));
 }
 
 __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a) {
   __shared__ uint32_t s_tile[2 * kWaves];
-  const int64_t list = blockIdx.x / a.chunks;
-  const int32_t chunk = blockIdx.x % a.chunks;
+  uint32_t thr, need_eq;
+  threshold(a, &thr, &need_eq);
+  const int64_t f = blockIdx.x;
   const int64_t M = a.num_lists * a.chunks;
-  const int64_t f = (int64_t)blockIdx.x;
-  const uint32_t thr = a.ws[kState + 0];
-  const uint32_t need_eq = a.ws[kState + 1];
-  const uint32_t* eqx = a.ws + kArrays + 2 * M;
-  const uint32_t* S = a.ws + kArrays + 3 * M;
-  const uint32_t eq0 = eqx[f];
+  uint32_t* eqx = a.ws + kArrays + 2 * M;
+  uint32_t* S = a.ws + kArrays + 3 * M;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  uint32_t eq0, offset;  // keys == T before item f (flat order); kept before f in its list
+  if (M <= kDirectPrefixItems) {
+    // sums over the items before f: all of them for eq, those of f's list for gt and eq
+    uint32_t* gt_arr = a.ws + kArrays;
+    uint32_t* eq_arr = gt_arr + M;
+    const int64_t ls = list * a.chunks;
+    uint32_t e_all = 0u, gt_in = 0u, e_in = 0u;
+    for (int64_t g = threadIdx.x; g < f; g += kThreads) {
+      const uint32_t e = ld_dev(eq_arr + g);
+      e_all += e;
+      if (g >= ls) {
+        gt_in += ld_dev(gt_arr + g);
+        e_in += e;
+      }
+    }
+    eq0 = block_sum<kThreads>(e_all, s_tile);
+    gt_in = block_sum<kThreads>(gt_in, s_tile);
+    e_in = block_sum<kThreads>(e_in, s_tile);
+    // keys == T are kept in flat order, so the run [ls, f) keeps the first
+    // (need_eq - eq before ls) of its e_in, clamped to [0, e_in]
+    const uint32_t eq_ls = eq0 - e_in;
+    const uint32_t room_ls = (need_eq > eq_ls) ? need_eq - eq_ls : 0u;
+    offset = gt_in + min(e_in, room_ls);
+    if (f - ls == a.chunks - 1 && threadIdx.x == 0) {  // last item of its list
+      const uint32_t room_f = (need_eq > eq0) ? need_eq - eq0 : 0u;
+      a.kept_count[list] =
+          a.prot + (int32_t)(offset + ld_dev(gt_arr + f) + min(ld_dev(eq_arr + f), room_f));
+    }
+  } else {
+    eq0 = ld_dev(eqx + f);
+    offset = ld_dev(S + f) - ld_dev(S + list * a.chunks);
+  }
   const uint32_t taken0 = min(eq0, need_eq);
-  int32_t* out = a.kept_idx + list * a.kept_ld + a.prot + (S[f] - S[list * a.chunks]);
-  const float* row = a.scores + list * a.ld;
-  const int32_t i0 = a.prot + chunk * kChunk;
-  const int32_t i1 = min(a.n, i0 + kChunk);
+  int32_t* out = a.kept_idx + list * a.kept_ld + a.prot + offset;
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
   const int wave = threadIdx.x / kWave;
   uint32_t carry_gt = 0u, carry_eq = 0u;
-  for (int32_t base = i0; base < i1; base += kThreads) {
-    const int32_t i = base + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const int32_t i = i0 + threadIdx.x + u * kThreads;
     const bool valid = i < i1;
-    const uint32_t k = valid ? rank_key(row[i]) : 0u;
+    const uint32_t k = keys[u];
     const bool gt = valid && k > thr;
     const bool eq = valid && k == thr;
     const uint64_t bg = __ballot(gt);
@@ -311,27 +384,18 @@ hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kep
   hipLaunchKernelGGL(global_init_kernel, dim3((unsigned)num_lists), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned blocks = (unsigned)(num_lists * chunks);
-  if (blocks > 0 && a.mode == kNormal) {
+  const unsigned items = (unsigned)(num_lists * chunks);
+  if (items == 0 || a.mode == kNone) return hipSuccess;  // the prompts are the whole result
+  if (a.mode == kNormal) {
     for (int lvl = 0; lvl < 3; ++lvl) {
-      hipLaunchKernelGGL(global_hist_kernel, dim3(blocks), dim3(kThreads), 0, stream, a, lvl);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  if (blocks > 0) {
-    hipLaunchKernelGGL(global_count_kernel, dim3(blocks), dim3(kThreads), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(global_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (blocks > 0) {
-    hipLaunchKernelGGL(global_emit_kernel, dim3(blocks), dim3(kThreads), 0, stream, a);
-    e = hipGetLastError();
-  }
-  return e;
+  hipLaunchKernelGGL(global_count_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(global_emit_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace kvevict

@@ -260,6 +260,7 @@ def test_compact_rejects_out_of_range_rows():
     (2, 20000, 0, 0.999, "ties"),
     (16, 4096, 256, 0.1, "constant"),    # every candidate tied
     (1, 1, 0, 1.0, "uniform"),
+    (8200, 100, 10, 0.3, "ties"),        # more items than the direct-prefix limit: scanned once
 ])
 def test_select_global(lists, n, prot, p, kind):
     say(f"select_global lists={lists} n={n} prot={prot} p={p} kind={kind}")
@@ -271,18 +272,21 @@ def test_select_global(lists, n, prot, p, kind):
     counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
     wsb = B.kvevict_select_global_workspace(lists, n, prot, ld=ld, kept_ld=kept_ld, p=p)
     ws = torch.full((wsb,), 0xAB, dtype=torch.uint8, device=DEV)
-    budget = B.kvevict_select_global(kept, kept_ld, counts, torch.from_numpy(s_pad).to(DEV), ld,
-                                     lists, n, prot, p, ws, wsb)
-    torch.cuda.synchronize()
     want_kept, want_counts, want_B = oracle.select_global(s, prot, p)
-    assert budget == want_B
-    got_counts = to_np(counts)
-    assert np.array_equal(got_counts, want_counts)
-    got = to_np(kept)
-    for l in range(lists):
-        c = want_counts[l]
-        assert np.array_equal(got[l, :c], want_kept[l, :c]), l
-        assert np.all(got[l, c:] == -3)
+    scores = torch.from_numpy(s_pad).to(DEV)
+    # three calls on the same workspace: each starts from what the last one left
+    for call in range(3):
+        budget = B.kvevict_select_global(kept, kept_ld, counts, scores, ld, lists, n, prot, p,
+                                         ws, wsb)
+        torch.cuda.synchronize()
+        assert budget == want_B
+        got_counts = to_np(counts)
+        assert np.array_equal(got_counts, want_counts), call
+        got = to_np(kept)
+        for l in range(lists):
+            c = want_counts[l]
+            assert np.array_equal(got[l, :c], want_kept[l, :c]), (call, l)
+            assert np.all(got[l, c:] == -3)
 
 
 # ---------------------------------------------------------------------------
