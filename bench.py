@@ -92,11 +92,15 @@ def time_workload(torch, rounds, cfg, steps, warmup):
     st = rounds.make_state(cfg, "cuda")
     torch.cuda.synchronize()
     round_id = 0
+    survival = None
     if cfg.rounds > 1:
         # repeated rounds: each step is one round of the persistent-budget loop; the
-        # append of r fresh tokens between rounds is input synthesis and stays untimed
+        # append of r fresh tokens between rounds is input synthesis and stays untimed,
+        # and so does the survival bookkeeping on sampled lists
+        survival = rounds.SurvivalTracker(st)
         for _ in range(warmup):
             rounds.run_round(st, round_id)
+            survival.after_round(st)
             rounds.append_tokens(st, round_id)
             rounds.swap(st)
             round_id += 1
@@ -116,6 +120,7 @@ def time_workload(torch, rounds, cfg, steps, warmup):
             timer.mark()
             t1.record()
             st.applied_rounds += 1
+            survival.after_round(st)
             rounds.append_tokens(st, round_id)
             rounds.swap(st)
             round_id += 1
@@ -144,7 +149,7 @@ def time_workload(torch, rounds, cfg, steps, warmup):
     errors = int(st.errors.item())
     out = {"state": st, "ms_per_step": ms_per, "kernels_ms": kern, "kv_bytes": kv_bytes,
            "errors": errors, "applied_rounds": st.applied_rounds - warmup,
-           "budget": st.budget}
+           "budget": st.budget, "survival": survival.report(st) if survival else None}
     return out
 
 
@@ -260,6 +265,8 @@ def main():
         }
         if cfg.select == "global":
             entry["budget"] = r["budget"]
+        if r["survival"] is not None:
+            entry["survival"] = r["survival"]
         if name == "batch":
             head = (cfg, r, entry)
             if not args.no_cpu_baseline:

@@ -16,6 +16,7 @@ rounds it applied.
 
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -175,3 +176,61 @@ def swap(st: RoundState):
     st.k_src, st.k_dst = st.k_dst, st.k_src
     st.v_src, st.v_dst = st.v_dst, st.v_src
     st.src_desc, st.dst_desc = st.dst_desc, st.src_desc
+
+
+# --- measurement: survival of entries across repeated rounds ------------------------
+
+class SurvivalTracker:
+    """Original token id of every slot on sampled lists, carried through each round's kept
+    indices (the HIP path's output).  Measurement only: it runs between rounds, outside the
+    timed round, and moves no K/V data.
+
+    Tokens present before the first round get ids 0..n-1 (their slots); each round's r
+    appended tokens get the next r ids.  The curve is the fraction of the first cache's
+    non-prompt entries still present after each round (Random Attention blog summary,
+    survival paragraph: survivors are redrawn every round), next to the law q^t with
+    q = (K - prot) / (K + r - prot) and the page's prompt-free (K / (K + r))^t.
+    """
+
+    def __init__(self, st: RoundState, stride: int = 16):
+        c = st.cfg
+        self.rows = torch.arange(0, c.lists, stride, device=st.device)
+        self.ids = torch.arange(st.n, device=st.device, dtype=torch.int64).repeat(len(self.rows), 1)
+        self.next_id = st.n
+        self.cohort = (c.prot, st.n)
+        self.curve: list[float] = []
+        self.prompt_survival = 1.0
+        self.slot_coverage = 1.0
+
+    def after_round(self, st: RoundState):
+        c = st.cfg
+        kept_ids = torch.gather(self.ids, 1, st.kept[self.rows].long())
+        ns = len(self.rows)
+        new = torch.arange(self.next_id, self.next_id + c.r, device=st.device,
+                           dtype=torch.int64).repeat(ns, 1)
+        self.ids = torch.cat([kept_ids, new], 1)
+        self.next_id += c.r
+        lo, hi = self.cohort
+        alive = int(((kept_ids >= lo) & (kept_ids < hi)).sum().item())
+        self.curve.append(alive / (ns * (hi - lo)))
+        prompt = torch.arange(c.prot, device=st.device, dtype=torch.int64)
+        self.prompt_survival = min(self.prompt_survival,
+                                   float((kept_ids[:, :c.prot] == prompt).float().mean().item())
+                                   if c.prot else 1.0)
+        # every kept slot holds a distinct token (strictly increasing ids)
+        distinct = bool((kept_ids[:, 1:] > kept_ids[:, :-1]).all().item())
+        self.slot_coverage = min(self.slot_coverage, 1.0 if distinct else 0.0)
+
+    def report(self, st: RoundState) -> dict:
+        c = st.cfg
+        q = (c.K - c.prot) / (c.K + c.r - c.prot)
+        N = len(self.rows) * (self.cohort[1] - self.cohort[0])
+        law = [q ** t for t in range(1, len(self.curve) + 1)]
+        z = [(m - e) / max(math.sqrt(e * (1 - e) / N), 1e-300) for m, e in zip(self.curve, law)]
+        return {"lists_sampled": len(self.rows), "entries_tracked": N,
+                "measured": [round(v, 6) for v in self.curve],
+                "law_q_pow_t": [round(v, 6) for v in law],
+                "page_approx_K_over_K_plus_r_pow_t": [round((c.K / (c.K + c.r)) ** t, 6)
+                                                       for t in range(1, len(self.curve) + 1)],
+                "max_abs_z": max(abs(v) for v in z) if z else 0.0,
+                "prompt_survival": self.prompt_survival, "slot_coverage": self.slot_coverage}

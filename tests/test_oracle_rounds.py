@@ -55,3 +55,36 @@ def test_survival_law(prot):
     if prot == 0:
         # the page's approximation: 1024/1088 = 0.941..., printed as 0.94
         assert round(K / (K + r), 2) == 0.94
+
+
+def test_survival_tracker_bookkeeping():
+    """The bench's survival tracker carries token ids through kept indices exactly as the
+    definition does (checked against a direct replay), on CPU tensors."""
+    import types
+
+    import torch
+
+    from kv_cache_eviction_05_amd.configs import LONGGEN
+    from kv_cache_eviction_05_amd.rounds import SurvivalTracker
+
+    cfg = LONGGEN.small(R=1, L=2, H=4, K=40, r=8, prot=5)
+    n = cfg.K + cfg.r
+    st = types.SimpleNamespace(cfg=cfg, device=torch.device("cpu"), n=n, kept=None)
+    tr = SurvivalTracker(st, stride=3)
+    ids = np.tile(np.arange(n, dtype=np.int64), (cfg.lists, 1))
+    next_id = n
+    for rnd in range(6):
+        s = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, 11, rnd, False, 0, cfg.lists)
+        kept = oracle.select_topk(s, cfg.K, cfg.prot)
+        st.kept = torch.from_numpy(kept)
+        tr.after_round(st)
+        ids = np.concatenate([np.take_along_axis(ids, kept.astype(np.int64), axis=1),
+                              np.tile(np.arange(next_id, next_id + cfg.r), (cfg.lists, 1))], axis=1)
+        next_id += cfg.r
+        assert np.array_equal(tr.ids.numpy(), ids[::3])
+        alive = np.isin(ids[::3, :cfg.K], np.arange(cfg.prot, n)).sum() / (len(ids[::3]) * (n - cfg.prot))
+        assert abs(tr.curve[-1] - alive) < 1e-12
+    rep = tr.report(st)
+    assert rep["prompt_survival"] == 1.0 and rep["slot_coverage"] == 1.0
+    q = (cfg.K - cfg.prot) / (cfg.K + cfg.r - cfg.prot)
+    assert rep["law_q_pow_t"][0] == round(q, 6)
