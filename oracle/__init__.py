@@ -194,3 +194,67 @@ def compact(src: dict, k_src: np.ndarray, v_src: np.ndarray, dst: dict, k_dst: n
                           dp, _ptr(k_dst), _ptr(v_dst), dls, _ptr(dpt), dld,
                           D, H, page_size, _ptr(kept), kept.shape[1], _ptr(kc), K,
                           group_begin, group_end, ipg)
+
+
+# ---------------------------------------------------------------------------
+# Gate-proportional per-layer budgets (GateSight Sec. 4.2; Appendix G,
+# layer_power_budget) and the shared list of a layer (Appendix H)
+# ---------------------------------------------------------------------------
+
+def layer_power_budget(gate, n_body: int, p: float) -> list:
+    """Entries kept per KV head in each attention layer, beyond the protected prefix.
+
+    GateSight Sec. 4.2: layer l keeps K_l proportional to its gate weight w_l per head, with
+    the model-wide total of a flat allocation; Appendix G: integerised by largest remainder so
+    that the total is L * round(p * n_body) (the page's 64 = 16 layers x 4 heads counts every
+    head of every layer; per head the layers sum to L * round(...)), the prompt kept in addition.
+    Readings: the gates are the float32 values given, taken exactly (rational arithmetic);
+    equal remainders go to the lower layer; a layer is capped at n_body and the excess is
+    shared among the others in proportion (the page's gates never reach the cap).
+    """
+    from fractions import Fraction
+
+    w = [Fraction(float(np.float32(g))) for g in gate]
+    if any(x <= 0 for x in w):
+        raise ValueError("gates must be positive")
+    L = len(w)
+    T = L * budget(1, n_body, 0, p)  # L * round(p * n_body), binary64 product, ties to even
+    capped: set = set()
+    while True:
+        free = [l for l in range(L) if l not in capped]
+        S = sum(w[l] for l in free)
+        T2 = T - len(capped) * n_body
+        over = [l for l in free if T2 * w[l] > n_body * S]
+        if not over:
+            break
+        capped.update(over)
+    q = [Fraction(n_body) if l in capped else Fraction(T2) * w[l] / S for l in range(L)]
+    K = [int(x.numerator // x.denominator) for x in q]
+    left = T - sum(K)
+    order = sorted((l for l in range(L) if l not in capped), key=lambda l: (-(q[l] - K[l]), l))
+    for l in order[:left]:
+        K[l] += 1
+    return K
+
+
+def shared_max_scores(scores: np.ndarray, H: int) -> np.ndarray:
+    """One score row per group of H consecutive lists: at each position the score of the head
+    that ranks best (GateSight Appendix H: the KV heads of a layer share one kept list, ranked
+    by the larger of their per-head predictions).  Ranking as everywhere: NaN as -inf, -0 equal
+    to +0; among equal ranks the lowest head's score (its bits) is taken."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    lists, n = s.shape
+    assert lists % H == 0
+    rank = s.astype(np.float64)
+    rank[np.isnan(rank)] = -np.inf
+    best = np.argmax(rank.reshape(-1, H, n), axis=1)  # first maximum: the lowest head
+    return np.take_along_axis(s.reshape(-1, H, n), best[:, None, :], axis=1)[:, 0, :].copy()
+
+
+def shared_kept_count(K: int, prot: int) -> int:
+    """Kept count of a shared layer list: K rounded down to a multiple of four (GateSight
+    Appendix H: the kept count of a layer is a multiple of four, for 4-token blocks)."""
+    k4 = (K // 4) * 4
+    if k4 < prot:
+        raise ValueError("the prompt does not fit a multiple-of-four count below K")
+    return k4
