@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="batch",
-                    help="comma list of batch,paged,paged_shared,global,longgen (or 'all')")
+                    help="comma list of batch,paged,paged_shared,global,longgen,layers,"
+                         "paged_shared_max (or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -54,11 +55,15 @@ def source_hash(path: str) -> str:
 
 def describe(cfg) -> str:
     layout = "paged 16-token pages" if cfg.layout == "paged" else "contiguous"
-    if cfg.select == "global":
+    if cfg.select in ("global", "layers"):
+        rule = ("global top-B" if cfg.select == "global"
+                else "gate-proportional per-layer top-K_l at the same total")
         return (f"{cfg.name}: {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, n={cfg.n}, "
                 f"prot={cfg.prot}, p={cfg.p}, weighted GDN score over 48 GDN layers x 48 heads, "
-                f"global top-B, {layout}")
-    draw = "shared draw per layer" if cfg.shared else "per-head random draw"
+                f"{rule}, {layout}")
+    draw = ("shared draw per layer" if cfg.shared else
+            "one list per layer by the max of per-head random scores, kept count a multiple of 4"
+            if cfg.shared_max else "per-head random draw")
     return (f"{cfg.name}: {cfg.R} requests x {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, "
             f"n={cfg.n}, K={cfg.K}, prot={cfg.prot}, {layout}, {draw}"
             + (f", {cfg.rounds} rounds with r={cfg.r} appended" if cfg.rounds > 1 else ""))
@@ -239,7 +244,8 @@ def main():
     binding.load()
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
-        names = ["batch", "paged", "paged_shared", "global", "longgen"]
+        names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
+                 "paged_shared_max"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None
@@ -263,7 +269,7 @@ def main():
             "applied_rounds": r["applied_rounds"],
             "bad_rows": r["errors"],
         }
-        if cfg.select == "global":
+        if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
         if r["survival"] is not None:
             entry["survival"] = r["survival"]

@@ -143,6 +143,60 @@ kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const flo
                                    int32_t prot, hipStream_t stream);
 
 /*
+ * Pin + per-layer top-K_l (GateSight Sec. 4.2 and Appendix G: every KV head of
+ * attention layer l keeps the protected prefix plus K_l entries, so a layer's
+ * kept cache is a dense prefix of K_l + prot rows per head).
+ *
+ * Groups are (request, layer) pairs, group = request*L + layer; list
+ * (group, head) = group*H + head has its scores at scores + list*ld.  Each
+ * list keeps [0, prot) and the layer_budget[group % L] best of [prot, n) in the
+ * ranking above, writes the kept indices in increasing order to
+ * kept_idx[list*kept_ld + j] and its count prot + layer_budget[layer] to
+ * kept_count[list] (device int32 [num_groups*H]); entries beyond the count are
+ * untouched.
+ * layer_budget  HOST int32 [L] (for example from kvevict_layer_power_budget),
+ *               each in [0, n - prot].
+ * Requires 1 <= L <= 64, num_groups a multiple of L, 0 <= prot <= n, ld >= n,
+ * kept_ld >= prot + max(layer_budget).
+ */
+kvevict_status kvevict_select_topk_layers(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                          const float* scores, int64_t ld, int64_t num_groups,
+                                          int32_t L, int32_t H, int32_t n, int32_t prot,
+                                          const int32_t* layer_budget, hipStream_t stream);
+
+/*
+ * Gate-proportional per-layer budgets (GateSight Sec. 4.2: layer l keeps K_l
+ * entries per head in proportion to its gate weight w_l, with the model-wide
+ * total of a flat allocation; Appendix G, layer_power_budget: integerised by
+ * largest remainder so that the layers' budgets sum to L*round(p*n_body); the
+ * protected prefix is kept in addition).  Host only; enqueues nothing.
+ *
+ * gate    HOST float [L], positive and finite, spanning at most 2^40.
+ * n_body  candidates per list (n - prot); p in [0, 1].
+ * budget  HOST int32 [L] out: K_l.
+ * The shares T*w_l/sum(w) are computed exactly on the float gates; equal
+ * remainders go to the lower layer; a layer whose share passes n_body keeps
+ * n_body and the others share what is left, in proportion.
+ */
+kvevict_status kvevict_layer_power_budget(const float* gate, int32_t L, int32_t n_body, double p,
+                                          int32_t* budget);
+
+/*
+ * Shared list scores of a layer (GateSight Appendix H: the KV heads of a layer
+ * share one kept list, ranked by the larger of their per-head scores).
+ *
+ * For every group g < num_groups and position i < n:
+ *     shared[g*shared_ld + i] = scores[(g*H + h)*ld + i]  for the head h whose
+ * score ranks best (NaN as -inf, -0 equal to +0; the lowest such head, whose
+ * bits are copied).  The shared rows then feed kvevict_select_topk as one list
+ * per group and kvevict_compact with idx_lists_per_group = 1.
+ * Requires H >= 1, ld >= n, shared_ld >= n.
+ */
+kvevict_status kvevict_reduce_max_heads(float* shared, int64_t shared_ld, const float* scores,
+                                        int64_t ld, int64_t num_groups, int32_t H, int32_t n,
+                                        hipStream_t stream);
+
+/*
  * Pin + model-wide top-B ([GS] problem statement: B = L*H*round(p*(n-prot))
  * exclusive of the protected prefix; KVzip-style global top-B).
  *

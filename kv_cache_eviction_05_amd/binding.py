@@ -28,6 +28,7 @@ LAYOUT_CONTIG = 0
 LAYOUT_PAGED = 1
 
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
+           "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -73,8 +74,13 @@ def load():
                                           ctypes.POINTER(_sz), _p]
     lib.kvevict_compact.argtypes = [ctypes.POINTER(KvDesc), _p, _p, ctypes.POINTER(KvDesc), _p, _p,
                                     _p, _i64, _p, _i32, _i64, _i32, _p, _p]
+    lib.kvevict_select_topk_layers.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i32, _i32, _i32,
+                                               _i32, _p, _p]
+    lib.kvevict_layer_power_budget.argtypes = [_p, _i32, _i32, _dbl, _p]
+    lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
-                 "kvevict_select_global", "kvevict_compact"):
+                 "kvevict_select_topk_layers", "kvevict_layer_power_budget",
+                 "kvevict_reduce_max_heads", "kvevict_select_global", "kvevict_compact"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -180,6 +186,41 @@ def kvevict_select_topk(kept_idx, kept_ld, scores, ld, num_lists, n, K, prot, st
     _check(load().kvevict_select_topk(_ptr(kept_idx), kept_ld, _ptr(scores), ld, num_lists, n, K,
                                       prot, _stream(stream)),
            "kvevict_select_topk")
+
+
+def kvevict_select_topk_layers(kept_idx, kept_ld, kept_count, scores, ld, num_groups, L, H, n,
+                               prot, layer_budget, stream=None):
+    budget = [int(x) for x in layer_budget]
+    if len(budget) != L:
+        raise ValueError("layer_budget must have L entries")
+    most = max(budget) if budget else 0
+    _need(scores, torch.float32, _rows(num_groups * H, ld, n), "scores")
+    _need(kept_idx, torch.int32, _rows(num_groups * H, kept_ld, prot + most), "kept_idx")
+    _need(kept_count, torch.int32, num_groups * H, "kept_count")
+    arr = (ctypes.c_int32 * L)(*budget)
+    _check(load().kvevict_select_topk_layers(_ptr(kept_idx), kept_ld, _ptr(kept_count),
+                                             _ptr(scores), ld, num_groups, L, H, n, prot, arr,
+                                             _stream(stream)),
+           "kvevict_select_topk_layers")
+
+
+def kvevict_layer_power_budget(gate, n_body, p) -> list:
+    """Host computation: per-layer kept counts per head (no GPU work)."""
+    g = [float(x) for x in gate]
+    L = len(g)
+    garr = (ctypes.c_float * max(L, 1))(*g)
+    out = (ctypes.c_int32 * max(L, 1))()
+    _check(load().kvevict_layer_power_budget(garr, L, n_body, p, out),
+           "kvevict_layer_power_budget")
+    return [int(out[i]) for i in range(L)]
+
+
+def kvevict_reduce_max_heads(shared, shared_ld, scores, ld, num_groups, H, n, stream=None):
+    _need(scores, torch.float32, _rows(num_groups * H, ld, n), "scores")
+    _need(shared, torch.float32, _rows(num_groups, shared_ld, n), "shared")
+    _check(load().kvevict_reduce_max_heads(_ptr(shared), shared_ld, _ptr(scores), ld, num_groups,
+                                           H, n, _stream(stream)),
+           "kvevict_reduce_max_heads")
 
 
 def kvevict_select_global_workspace(num_lists, n, prot, ld=None, kept_ld=None, p=0.0) -> int:

@@ -16,6 +16,12 @@ Five synthetic workloads, each a single-GPU share at its real shape:
             x 48 heads, then one model-wide top-B (GateSight-shaped).
   longgen   128 x 36 x 8, D=128, K=3072, r=64, prot=557: 30 consecutive rounds,
             64 fresh tokens appended between rounds, rescored every round.
+  layers    the global round's shape with GateSight's per-layer allocation:
+            K_l proportional to a gate weight per layer, at the same total.
+  paged_shared_max
+            the paged round with one kept list per (request, layer), ranked
+            by the larger of the per-head random scores, kept count a
+            multiple of four.
 
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
@@ -40,8 +46,9 @@ class RoundConfig:
     layout: str = "contig"     # "contig" or "paged"
     page_size: int = 16
     scorer: str = "random"     # "random" or "weighted"
-    select: str = "topk"       # "topk" or "global"
+    select: str = "topk"       # "topk", "global" or "layers" (gate-proportional budgets)
     shared: bool = False       # one draw per (request, layer), applied to all heads
+    shared_max: bool = False   # one list per (request, layer) ranked by the max over heads
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -60,8 +67,13 @@ class RoundConfig:
 
     @property
     def lists(self) -> int:
-        """Number of score/index lists: one per (request, layer, head), or per layer if shared."""
-        return self.groups if self.shared else self.groups * self.H
+        """Number of index lists: one per (request, layer, head), or per layer if shared."""
+        return self.groups if (self.shared or self.shared_max) else self.groups * self.H
+
+    @property
+    def kept_shared(self) -> int:
+        """Kept count of a shared-max list: K rounded down to a multiple of four."""
+        return (self.K // 4) * 4
 
     @property
     def row_bytes(self) -> int:
@@ -97,5 +109,10 @@ PAGED_SHARED = replace(PAGED, name="paged_shared", shared=True)
 GLOBAL = RoundConfig("global", R=1, L=16, H=4, D=256, K=0, r=0, prot=256, scorer="weighted",
                      select="global", p=0.25, n_override=32768)
 LONGGEN = RoundConfig("longgen", R=128, L=36, H=8, D=128, K=3072, r=64, prot=557, rounds=30)
+# next rows: GateSight's deployed per-layer allocation at the global round's shape and total,
+# and the shared list of a layer ranked by the max over its KV heads (kept count % 4 == 0)
+LAYERS = replace(GLOBAL, name="layers", select="layers")
+PAGED_SHARED_MAX = replace(PAGED, name="paged_shared_max", shared_max=True)
 
-ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN)}
+ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
+                           PAGED_SHARED_MAX)}

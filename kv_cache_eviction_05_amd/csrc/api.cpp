@@ -8,6 +8,7 @@
 #include <cfenv>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "kvevict.h"
 #include "kvevict_launch.hpp"
@@ -110,8 +111,111 @@ kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const flo
   if (num_lists < 0 || num_lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
   if (prot < 0 || K < prot || n < K || ld < n || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
   if (num_lists > 0 && K > 0 && (!kept_idx || !scores)) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_select_topk(kept_idx, kept_ld, nullptr, scores, ld, num_lists,
+                                                n, K, prot, 0, 1, nullptr, stream));
+}
+
+kvevict_status kvevict_select_topk_layers(int32_t* kept_idx, int64_t kept_ld,
+                                          int32_t* kept_count, const float* scores, int64_t ld,
+                                          int64_t num_groups, int32_t L, int32_t H, int32_t n,
+                                          int32_t prot, const int32_t* layer_budget,
+                                          hipStream_t stream) {
+  if (num_groups < 0 || L < 1 || L > kvevict::kMaxBudgetLayers || H < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups % L != 0) return KVEVICT_ERR_INVALID_ARG;  // whole requests of L layers
+  if (prot < 0 || n < prot || ld < n || !layer_budget) return KVEVICT_ERR_INVALID_ARG;
+  int32_t most = 0;
+  for (int32_t l = 0; l < L; ++l) {
+    if (layer_budget[l] < 0 || layer_budget[l] > n - prot) return KVEVICT_ERR_INVALID_ARG;
+    most = layer_budget[l] > most ? layer_budget[l] : most;
+  }
+  if (kept_ld < prot + most) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_groups * H;
+  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (lists > 0 && (!kept_idx || !kept_count || !scores)) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_select_topk(kept_idx, kept_ld, kept_count, scores, ld, lists,
+                                                n, prot, prot, L, H, layer_budget, stream));
+}
+
+kvevict_status kvevict_reduce_max_heads(float* shared, int64_t shared_ld, const float* scores,
+                                        int64_t ld, int64_t num_groups, int32_t H, int32_t n,
+                                        hipStream_t stream) {
+  if (num_groups < 0 || H < 1 || n < 0 || ld < n || shared_ld < n) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > 0 && n > 0 && (!shared || !scores)) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(
-      kvevict::launch_select_topk(kept_idx, kept_ld, scores, ld, num_lists, n, K, prot, stream));
+      kvevict::launch_reduce_max_heads(shared, shared_ld, scores, ld, num_groups, H, n, stream));
+}
+
+kvevict_status kvevict_layer_power_budget(const float* gate, int32_t L, int32_t n_body, double p,
+                                          int32_t* budget) {
+  // Exact arithmetic on the float gates: gate_l = m_l * 2^e_l with m_l < 2^24, scaled
+  // to integers w_l = m_l * 2^(e_l - e_min) (gates may span at most 2^40).
+  if (!gate || !budget || L < 1 || L > 4096 || n_body < 0) return KVEVICT_ERR_INVALID_ARG;
+  if (!(p >= 0.0 && p <= 1.0)) return KVEVICT_ERR_INVALID_ARG;
+  typedef unsigned __int128 u128;
+  std::vector<uint32_t> mant(L);
+  std::vector<int> expo(L);
+  int emin = 1 << 30, emax = -(1 << 30);
+  for (int32_t l = 0; l < L; ++l) {
+    const float g = gate[l];
+    if (!(g > 0.0f) || !std::isfinite(g)) return KVEVICT_ERR_INVALID_ARG;
+    int e = 0;
+    const float f = std::frexp(g, &e);  // g = f * 2^e, f in [0.5, 1)
+    mant[l] = (uint32_t)std::ldexp(f, 24);
+    expo[l] = e - 24;
+    emin = expo[l] < emin ? expo[l] : emin;
+    emax = expo[l] > emax ? expo[l] : emax;
+  }
+  if (emax - emin > 40) return KVEVICT_ERR_INVALID_ARG;
+  std::vector<u128> w(L);
+  for (int32_t l = 0; l < L; ++l) w[l] = (u128)mant[l] << (expo[l] - emin);
+  // flat per-list budget round(p * n_body): binary64 product, ties to even
+  const int saved = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  const int64_t flat = (int64_t)std::nearbyint(p * (double)n_body);
+  std::fesetround(saved);
+  const int64_t T = (int64_t)L * flat;
+  // layers whose proportional share passes n_body are capped there; the rest share what is left
+  std::vector<char> capped(L, 0);
+  int64_t ncap = 0;
+  u128 S = 0;
+  int64_t T2 = T;
+  for (;;) {
+    S = 0;
+    for (int32_t l = 0; l < L; ++l)
+      if (!capped[l]) S += w[l];
+    T2 = T - ncap * (int64_t)n_body;
+    bool more = false;
+    for (int32_t l = 0; l < L; ++l) {
+      if (!capped[l] && (u128)T2 * w[l] > (u128)n_body * S) {
+        capped[l] = 1;
+        ++ncap;
+        more = true;
+      }
+    }
+    if (!more) break;
+  }
+  // floors of the shares, then one more for the largest remainders (ties: lower layer)
+  std::vector<u128> rem(L, 0);
+  int64_t given = 0;
+  for (int32_t l = 0; l < L; ++l) {
+    if (capped[l]) {
+      budget[l] = n_body;
+    } else {
+      const u128 q = (u128)T2 * w[l];
+      budget[l] = (int32_t)(q / S);
+      rem[l] = q % S;
+    }
+    given += budget[l];
+  }
+  for (int64_t left = T - given; left > 0; --left) {
+    int32_t pick = -1;
+    for (int32_t l = 0; l < L; ++l)
+      if (!capped[l] && rem[l] != (u128)-1 && (pick < 0 || rem[l] > rem[pick])) pick = l;
+    if (pick < 0) return KVEVICT_ERR_INVALID_ARG;  // unreachable: T <= L * n_body
+    budget[pick] += 1;
+    rem[pick] = (u128)-1;  // taken
+  }
+  return KVEVICT_OK;
 }
 
 kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,

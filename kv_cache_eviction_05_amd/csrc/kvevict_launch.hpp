@@ -23,9 +23,17 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
                                  int32_t w_slots, const WindowTable& win, int32_t L, int32_t H,
                                  int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
 
-hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, const float* scores, int64_t ld,
-                              int64_t num_lists, int32_t n, int32_t K, int32_t prot,
-                              hipStream_t stream);
+constexpr int kMaxBudgetLayers = 64;
+
+// Per-head top-K: every list keeps K (layer_kk == nullptr) or, with per-layer
+// budgets, prot + layer_kk[(list / H) % L]; kept_count (optional) receives the count.
+hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                              const float* scores, int64_t ld, int64_t num_lists, int32_t n,
+                              int32_t K, int32_t prot, int32_t L, int32_t H,
+                              const int32_t* layer_kk, hipStream_t stream);
+
+hipError_t launch_reduce_max_heads(float* out, int64_t out_ld, const float* scores, int64_t ld,
+                                   int64_t num_groups, int32_t H, int32_t n, hipStream_t stream);
 
 size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot);
 

@@ -1,5 +1,8 @@
 // Pin + per-head top-K ("Random Attention" blog summary, Algorithm 1: prompt
-// pinned to +inf, top-K per KV head, return the keep set).
+// pinned to +inf, top-K per KV head, return the keep set), with the per-layer
+// budgets of GateSight (Sec. 4.2, Appendix G: every head of layer l keeps its
+// prompt plus K_l entries), and the shared list of a layer (Appendix H: one
+// list per layer ranked by the larger of its per-head scores).
 //
 // One workgroup (256 threads, 4 waves) per list.  The n - prot candidate keys
 // (rank_key of the score) are staged in LDS; an 8-bit-digit radix select
@@ -18,12 +21,23 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int32_t kMaxLdsKeys = 15360;  // 60 KiB of keys (+ ~1 KiB static LDS)
 
+struct TopkArgs {
+  int32_t* kept_idx;
+  int64_t kept_ld;
+  int32_t* kept_count;  // optional: prot + kept candidates of each list
+  const float* scores;
+  int64_t ld;
+  int32_t n, K, prot;
+  int32_t L, H;                       // L > 0: list (g, h) = g*H + h keeps kk[g % L]
+  int32_t kk[kMaxBudgetLayers];       // candidates kept per head in each layer
+};
+
 template <bool kKeysInLds>
-__global__ __launch_bounds__(kThreads) void select_topk_kernel(int32_t* __restrict__ kept_idx,
-                                                              int64_t kept_ld,
-                                                              const float* __restrict__ scores,
-                                                              int64_t ld, int32_t n, int32_t K,
-                                                              int32_t prot) {
+__global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
+  int32_t* __restrict__ kept_idx = a.kept_idx;
+  const float* __restrict__ scores = a.scores;
+  const int64_t kept_ld = a.kept_ld, ld = a.ld;
+  const int32_t n = a.n, prot = a.prot;
   extern __shared__ uint32_t s_keys[];
   __shared__ uint32_t s_hist[256];
   __shared__ uint32_t s_scan[kWaves];
@@ -34,11 +48,12 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(int32_t* __restri
   const float* row = scores + list * ld;
   int32_t* out = kept_idx + list * kept_ld;
   const int32_t m = n - prot;  // candidates
-  const int32_t kk = K - prot; // candidates to keep
+  const int32_t kk = a.L > 0 ? a.kk[(list / a.H) % a.L] : a.K - prot;  // candidates to keep
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
 
   for (int32_t j = tid; j < prot; j += kThreads) out[j] = j;
+  if (a.kept_count && tid == 0) a.kept_count[list] = prot + kk;
   if (kk <= 0) return;
 
   if (kKeysInLds) {
@@ -126,20 +141,74 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(int32_t* __restri
 
 }  // namespace
 
-hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, const float* scores, int64_t ld,
-                              int64_t num_lists, int32_t n, int32_t K, int32_t prot,
-                              hipStream_t stream) {
+hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                              const float* scores, int64_t ld, int64_t num_lists, int32_t n,
+                              int32_t K, int32_t prot, int32_t L, int32_t H,
+                              const int32_t* layer_kk, hipStream_t stream) {
   if (num_lists == 0) return hipSuccess;
+  TopkArgs a;
+  a.kept_idx = kept_idx;
+  a.kept_ld = kept_ld;
+  a.kept_count = kept_count;
+  a.scores = scores;
+  a.ld = ld;
+  a.n = n;
+  a.K = K;
+  a.prot = prot;
+  a.L = layer_kk ? L : 0;
+  a.H = H;
+  for (int32_t l = 0; l < kMaxBudgetLayers; ++l) a.kk[l] = (layer_kk && l < L) ? layer_kk[l] : 0;
   const int32_t m = n - prot;
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
     hipLaunchKernelGGL(select_topk_kernel<true>, dim3((unsigned)num_lists), dim3(kThreads), lds,
-                       stream, kept_idx, kept_ld, scores, ld, n, K, prot);
+                       stream, a);
   } else {
     hipLaunchKernelGGL(select_topk_kernel<false>, dim3((unsigned)num_lists), dim3(kThreads), 0,
-                       stream, kept_idx, kept_ld, scores, ld, n, K, prot);
+                       stream, a);
   }
   return hipGetLastError();
+}
+
+namespace {
+
+// Shared score of each (group, position): the score of the head whose
+// rank_key is largest, the lowest head among equals (its bits are kept).
+__global__ __launch_bounds__(kThreads) void reduce_max_heads_kernel(
+    float* __restrict__ out, int64_t out_ld, const float* __restrict__ scores, int64_t ld,
+    int64_t g0, int32_t H, int32_t n) {
+  const int64_t g = g0 + blockIdx.y;
+  const int32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const float* base = scores + g * H * ld + i;
+  float best = base[0];
+  uint32_t best_key = rank_key(best);
+  for (int32_t h = 1; h < H; ++h) {
+    const float v = base[h * ld];
+    const uint32_t k = rank_key(v);
+    if (k > best_key) {
+      best = v;
+      best_key = k;
+    }
+  }
+  out[g * out_ld + i] = best;
+}
+
+}  // namespace
+
+hipError_t launch_reduce_max_heads(float* out, int64_t out_ld, const float* scores, int64_t ld,
+                                   int64_t num_groups, int32_t H, int32_t n, hipStream_t stream) {
+  if (num_groups == 0 || n == 0) return hipSuccess;
+  const unsigned bx = (unsigned)((n + kThreads - 1) / kThreads);
+  const int64_t kMaxY = 65535;
+  for (int64_t g0 = 0; g0 < num_groups; g0 += kMaxY) {
+    const int64_t rows = (num_groups - g0 < kMaxY) ? num_groups - g0 : kMaxY;
+    hipLaunchKernelGGL(reduce_max_heads_kernel, dim3(bx, (unsigned)rows), dim3(kThreads), 0,
+                       stream, out, out_ld, scores, ld, g0, H, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvevict

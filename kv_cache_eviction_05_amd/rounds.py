@@ -52,6 +52,8 @@ class RoundState:
     n: int = 0
     applied_rounds: int = 0
     budget: int = 0
+    layer_budget: list = field(default_factory=list)
+    head_scores: torch.Tensor | None = None  # per-head scores before the max over heads
 
     @property
     def idx_lists(self) -> int:
@@ -60,8 +62,10 @@ class RoundState:
     def kv_bytes_moved(self) -> int:
         """Read + write bytes of the kept K and V rows of one round."""
         c = self.cfg
-        if c.select == "global":
+        if c.select in ("global", "layers"):
             rows = int(self.kept_count.sum().item())
+        elif c.shared_max:
+            rows = c.groups * c.H * c.kept_shared
         else:
             rows = c.groups * c.H * c.K
         return rows * c.row_bytes * 2 * 2
@@ -95,14 +99,21 @@ def _desc_pair(cfg: RoundConfig, n_src: int, cap_dst: int, device, seed: int):
 def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) -> RoundState:
     device = torch.device(device)
     n = cfg.n
-    cap_dst = n if cfg.select == "global" else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
+    cap_dst = n if cfg.select in ("global", "layers") else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
     ks, vs, kd, vd, sd, dd, spt, dpt = _desc_pair(cfg, n, cap_dst, device, kv_seed)
     lists = cfg.lists if cfg.select == "topk" else cfg.groups * cfg.H
     scores = torch.empty((lists, n), dtype=torch.float32, device=device)
-    kept_cols = n if cfg.select == "global" else cfg.K
+    kept_cols = n if cfg.select in ("global", "layers") else cfg.K
     kept = torch.zeros((lists, kept_cols), dtype=torch.int32, device=device)
     st = RoundState(cfg, device, ks, vs, kd, vd, scores, kept, sd, dd,
                     torch.zeros(1, dtype=torch.int32, device=device), src_pt=spt, dst_pt=dpt, n=n)
+    if cfg.shared_max:
+        st.head_scores = torch.empty((cfg.groups * cfg.H, n), dtype=torch.float32, device=device)
+    if cfg.select == "layers":
+        st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
+        st.layer_budget = B.kvevict_layer_power_budget(synth.layer_gates(cfg.L, synth.SEED_GATES),
+                                                       n - cfg.prot, cfg.p)
+        st.budget = sum(st.layer_budget) * cfg.R * cfg.H  # non-prompt entries kept
     if cfg.select == "global":
         st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
         st.workspace_bytes = B.kvevict_select_global_workspace(lists, n, cfg.prot, p=cfg.p)
@@ -119,7 +130,14 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
 
 def score(st: RoundState, round_id: int, stream=None):
     c = st.cfg
-    if c.scorer == "random":
+    if c.scorer == "random" and c.shared_max:
+        # per-head draws, then one list per (request, layer) by the max over its heads
+        hs = st.head_scores
+        B.kvevict_score_random(hs, hs.shape[1], c.R, c.L, c.H, st.n, c.prot, c.seed, round_id,
+                               False, stream)
+        B.kvevict_reduce_max_heads(st.scores, st.scores.shape[1], hs, hs.shape[1], c.groups, c.H,
+                                   st.n, stream)
+    elif c.scorer == "random":
         B.kvevict_score_random(st.scores, st.scores.shape[1], c.R, c.L, c.H, st.n, c.prot, c.seed,
                                round_id, c.shared, stream)
     else:
@@ -133,8 +151,13 @@ def select(st: RoundState, stream=None):
     c = st.cfg
     lists = st.scores.shape[0]
     if c.select == "topk":
+        K = c.kept_shared if c.shared_max else c.K
         B.kvevict_select_topk(st.kept, st.kept.shape[1], st.scores, st.scores.shape[1], lists, st.n,
-                              c.K, c.prot, stream)
+                              K, c.prot, stream)
+    elif c.select == "layers":
+        B.kvevict_select_topk_layers(st.kept, st.kept.shape[1], st.kept_count, st.scores,
+                                     st.scores.shape[1], c.groups, c.L, c.H, st.n, c.prot,
+                                     st.layer_budget, stream)
     else:
         st.budget = B.kvevict_select_global(st.kept, st.kept.shape[1], st.kept_count, st.scores,
                                             st.scores.shape[1], lists, st.n, c.prot, c.p,
@@ -144,10 +167,10 @@ def select(st: RoundState, stream=None):
 def compact(st: RoundState, stream=None):
     c = st.cfg
     if c.select == "topk":
-        K, count = c.K, None
+        K, count = (c.kept_shared if c.shared_max else c.K), None
     else:
         K, count = st.n, st.kept_count
-    ipg = 1 if c.shared else c.H
+    ipg = 1 if (c.shared or c.shared_max) else c.H
     B.kvevict_compact(st.src_desc, st.k_src, st.v_src, st.dst_desc, st.k_dst, st.v_dst, st.kept,
                       st.kept.shape[1], count, K, c.groups, ipg, st.errors, stream)
 

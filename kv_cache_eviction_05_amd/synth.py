@@ -11,7 +11,9 @@ Distributions follow the workloads the pages describe:
     magnitude |v| = exp(N(0,1)) (log-normal), planar [G][n][Hg] fp32
     (GateSight, native GDN signals paragraph);
   * per-head weights N(0, 1), [L][H][slots][Hg] fp32;
-  * page tables: seeded random permutations of a page pool.
+  * page tables: seeded random permutations of a page pool;
+  * layer gate weights: log-uniform over the page's measured range 0.022 to
+    0.459 (GateSight Sec. 4.2), float32 [L].
 
 Every generator takes an explicit seed and device; the same call on the same
 device returns the same tensor.
@@ -27,6 +29,7 @@ SEED_SIGNALS = 2
 SEED_WEIGHTS = 3
 SEED_PAGES = 4
 SEED_APPEND = 5
+SEED_GATES = 6
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -95,3 +98,11 @@ def uniform_scores(lists: int, n: int, seed: int, device) -> torch.Tensor:
     """fp32 [lists][n] scores uniform in [0, 1)."""
     g = _gen(seed, device)
     return torch.rand((lists, n), generator=g, device=device).contiguous()
+
+
+def layer_gates(L: int, seed: int) -> list:
+    """float32 gate weights [L], log-uniform over [0.022, 0.459] (host list)."""
+    g = _gen(seed, "cpu")
+    u = torch.rand((L,), generator=g, dtype=torch.float64)
+    lo, hi = torch.log(torch.tensor(0.022, dtype=torch.float64)), torch.log(torch.tensor(0.459, dtype=torch.float64))
+    return [float(x) for x in torch.exp(lo + u * (hi - lo)).to(torch.float32)]

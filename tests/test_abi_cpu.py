@@ -27,8 +27,9 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
-                          "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
-                          "kvevict_abi_version"}
+                          "kvevict_select_topk_layers", "kvevict_layer_power_budget",
+                          "kvevict_reduce_max_heads", "kvevict_select_global", "kvevict_compact",
+                          "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
@@ -135,3 +136,58 @@ def test_compact_validation():
     assert call(src, small) == B.KVEVICT_ERR_INVALID_ARG  # 63 pages x 16 < K = 1024
     weird = B.KvDesc(7, D, H, 16, 100, 0, FAKE, 63)
     assert call(weird, dst) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_layer_power_budget_matches_the_oracle():
+    """The library's exact largest-remainder budgets equal the oracle's rational ones (host only)."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(5)
+    cases = [([1, 2, 3, 4], 100, 0.3), ([1, 2, 4], 12, 1 / 3), ([1, 1, 2], 4, 0.5),
+             ([0.1] * 16, 32512, 0.25), ([0.05, 0.4, 0.2], 500, 1.0), ([0.02, 0.02, 0.9], 100, 0.6),
+             (np.geomspace(0.022, 0.459, 16), 32512, 0.25), ([0.3], 7, 0.5), ([0.5, 0.5], 0, 0.7)]
+    for _ in range(200):
+        L = int(rng.integers(1, 70))
+        gate = np.exp(rng.uniform(np.log(0.022), np.log(0.459), L)).astype(np.float32)
+        if rng.random() < 0.2:  # repeated gates: equal remainders
+            gate[rng.integers(0, L, L // 2)] = gate[0]
+        cases.append((gate, int(rng.integers(0, 50000)), float(rng.uniform(0, 1))))
+    for gate, n_body, p in cases:
+        g32 = np.asarray(gate, dtype=np.float32)
+        assert B.kvevict_layer_power_budget(g32, n_body, p) == \
+            oracle.layer_power_budget(g32, n_body, p), (list(g32), n_body, p)
+
+
+def test_layer_power_budget_validation():
+    f = (ctypes.c_float * 3)(0.1, 0.2, 0.3)
+    bad = (ctypes.c_float * 3)(0.1, 0.0, 0.3)
+    nan = (ctypes.c_float * 2)(0.1, float("nan"))
+    span = (ctypes.c_float * 2)(1.0, 1e-20)
+    out = (ctypes.c_int32 * 3)()
+    assert status("kvevict_layer_power_budget", f, 3, 100, 0.5, out) == B.KVEVICT_OK
+    assert status("kvevict_layer_power_budget", bad, 3, 100, 0.5, out) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_layer_power_budget", nan, 2, 100, 0.5, out) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_layer_power_budget", span, 2, 100, 0.5, out) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_layer_power_budget", f, 3, 100, 1.5, out) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_layer_power_budget", f, 0, 100, 0.5, out) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_layer_power_budget", None, 3, 100, 0.5, out) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_select_topk_layers_and_reduce_validation():
+    b = (ctypes.c_int32 * 2)(10, 20)
+    over = (ctypes.c_int32 * 2)(10, 100)
+    # groups not a multiple of L, L out of range, a budget above n - prot, kept_ld too small
+    assert status("kvevict_select_topk_layers", FAKE, 64, FAKE, FAKE, 64, 3, 2, 4, 64, 8, b, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 64, FAKE, FAKE, 64, 4, 0, 4, 64, 8, b, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 64, FAKE, FAKE, 64, 4, 65, 4, 64, 8, b, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 64, FAKE, FAKE, 64, 4, 2, 4, 64, 8, over, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 27, FAKE, FAKE, 64, 4, 2, 4, 64, 8, b, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 64, None, FAKE, 64, 4, 2, 4, 64, 8, b, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_select_topk_layers", FAKE, 64, FAKE, FAKE, 64, 4, 2, 4, 64, 8, None, None) == B.KVEVICT_ERR_INVALID_ARG
+    # reduce: ld < n, out ld < n, H < 1, null pointers
+    assert status("kvevict_reduce_max_heads", FAKE, 64, FAKE, 63, 2, 4, 64, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_reduce_max_heads", FAKE, 63, FAKE, 64, 2, 4, 64, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_reduce_max_heads", FAKE, 64, FAKE, 64, 2, 0, 64, None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_reduce_max_heads", None, 64, FAKE, 64, 2, 4, 64, None) == B.KVEVICT_ERR_INVALID_ARG

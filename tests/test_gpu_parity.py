@@ -379,3 +379,61 @@ def test_score_weighted_special_signals():
     rel = np.abs(got[fin] - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30)
     assert rel.max() <= 1e-5
     assert np.isnan(want).any() and np.isinf(want[:, prot:]).any()  # the case is exercised
+
+
+# ---------------------------------------------------------------------------
+# per-layer budgets and the shared list of a layer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,L,H,n,prot,kind", [
+    (2, 3, 4, 700, 50, "uniform"),
+    (1, 5, 2, 300, 0, "ties"),
+    (3, 2, 3, 257, 256, "uniform"),      # one candidate per list
+    (2, 4, 2, 600, 10, "special"),
+])
+def test_select_topk_layers(R, L, H, n, prot, kind):
+    say(f"select_topk_layers R={R} L={L} H={H} n={n} prot={prot} kind={kind}")
+    lists = R * L * H
+    s = make_scores(kind, lists, n, seed=lists + n)
+    rng = np.random.default_rng(n)
+    gate = np.exp(rng.uniform(np.log(0.022), np.log(0.459), L)).astype(np.float32)
+    budget = oracle.layer_power_budget(gate, n - prot, 0.4)
+    budget[0] = 0                        # a layer that keeps only its prompt
+    budget[-1] = n - prot                # a layer that keeps everything
+    assert B.kvevict_layer_power_budget(gate, n - prot, 0.4)[1:-1] == budget[1:-1]
+    kept_ld = n + 3
+    kept = torch.full((lists, kept_ld), -3, dtype=torch.int32, device=DEV)
+    counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    B.kvevict_select_topk_layers(kept, kept_ld, counts, torch.from_numpy(s).to(DEV), n, R * L, L,
+                                 H, n, prot, budget)
+    torch.cuda.synchronize()
+    got, got_c = to_np(kept), to_np(counts)
+    for lst in range(lists):
+        layer = (lst // H) % L
+        K = prot + budget[layer]
+        assert got_c[lst] == K
+        want = oracle.select_topk(s[lst:lst + 1], K, prot)[0]
+        assert np.array_equal(got[lst, :K], want), lst
+        assert np.all(got[lst, K:] == -3)
+
+
+@pytest.mark.parametrize("G,H,n,pad", [(5, 4, 1000, 3), (3, 1, 77, 0), (2, 8, 4099, 1)])
+def test_reduce_max_heads(G, H, n, pad):
+    say(f"reduce_max_heads G={G} H={H} n={n}")
+    rng = np.random.default_rng(G * n)
+    s = rng.integers(0, 6, (G * H, n)).astype(np.float32) / 5.0  # many equal ranks across heads
+    pick = rng.random((G * H, n))
+    s[pick < 0.05] = np.nan
+    s[(pick >= 0.05) & (pick < 0.08)] = -0.0
+    s[(pick >= 0.08) & (pick < 0.1)] = -np.inf
+    s[(pick >= 0.1) & (pick < 0.11)] = np.inf
+    ld = n + pad
+    s_pad = np.full((G * H, ld), 7.0, np.float32)
+    s_pad[:, :n] = s
+    out = torch.full((G, n + 2), 5.0, dtype=torch.float32, device=DEV)
+    B.kvevict_reduce_max_heads(out, n + 2, torch.from_numpy(s_pad).to(DEV), ld, G, H, n)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    want = oracle.shared_max_scores(s, H)
+    assert np.array_equal(got[:, :n].view(np.uint32), want.view(np.uint32))  # bit for bit
+    assert np.all(got[:, n:] == 5.0)

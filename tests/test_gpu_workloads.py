@@ -257,3 +257,72 @@ def test_longgen_rounds_replayed_by_oracle():
         assert abs(got - e) < 3 * math.sqrt(e * (1 - e) / N) + 1e-12, (t, got, e)
     del st
     free()
+
+
+def test_paged_shared_max_round_sampled():
+    """Paged round with one list per (request, layer) by the max of the per-head scores and a
+    kept count rounded down to a multiple of four: sampled groups against the oracle."""
+    cfg = configs.PAGED_SHARED_MAX.small(R=8)
+    say("paged shared-max round: allocating")
+    st = rounds.make_state(cfg, DEV)
+    rounds.run_round(st, round_id=5)
+    torch.cuda.synchronize()
+    assert int(st.errors.item()) == 0
+    K4 = cfg.kept_shared
+    assert K4 % 4 == 0 and K4 == oracle.shared_kept_count(cfg.K, cfg.prot)
+    check_kept_properties(st.kept, K4, cfg.prot, cfg.n)
+    ps, H, D = cfg.page_size, cfg.H, cfg.D
+    src_pt, dst_pt = st.src_pt.cpu().numpy(), st.dst_pt.cpu().numpy()
+    for g in sample_lists(cfg.groups, 8, seed=5):
+        heads = oracle.score_random(cfg.L, H, cfg.n, cfg.prot, cfg.seed, 5, False, g * H, g * H + H)
+        want_s = oracle.shared_max_scores(heads, H)
+        assert np.array_equal(st.scores[g:g + 1].cpu().numpy(), want_s), g
+        want_k = oracle.select_topk(want_s, K4, cfg.prot)
+        assert np.array_equal(st.kept[g:g + 1, :K4].cpu().numpy(), want_k), g
+        sp = torch.from_numpy(src_pt[g].astype(np.int64)).to(DEV)
+        dp = torch.from_numpy(dst_pt[g].astype(np.int64)).to(DEV)
+        ks, vs = u16(st.k_src[sp]), u16(st.v_src[sp])
+        pt_s = np.arange(len(src_pt[g]), dtype=np.int32)[None, :]
+        pt_d = np.arange(len(dst_pt[g]), dtype=np.int32)[None, :]
+        kd = np.zeros((len(dst_pt[g]), ps, H, D), np.uint16)
+        vd = np.zeros_like(kd)
+        oracle.compact({"paged": True, "page_table": pt_s}, ks, vs,
+                       {"paged": True, "page_table": pt_d}, kd, vd, want_k, K4, D, H, 0, 1,
+                       ipg=1, page_size=ps)
+        assert np.array_equal(u16(st.k_dst[dp]), kd), g
+        assert np.array_equal(u16(st.v_dst[dp]), vd), g
+    del st
+    free()
+
+
+def test_layers_round():
+    """GateSight's per-layer allocation at the global round's shape: every head of layer l
+    keeps prot + K_l, the K_l sum to the flat total, selection bit-exact on identical scores,
+    compaction equal to the gather of the kept rows."""
+    cfg = configs.LAYERS
+    say("layers round: allocating")
+    st = rounds.make_state(cfg, DEV)
+    rounds.run_round(st)
+    torch.cuda.synchronize()
+    lists, n_body = cfg.L * cfg.H, cfg.n - cfg.prot
+    gate = synth.layer_gates(cfg.L, synth.SEED_GATES)
+    want_b = oracle.layer_power_budget(gate, n_body, cfg.p)
+    assert st.layer_budget == want_b
+    assert sum(want_b) == cfg.L * oracle.budget(1, n_body, 0, cfg.p)
+    counts = st.kept_count.cpu().numpy()
+    assert np.array_equal(counts, cfg.prot + np.repeat(np.array(want_b), cfg.H))
+    assert int(st.errors.item()) == 0
+    say("layers round: compaction of every list")
+    check_contig_gather(st, cfg.n, counts=st.kept_count, chunk=8)
+    say("layers round: selection on identical (oracle-side) scores")
+    s = synth.uniform_scores(lists, cfg.n, seed=23, device="cpu").numpy()
+    s[:, :cfg.prot] = np.inf
+    st.scores.copy_(torch.from_numpy(s))
+    rounds.select(st)
+    torch.cuda.synchronize()
+    got = st.kept.cpu().numpy()
+    for lst in range(lists):
+        K = cfg.prot + want_b[lst // cfg.H]
+        assert np.array_equal(got[lst, :K], oracle.select_topk(s[lst:lst + 1], K, cfg.prot)[0]), lst
+    del st
+    free()
