@@ -63,7 +63,9 @@ def describe(cfg) -> str:
                 f"{rule}, {layout}")
     draw = ("shared draw per layer" if cfg.shared else
             "one list per layer by the max of per-head random scores, kept count a multiple of 4"
-            if cfg.shared_max else "per-head random draw")
+            if cfg.shared_max else
+            "KeyDiff scores (-cosine to the head's mean key)" if cfg.scorer == "keydiff" else
+            "per-head random draw")
     return (f"{cfg.name}: {cfg.R} requests x {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, "
             f"n={cfg.n}, K={cfg.K}, prot={cfg.prot}, {layout}, {draw}"
             + (f", {cfg.rounds} rounds with r={cfg.r} appended" if cfg.rounds > 1 else ""))
@@ -245,7 +247,7 @@ def main():
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
         names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
-                 "paged_shared_max"]
+                 "paged_shared_max", "keydiff"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None

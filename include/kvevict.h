@@ -130,6 +130,26 @@ kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* be
                                       int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
 
 /*
+ * KeyDiff scores (GateSight Sec. 5.1 baselines paragraph: the cosine
+ * similarity of each cached key to the unnormalised mean key of its head; the
+ * least similar keys are kept, under flat per-head budgets with
+ * kvevict_select_topk).
+ *
+ * For every list (group g, head h), list = g*H + h, with its n keys in the
+ * store `keys` (contiguous or paged, see kvevict_kv_desc; values are not read):
+ *     scores[list*ld + i] = -cos(k_i, mean of k_0 .. k_{n-1})   for i >= prot,
+ *                           +inf                                for i <  prot,
+ * in binary64 with one rounding to fp32.  A key or a mean of norm zero gives
+ * cos = 0; a zero score is written as +0.  A paged row whose page id falls
+ * outside the pool reads as zeros.
+ * Requires D = head_dim in {8, 16, 32, ..., 512}, 0 <= prot <= n <= rows of a
+ * list, ld >= n.  KVEVICT_ERR_UNSUPPORTED for other D.
+ */
+kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv_desc* keys,
+                                     const void* k_cache, int64_t num_groups, int32_t n,
+                                     int32_t prot, hipStream_t stream);
+
+/*
  * Pin + per-head top-K ([RA] Algorithm 1: prompt = +inf, topk, return keep).
  *
  * For each of num_lists lists (row at scores + list*ld): keeps [0, prot) and

@@ -29,6 +29,7 @@ LAYOUT_PAGED = 1
 
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
+           "kvevict_score_keydiff",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -78,9 +79,12 @@ def load():
                                                _i32, _p, _p]
     lib.kvevict_layer_power_budget.argtypes = [_p, _i32, _i32, _dbl, _p]
     lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
+    lib.kvevict_score_keydiff.argtypes = [_p, _i64, ctypes.POINTER(KvDesc), _p, _i64, _i32, _i32,
+                                          _p]
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
-                 "kvevict_reduce_max_heads", "kvevict_select_global", "kvevict_compact"):
+                 "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
+                 "kvevict_compact"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -186,6 +190,16 @@ def kvevict_select_topk(kept_idx, kept_ld, scores, ld, num_lists, n, K, prot, st
     _check(load().kvevict_select_topk(_ptr(kept_idx), kept_ld, _ptr(scores), ld, num_lists, n, K,
                                       prot, _stream(stream)),
            "kvevict_select_topk")
+
+
+def kvevict_score_keydiff(scores, ld, keys: KvDesc, k_cache, num_groups, n, prot, stream=None):
+    _need(scores, torch.float32, _rows(num_groups * keys.heads, ld, n), "scores")
+    _need(k_cache, torch.bfloat16, _store_elems(keys, num_groups), "k_cache")
+    if keys.layout == LAYOUT_PAGED and num_groups > 0:
+        _need(keys._pt, torch.int32, num_groups * keys.pt_ld, "page table")
+    _check(load().kvevict_score_keydiff(_ptr(scores), ld, ctypes.byref(keys), _ptr(k_cache),
+                                        num_groups, n, prot, _stream(stream)),
+           "kvevict_score_keydiff")
 
 
 def kvevict_select_topk_layers(kept_idx, kept_ld, kept_count, scores, ld, num_groups, L, H, n,

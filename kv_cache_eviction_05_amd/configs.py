@@ -22,6 +22,8 @@ Five synthetic workloads, each a single-GPU share at its real shape:
             the paged round with one kept list per (request, layer), ranked
             by the larger of the per-head random scores, kept count a
             multiple of four.
+  keydiff   the batch round scored by KeyDiff (-cosine of each key to the
+            mean key of its head) instead of the random draw.
 
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
@@ -45,7 +47,7 @@ class RoundConfig:
     prot: int         # protected prompt prefix
     layout: str = "contig"     # "contig" or "paged"
     page_size: int = 16
-    scorer: str = "random"     # "random" or "weighted"
+    scorer: str = "random"     # "random", "weighted" or "keydiff"
     select: str = "topk"       # "topk", "global" or "layers" (gate-proportional budgets)
     shared: bool = False       # one draw per (request, layer), applied to all heads
     shared_max: bool = False   # one list per (request, layer) ranked by the max over heads
@@ -113,6 +115,8 @@ LONGGEN = RoundConfig("longgen", R=128, L=36, H=8, D=128, K=3072, r=64, prot=557
 # and the shared list of a layer ranked by the max over its KV heads (kept count % 4 == 0)
 LAYERS = replace(GLOBAL, name="layers", select="layers")
 PAGED_SHARED_MAX = replace(PAGED, name="paged_shared_max", shared_max=True)
+# a content scorer that reads every key once more: KeyDiff at the batch round's shape
+KEYDIFF = replace(BATCH, name="keydiff", scorer="keydiff")
 
 ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
-                           PAGED_SHARED_MAX)}
+                           PAGED_SHARED_MAX, KEYDIFF)}

@@ -115,6 +115,24 @@ kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const flo
                                                 n, K, prot, 0, 1, nullptr, stream));
 }
 
+kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv_desc* keys,
+                                     const void* k_cache, int64_t num_groups, int32_t n,
+                                     int32_t prot, hipStream_t stream) {
+  if (!keys || num_groups < 0 || n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
+  const int32_t D = keys->head_dim, H = keys->heads;
+  kvevict::StoreView sv;
+  const kvevict_status st = check_store(keys, k_cache, k_cache, num_groups, &sv);
+  if (st != KVEVICT_OK) return st;
+  const int32_t vpr = D / 8;
+  if (vpr > 64 || (vpr & (vpr - 1)) != 0) return KVEVICT_ERR_UNSUPPORTED;  // D in {8, 16, ..., 512}
+  if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_groups * H;
+  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_score_keydiff(scores, ld, sv, k_cache, D, H, lists, n, prot,
+                                                  stream));
+}
+
 kvevict_status kvevict_select_topk_layers(int32_t* kept_idx, int64_t kept_ld,
                                           int32_t* kept_count, const float* scores, int64_t ld,
                                           int64_t num_groups, int32_t L, int32_t H, int32_t n,

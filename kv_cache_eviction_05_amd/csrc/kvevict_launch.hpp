@@ -58,4 +58,9 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
                           int32_t K, int64_t num_groups, int32_t ipg, uint32_t* errors,
                           hipStream_t stream);
 
+// KeyDiff scores of num_lists lists of n keys (D a power of two in [8, 512]).
+hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys, const void* k,
+                                int32_t D, int32_t H, int64_t num_lists, int32_t n, int32_t prot,
+                                hipStream_t stream);
+
 }  // namespace kvevict

@@ -140,6 +140,9 @@ def score(st: RoundState, round_id: int, stream=None):
     elif c.scorer == "random":
         B.kvevict_score_random(st.scores, st.scores.shape[1], c.R, c.L, c.H, st.n, c.prot, c.seed,
                                round_id, c.shared, stream)
+    elif c.scorer == "keydiff":
+        B.kvevict_score_keydiff(st.scores, st.scores.shape[1], st.src_desc, st.k_src, c.groups,
+                                st.n, c.prot, stream)
     else:
         n = st.n
         B.kvevict_score_weighted(st.scores, st.scores.shape[1], st.beta, st.vnorm, n * c.Hg, c.Hg,

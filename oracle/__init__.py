@@ -12,6 +12,7 @@ definitions.  Arrays are numpy; bf16 rows are handled as ``uint16`` bytes.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -258,3 +259,40 @@ def shared_kept_count(K: int, prot: int) -> int:
     if k4 < prot:
         raise ValueError("the prompt does not fit a multiple-of-four count below K")
     return k4
+
+
+# ---------------------------------------------------------------------------
+# KeyDiff key scores (GateSight Sec. 5.1 baselines paragraph: cosine similarity
+# of each cached key to the unnormalised mean key of its head; the least
+# similar keys are kept under flat per-head budgets)
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 stored as uint16 -> float64 (exact: the 16 bits are the top of a float32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def score_keydiff(keys: np.ndarray, prot: int) -> np.ndarray:
+    """Scores float32 [lists][n] from keys (uint16 bf16 bits) [lists][n][D].
+
+    score_i = -cos(k_i, mean_j k_j), the mean over all n keys of the list, in binary64,
+    rounded once to float32; higher is kept first, so the least similar keys survive.
+    Readings: the mean runs over every entry of the list, prompt included; a key or a mean
+    of norm zero gives cos = 0; a zero score is written as +0; slots < prot score +inf.
+    """
+    k = bf16_to_f64(keys)
+    lists, n, D = k.shape
+    out = np.empty((lists, n), dtype=np.float32)
+    for l in range(lists):
+        mean = k[l].sum(axis=0) / n if n else np.zeros(D)
+        mm = float(np.dot(mean, mean))
+        for i in range(n):
+            if i < prot:
+                out[l, i] = np.inf
+                continue
+            kk = float(np.dot(k[l, i], k[l, i]))
+            den = math.sqrt(kk) * math.sqrt(mm)
+            cos = float(np.dot(k[l, i], mean)) / den if den > 0 else 0.0
+            v = np.float32(-cos)
+            out[l, i] = v if v != 0 else np.float32(0.0)  # -0 written as +0
+    return out

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                           "kvevict_select_topk_layers", "kvevict_layer_power_budget",
-                          "kvevict_reduce_max_heads", "kvevict_select_global", "kvevict_compact",
+                          "kvevict_reduce_max_heads", "kvevict_score_keydiff",
+                          "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
@@ -191,3 +192,17 @@ def test_select_topk_layers_and_reduce_validation():
     assert status("kvevict_reduce_max_heads", FAKE, 63, FAKE, 64, 2, 4, 64, None) == B.KVEVICT_ERR_INVALID_ARG
     assert status("kvevict_reduce_max_heads", FAKE, 64, FAKE, 64, 2, 0, 64, None) == B.KVEVICT_ERR_INVALID_ARG
     assert status("kvevict_reduce_max_heads", None, 64, FAKE, 64, 2, 4, 64, None) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_score_keydiff_validation():
+    d = B.contig_desc(128, 8, 1088)
+    d24 = B.contig_desc(24, 8, 1088)
+    d1024 = B.contig_desc(1024, 1, 16)
+    st = lambda desc, *a: status("kvevict_score_keydiff", FAKE, a[0], ctypes.byref(desc), FAKE, *a[1:], None)
+    assert st(d24, 1088, 4, 1088, 0) == B.KVEVICT_ERR_UNSUPPORTED      # D not a power of two
+    assert st(d1024, 16, 4, 16, 0) == B.KVEVICT_ERR_UNSUPPORTED        # D above 512
+    assert st(d, 1087, 4, 1088, 0) == B.KVEVICT_ERR_INVALID_ARG        # ld < n
+    assert st(d, 2000, 4, 1089, 0) == B.KVEVICT_ERR_INVALID_ARG        # n beyond the store
+    assert st(d, 1088, 4, 1088, 1089) == B.KVEVICT_ERR_INVALID_ARG     # prot > n
+    assert st(d, 1088, -1, 1088, 0) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_score_keydiff", FAKE, 1088, None, FAKE, 4, 1088, 0, None) == B.KVEVICT_ERR_INVALID_ARG

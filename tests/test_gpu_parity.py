@@ -437,3 +437,70 @@ def test_reduce_max_heads(G, H, n, pad):
     want = oracle.shared_max_scores(s, H)
     assert np.array_equal(got[:, :n].view(np.uint32), want.view(np.uint32))  # bit for bit
     assert np.all(got[:, n:] == 5.0)
+
+
+# ---------------------------------------------------------------------------
+# KeyDiff key scores
+# ---------------------------------------------------------------------------
+
+def rand_keys(shape, seed):
+    """uint16 bf16 bits of N(0,1) keys."""
+    rng = np.random.default_rng(seed)
+    f = rng.standard_normal(shape).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def assert_keydiff_close(got, want):
+    """Within two fp32 ulps (binary64 on both sides, summation order differs)."""
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isposinf(got), np.isposinf(want))
+    g, o = got[fin].astype(np.float64), want[fin].astype(np.float64)
+    tol = 2 * np.spacing(np.abs(want[fin])).astype(np.float64)
+    assert np.all(np.abs(g - o) <= tol), float(np.max(np.abs(g - o)))
+    return float(np.mean(got[fin] == want[fin])) if fin.any() else 1.0
+
+
+@pytest.mark.parametrize("groups,H,n,D,prot,cap", [
+    (3, 4, 1088, 128, 128, 1088),   # the batch shape
+    (2, 3, 777, 256, 5, 800),       # ragged, padded rows, D = 256
+    (2, 2, 70, 64, 70, 70),         # every slot protected
+    (1, 2, 1, 128, 0, 4),           # one key per list
+])
+def test_score_keydiff_contig(groups, H, n, D, prot, cap):
+    say(f"score_keydiff contig groups={groups} H={H} n={n} D={D} prot={prot}")
+    lists = groups * H
+    keys = rand_keys((lists, cap, D), seed=n * D)
+    keys[0, min(3, n - 1)] = 0  # a zero key
+    ld = n + 2
+    s = torch.full((lists, ld), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_keydiff(s, ld, B.contig_desc(D, H, cap), bf16_from_bits(keys), groups, n, prot)
+    torch.cuda.synchronize()
+    got = to_np(s)
+    assert np.all(np.isnan(got[:, n:]))
+    want = oracle.score_keydiff(np.ascontiguousarray(keys[:, :n]), prot)
+    same = assert_keydiff_close(got[:, :n], want)
+    say(f"  bit-identical fraction {same:.6f}")
+
+
+def test_score_keydiff_paged():
+    groups, H, D, ps, n, prot = 3, 8, 128, 16, 530, 17
+    say("score_keydiff paged")
+    per = -(-n // ps)
+    pool = groups * per + 5
+    rng = np.random.default_rng(9)
+    pt = rng.permutation(pool)[: groups * per].astype(np.int32).reshape(groups, per)
+    pt[2, 4] = pool + 9  # out of the pool: that page's rows read as zeros
+    store = rand_keys((pool, ps, H, D), seed=4)
+    s = torch.zeros((groups * H, n), dtype=torch.float32, device=DEV)
+    B.kvevict_score_keydiff(s, n, B.paged_desc(D, H, ps, pool, torch.from_numpy(pt).to(DEV)),
+                            bf16_from_bits(store), groups, n, prot)
+    torch.cuda.synchronize()
+    keys = np.zeros((groups * H, n, D), np.uint16)
+    for g in range(groups):
+        for t in range(n):
+            page = pt[g, t // ps]
+            if page < pool:
+                keys[g * H:(g + 1) * H, t] = store[page, t % ps]
+    want = oracle.score_keydiff(keys, prot)
+    same = assert_keydiff_close(to_np(s), want)
+    say(f"  bit-identical fraction {same:.6f}")

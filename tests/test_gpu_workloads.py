@@ -326,3 +326,25 @@ def test_layers_round():
         assert np.array_equal(got[lst, :K], oracle.select_topk(s[lst:lst + 1], K, cfg.prot)[0]), lst
     del st
     free()
+
+
+def test_keydiff_round_sampled():
+    """The batch round scored by KeyDiff: sampled lists against the oracle's scores (two fp32
+    ulps), selection given the GPU's scores, and the whole gather."""
+    cfg = configs.KEYDIFF.small(R=16)
+    say("keydiff round: allocating")
+    st = rounds.make_state(cfg, DEV)
+    rounds.run_round(st)
+    torch.cuda.synchronize()
+    assert int(st.errors.item()) == 0
+    check_kept_properties(st.kept, cfg.K, cfg.prot, cfg.n)
+    check_contig_gather(st, cfg.K)
+    got_s = st.scores.cpu().numpy()
+    for l in sample_lists(cfg.lists, 12, seed=8):
+        want = oracle.score_keydiff(u16(st.k_src[l:l + 1]), cfg.prot)
+        fin = np.isfinite(want)
+        assert np.all(np.abs(got_s[l:l + 1][fin] - want[fin]) <= 2 * np.spacing(np.abs(want[fin]))), l
+        assert np.array_equal(st.kept[l].cpu().numpy(),
+                              oracle.select_topk(got_s[l:l + 1], cfg.K, cfg.prot)[0]), l
+    del st
+    free()
