@@ -61,6 +61,8 @@ def describe(cfg) -> str:
         return (f"{cfg.name}: {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, n={cfg.n}, "
                 f"prot={cfg.prot}, p={cfg.p}, weighted GDN score over 48 GDN layers x 48 heads, "
                 f"{rule}, {layout}")
+    if cfg.inplace:
+        layout += ", compacted in place (unchanged prefix stays, freed pages to a list)"
     draw = ("shared draw per layer" if cfg.shared else
             "one list per layer by the max of per-head random scores, kept count a multiple of 4"
             if cfg.shared_max else
@@ -131,6 +133,30 @@ def time_workload(torch, rounds, cfg, steps, warmup):
             rounds.append_tokens(st, round_id)
             rounds.swap(st)
             round_id += 1
+            torch.cuda.synchronize()
+            total_ms += t0.elapsed_time(t1)
+        ms_per = total_ms / steps
+    elif cfg.inplace:
+        # one round in place: the cache is restored before every round, untimed
+        for _ in range(warmup):
+            rounds.restore(st)
+            rounds.run_round(st, 0)
+        timer = Timer(torch, ["score", "select", "compact"])
+        total_ms = 0.0
+        for s in range(steps):
+            rounds.restore(st)
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            timer.mark()
+            rounds.score(st, s)
+            timer.mark()
+            rounds.select(st)
+            timer.mark()
+            rounds.compact(st)
+            timer.mark()
+            t1.record()
+            st.applied_rounds += 1
             torch.cuda.synchronize()
             total_ms += t0.elapsed_time(t1)
         ms_per = total_ms / steps
@@ -247,7 +273,7 @@ def main():
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
         names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
-                 "paged_shared_max", "keydiff"]
+                 "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None

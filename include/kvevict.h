@@ -263,6 +263,39 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
                                int32_t idx_lists_per_group, uint32_t* errors,
                                hipStream_t stream);
 
+/*
+ * In-place chronological compaction with a free-page list (GateSight Sec. 4.3
+ * and Appendix G: each layer moves the entries it keeps to the front of its
+ * own pages, and the freed tail blocks return to the pool, which releases
+ * their memory).
+ *
+ * For every group g < num_groups, head h < H and j < count, in place:
+ *     K row (g, h, j) <- K row (g, h, idx[j])   and the same for V,
+ * with idx and count chosen as in kvevict_compact.  Each index list must be
+ * strictly increasing (as the selections produce), so idx[j] >= j and rows
+ * only move towards the front; rows with idx[j] == j are not touched.  Rows
+ * at and beyond count keep whatever they held (stale).
+ * n       rows of each list in use before the call (count <= K <= n).
+ * PAGED:  the group's pages ceil(count_max / page_size) .. ceil(n / page_size) - 1,
+ *         count_max the largest count among the group's index lists, are
+ *         appended to freed_pages (device int32, room for num_groups *
+ *         ceil(n / page_size) ids) at offsets taken with an atomic add on
+ *         *freed_count (device uint32, not reset by the call), in an order
+ *         that may differ from call to call.  The page table itself is read
+ *         only: the caller shortens its block table to the kept pages.
+ *         CONTIG: freed_pages and freed_count are ignored (may be NULL).
+ * errors  optional device counter: each row whose index is below its slot or
+ *         outside the store, or whose page id is invalid, is skipped and adds 1.
+ *         Counts outside [0, K] are clamped.
+ * Calls on the same store must not overlap.
+ */
+kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
+                                       const int32_t* kept_idx, int64_t kept_ld,
+                                       const int32_t* kept_count, int32_t K, int32_t n,
+                                       int64_t num_groups, int32_t idx_lists_per_group,
+                                       int32_t* freed_pages, uint32_t* freed_count,
+                                       uint32_t* errors, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kvevict_status_string(kvevict_status status);
 

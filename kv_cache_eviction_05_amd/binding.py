@@ -29,7 +29,7 @@ LAYOUT_PAGED = 1
 
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
-           "kvevict_score_keydiff",
+           "kvevict_score_keydiff", "kvevict_compact_inplace",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -81,10 +81,12 @@ def load():
     lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
     lib.kvevict_score_keydiff.argtypes = [_p, _i64, ctypes.POINTER(KvDesc), _p, _i64, _i32, _i32,
                                           _p]
+    lib.kvevict_compact_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _p, _i64, _p, _i32,
+                                            _i32, _i64, _i32, _p, _p, _p, _p]
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
-                 "kvevict_compact"):
+                 "kvevict_compact", "kvevict_compact_inplace"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -288,3 +290,23 @@ def kvevict_compact(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_i
 
 def kvevict_abi_version() -> int:
     return int(load().kvevict_abi_version())
+
+
+def kvevict_compact_inplace(store: KvDesc, k, v, kept_idx, kept_ld, kept_count, K, n, num_groups,
+                            idx_lists_per_group, freed_pages=None, freed_count=None, errors=None,
+                            stream=None):
+    _need(k, torch.bfloat16, _store_elems(store, num_groups), "k")
+    _need(v, torch.bfloat16, _store_elems(store, num_groups), "v")
+    idx_lists = num_groups * idx_lists_per_group
+    _need(kept_idx, torch.int32, _rows(idx_lists, kept_ld, K), "kept_idx")
+    _need(kept_count, torch.int32, idx_lists, "kept_count")
+    _need(errors, torch.int32, 1, "errors")
+    if store.layout == LAYOUT_PAGED and num_groups > 0:
+        _need(store._pt, torch.int32, num_groups * store.pt_ld, "page table")
+        _need(freed_pages, torch.int32, num_groups * -(-n // store.page_size), "freed_pages")
+        _need(freed_count, torch.int32, 1, "freed_count")
+    _check(load().kvevict_compact_inplace(ctypes.byref(store), _ptr(k), _ptr(v), _ptr(kept_idx),
+                                          kept_ld, _ptr(kept_count), K, n, num_groups,
+                                          idx_lists_per_group, _ptr(freed_pages),
+                                          _ptr(freed_count), _ptr(errors), _stream(stream)),
+           "kvevict_compact_inplace")

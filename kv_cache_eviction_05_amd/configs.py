@@ -24,6 +24,10 @@ Five synthetic workloads, each a single-GPU share at its real shape:
             multiple of four.
   keydiff   the batch round scored by KeyDiff (-cosine of each key to the
             mean key of its head) instead of the random draw.
+  paged_inplace, longgen_inplace
+            the paged and the 30-round workloads compacted in place: kept rows
+            move to the front of their own rows or pages, the unchanged prefix
+            stays, freed tail pages go to a free list.
 
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
@@ -51,6 +55,7 @@ class RoundConfig:
     select: str = "topk"       # "topk", "global" or "layers" (gate-proportional budgets)
     shared: bool = False       # one draw per (request, layer), applied to all heads
     shared_max: bool = False   # one list per (request, layer) ranked by the max over heads
+    inplace: bool = False      # compact in place (front of the same rows / pages)
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -117,6 +122,9 @@ LAYERS = replace(GLOBAL, name="layers", select="layers")
 PAGED_SHARED_MAX = replace(PAGED, name="paged_shared_max", shared_max=True)
 # a content scorer that reads every key once more: KeyDiff at the batch round's shape
 KEYDIFF = replace(BATCH, name="keydiff", scorer="keydiff")
+# in-place compaction to the front of the same pages, freed tail pages to a pool
+PAGED_INPLACE = replace(PAGED, name="paged_inplace", inplace=True)
+LONGGEN_INPLACE = replace(LONGGEN, name="longgen_inplace", inplace=True)
 
 ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
-                           PAGED_SHARED_MAX, KEYDIFF)}
+                           PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE)}

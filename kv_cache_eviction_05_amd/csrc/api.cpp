@@ -295,6 +295,31 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
                                             idx_lists_per_group, errors, stream));
 }
 
+kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
+                                       const int32_t* kept_idx, int64_t kept_ld,
+                                       const int32_t* kept_count, int32_t K, int32_t n,
+                                       int64_t num_groups, int32_t idx_lists_per_group,
+                                       int32_t* freed_pages, uint32_t* freed_count,
+                                       uint32_t* errors, hipStream_t stream) {
+  if (!store) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups < 0 || K < 0 || n < K || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
+  const int32_t H = store->heads, D = store->head_dim;
+  if (idx_lists_per_group != 1 && idx_lists_per_group != H) return KVEVICT_ERR_INVALID_ARG;
+  kvevict::StoreView sv;
+  const kvevict_status st = check_store(store, k, v, num_groups, &sv);
+  if (st != KVEVICT_OK) return st;
+  if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;
+  if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;  // K and V are distinct stores
+  if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
+  if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_compact_inplace(sv, k, v, D, H, kept_idx, kept_ld, kept_count,
+                                                    K, n, num_groups, idx_lists_per_group,
+                                                    sv.paged ? freed_pages : nullptr,
+                                                    freed_count, errors, stream));
+}
+
 const char* kvevict_status_string(kvevict_status status) {
   switch (status) {
     case KVEVICT_OK: return "ok";

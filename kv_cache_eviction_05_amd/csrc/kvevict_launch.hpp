@@ -63,4 +63,13 @@ hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys
                                 int32_t D, int32_t H, int64_t num_lists, int32_t n, int32_t prot,
                                 hipStream_t stream);
 
+// In-place compaction of num_groups groups of one store (rows move to the
+// front); paged: the tail pages beyond ceil(count_max / page_size) of the
+// first n rows are appended to freed at atomicAdd(freed_count, ...).
+hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t D, int32_t H,
+                                  const int32_t* kept_idx, int64_t kept_ld,
+                                  const int32_t* kept_count, int32_t K, int32_t n,
+                                  int64_t num_groups, int32_t ipg, int32_t* freed,
+                                  uint32_t* freed_count, uint32_t* errors, hipStream_t stream);
+
 }  // namespace kvevict

@@ -54,14 +54,25 @@ class RoundState:
     budget: int = 0
     layer_budget: list = field(default_factory=list)
     head_scores: torch.Tensor | None = None  # per-head scores before the max over heads
+    k_pristine: torch.Tensor | None = None   # in place, one round: the cache before the round
+    v_pristine: torch.Tensor | None = None
+    freed: torch.Tensor | None = None        # in place, paged: the free-page list
+    freed_count: torch.Tensor | None = None
 
     @property
     def idx_lists(self) -> int:
         return self.cfg.lists
 
     def kv_bytes_moved(self) -> int:
-        """Read + write bytes of the kept K and V rows of one round."""
+        """Read + write bytes of the kept K and V rows of one round (in place: of the rows
+        that move, those whose kept index differs from their slot)."""
         c = self.cfg
+        if c.inplace:
+            K = c.kept_shared if c.shared_max else c.K
+            j = torch.arange(K, device=self.kept.device, dtype=self.kept.dtype)
+            moved = int((self.kept[:, :K] != j).sum().item())
+            heads = c.H if (c.shared or c.shared_max) else 1
+            return moved * heads * c.row_bytes * 2 * 2
         if c.select in ("global", "layers"):
             rows = int(self.kept_count.sum().item())
         elif c.shared_max:
@@ -100,6 +111,8 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
     device = torch.device(device)
     n = cfg.n
     cap_dst = n if cfg.select in ("global", "layers") else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
+    if cfg.inplace:
+        cap_dst = 1  # no destination store: rows move within the source
     ks, vs, kd, vd, sd, dd, spt, dpt = _desc_pair(cfg, n, cap_dst, device, kv_seed)
     lists = cfg.lists if cfg.select == "topk" else cfg.groups * cfg.H
     scores = torch.empty((lists, n), dtype=torch.float32, device=device)
@@ -109,6 +122,13 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
                     torch.zeros(1, dtype=torch.int32, device=device), src_pt=spt, dst_pt=dpt, n=n)
     if cfg.shared_max:
         st.head_scores = torch.empty((cfg.groups * cfg.H, n), dtype=torch.float32, device=device)
+    if cfg.inplace:
+        st.k_dst, st.v_dst, st.dst_desc, st.dst_pt = st.k_src, st.v_src, st.src_desc, st.src_pt
+        if cfg.rounds == 1:
+            st.k_pristine, st.v_pristine = ks.clone(), vs.clone()
+        if cfg.layout == "paged":
+            st.freed = torch.empty(cfg.groups * spt.shape[1], dtype=torch.int32, device=device)
+            st.freed_count = torch.zeros(1, dtype=torch.int32, device=device)
     if cfg.select == "layers":
         st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
         st.layer_budget = B.kvevict_layer_power_budget(synth.layer_gates(cfg.L, synth.SEED_GATES),
@@ -174,6 +194,11 @@ def compact(st: RoundState, stream=None):
     else:
         K, count = st.n, st.kept_count
     ipg = 1 if (c.shared or c.shared_max) else c.H
+    if c.inplace:
+        B.kvevict_compact_inplace(st.src_desc, st.k_src, st.v_src, st.kept, st.kept.shape[1], count,
+                                  K, st.n, c.groups, ipg, st.freed, st.freed_count, st.errors,
+                                  stream)
+        return
     B.kvevict_compact(st.src_desc, st.k_src, st.v_src, st.dst_desc, st.k_dst, st.v_dst, st.kept,
                       st.kept.shape[1], count, K, c.groups, ipg, st.errors, stream)
 
@@ -197,8 +222,19 @@ def append_tokens(st: RoundState, round_id: int):
                                                      st.device))
 
 
+def restore(st: RoundState):
+    """In place, one round: put the cache back as it was before the round (input set-up)."""
+    st.k_src.copy_(st.k_pristine)
+    st.v_src.copy_(st.v_pristine)
+    if st.freed_count is not None:
+        st.freed_count.zero_()
+
+
 def swap(st: RoundState):
-    """The compacted cache (K kept + r appended rows) becomes the next round's source."""
+    """The compacted cache (K kept + r appended rows) becomes the next round's source
+    (in place there is one cache: nothing to swap)."""
+    if st.cfg.inplace:
+        return
     st.k_src, st.k_dst = st.k_dst, st.k_src
     st.v_src, st.v_dst = st.v_dst, st.v_src
     st.src_desc, st.dst_desc = st.dst_desc, st.src_desc

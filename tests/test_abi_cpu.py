@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                           "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                           "kvevict_reduce_max_heads", "kvevict_score_keydiff",
-                          "kvevict_select_global", "kvevict_compact",
+                          "kvevict_compact_inplace", "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:

@@ -504,3 +504,108 @@ def test_score_keydiff_paged():
     want = oracle.score_keydiff(keys, prot)
     same = assert_keydiff_close(to_np(s), want)
     say(f"  bit-identical fraction {same:.6f}")
+
+
+# ---------------------------------------------------------------------------
+# in-place compaction with a free-page list
+# ---------------------------------------------------------------------------
+
+def keep_sets(lists, n, K, prot, seed, variable=False):
+    """Strictly increasing keep sets (and counts) from the oracle's top-K of random scores."""
+    rng = np.random.default_rng(seed)
+    s = rng.random((lists, n), dtype=np.float32)
+    s[:, :prot] = np.inf
+    kept = oracle.select_topk(s, K, prot)
+    counts = np.full(lists, K, np.int32)
+    if variable:  # a prefix of an increasing keep set is itself increasing
+        counts = rng.integers(0, K + 1, lists).astype(np.int32)
+    return np.ascontiguousarray(kept), counts
+
+
+@pytest.mark.parametrize("layout,shared,variable,D", [
+    ("contig", False, False, 128),
+    ("contig", True, False, 64),
+    ("contig", False, True, 256),
+    ("paged", False, False, 128),
+    ("paged", True, False, 128),
+    ("paged", False, True, 64),
+])
+def test_compact_inplace(layout, shared, variable, D):
+    groups, H, ps, n, K, prot = 5, 4, 16, 300, 240, 37
+    say(f"compact_inplace {layout} shared={shared} variable={variable} D={D}")
+    ipg = 1 if shared else H
+    kept, counts = keep_sets(groups * ipg, n, K, prot, seed=D + n, variable=variable)
+    pool = groups * (n // ps + 1) + 3
+    if layout == "contig":
+        shape = (groups * H, n, D)
+        desc = B.contig_desc(D, H, n)
+        pt = None
+    else:
+        shape = (pool, ps, H, D)
+        rng = np.random.default_rng(4)
+        per = -(-n // ps)
+        pt = rng.permutation(pool)[: groups * per].astype(np.int32).reshape(groups, per)
+        desc = B.paged_desc(D, H, ps, pool, torch.from_numpy(pt).to(DEV))
+    ks, vs = rand_bits(shape, 40), rand_bits(shape, 41)
+    k, v = bf16_from_bits(ks), bf16_from_bits(vs)
+    freed = torch.full((groups * (n // ps + 1),), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_compact_inplace(desc, k, v, torch.from_numpy(kept).to(DEV), K,
+                              torch.from_numpy(counts).to(DEV) if variable else None, K, n,
+                              groups, ipg, freed, fcount, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    # want: the oracle's out-of-place compaction of the original, below each count
+    if layout == "contig":
+        kd = np.zeros((groups * H, K, D), np.uint16)
+        vd = np.zeros_like(kd)
+        oracle.compact({"list_stride": n * D}, ks, vs, {"list_stride": K * D}, kd, vd, kept, K, D,
+                       H, 0, groups, ipg=ipg, kept_count=counts if variable else None)
+        gk, gv = u16(k), u16(v)
+        for lst in range(groups * H):
+            c = counts[(lst // H) * ipg + (0 if shared else lst % H)]
+            assert np.array_equal(gk[lst, :c], kd[lst, :c]), lst
+            assert np.array_equal(gv[lst, :c], vd[lst, :c]), lst
+            assert np.array_equal(gk[lst, c:], ks[lst, c:]), lst  # rows past the count untouched
+            assert np.array_equal(gv[lst, c:], vs[lst, c:]), lst
+        assert int(fcount.item()) == 0
+    else:
+        gk, gv = u16(k), u16(v)
+        per = pt.shape[1]
+        want_free = []
+        for g in range(groups):
+            il = np.arange(g * ipg, g * ipg + ipg)
+            cs = counts[il] if variable else np.full(ipg, K)
+            # rows of the group as [H][n][D], before and after
+            before_k = np.stack([ks[pt[g, t // ps], t % ps] for t in range(n)], 1)  # [H][n][D]
+            after_k = np.stack([gk[pt[g, t // ps], t % ps] for t in range(n)], 1)
+            before_v = np.stack([vs[pt[g, t // ps], t % ps] for t in range(n)], 1)
+            after_v = np.stack([gv[pt[g, t // ps], t % ps] for t in range(n)], 1)
+            for h in range(H):
+                li = 0 if shared else h
+                c = cs[li]
+                idx = kept[g * ipg + li, :c]
+                assert np.array_equal(after_k[h, :c], before_k[h, idx]), (g, h)
+                assert np.array_equal(after_v[h, :c], before_v[h, idx]), (g, h)
+                assert np.array_equal(after_k[h, c:], before_k[h, c:]), (g, h)
+            keep = -(-int(cs.max()) // ps)
+            want_free += list(pt[g, keep:per])
+        got_free = to_np(freed)[: int(fcount.item())]
+        assert sorted(got_free) == sorted(want_free)  # freed blocks verified against the pool
+
+
+def test_compact_inplace_rejects_bad_indices():
+    """An index below its slot (a row would move backwards) is skipped and counted."""
+    groups, H, D, n, K = 1, 2, 64, 64, 40
+    kept = np.tile(np.arange(K, dtype=np.int32) + 5, (H, 1))
+    kept[1, 10] = 3  # below its slot
+    ks, vs = rand_bits((groups * H, n, D), 50), rand_bits((groups * H, n, D), 51)
+    k, v = bf16_from_bits(ks), bf16_from_bits(vs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_compact_inplace(B.contig_desc(D, H, n), k, v, torch.from_numpy(kept).to(DEV), K,
+                              None, K, n, groups, H, None, None, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    gk = u16(k)
+    assert np.array_equal(gk[0, :K], ks[0, 5:K + 5])

@@ -348,3 +348,67 @@ def test_keydiff_round_sampled():
                               oracle.select_topk(got_s[l:l + 1], cfg.K, cfg.prot)[0]), l
     del st
     free()
+
+
+def test_paged_inplace_round_sampled():
+    """Paged round compacted in place: on sampled groups every head's first K rows are the kept
+    rows of the cache before the round and the rows past K are untouched; every group returns
+    its 4 tail pages (132 -> 128) and the free list holds exactly those pages."""
+    cfg = configs.PAGED_INPLACE.small(R=8)
+    say("paged in-place round: allocating")
+    st = rounds.make_state(cfg, DEV)
+    ps, H, D, n, K = cfg.page_size, cfg.H, cfg.D, cfg.n, cfg.K
+    pt = st.src_pt.cpu().numpy()
+    samples = sample_lists(cfg.groups, 6, seed=2)
+    before = {g: (u16(st.k_src[torch.from_numpy(pt[g].astype(np.int64)).to(DEV)]),
+                  u16(st.v_src[torch.from_numpy(pt[g].astype(np.int64)).to(DEV)])) for g in samples}
+    rounds.run_round(st, round_id=1)
+    torch.cuda.synchronize()
+    assert int(st.errors.item()) == 0
+    check_kept_properties(st.kept, K, cfg.prot, n)
+    kept = st.kept.cpu().numpy()
+    for g in samples:
+        idx_pages = torch.from_numpy(pt[g].astype(np.int64)).to(DEV)
+        ak, av = u16(st.k_src[idx_pages]), u16(st.v_src[idx_pages])
+        bk, bv = before[g]
+        # [pages][16][H][D] -> [H][rows][D]
+        rows = lambda a: a.reshape(-1, H, D).transpose(1, 0, 2)[:, :n]
+        for h in range(H):
+            idx = kept[g * H + h]
+            assert np.array_equal(rows(ak)[h, :K], rows(bk)[h, idx]), (g, h)
+            assert np.array_equal(rows(av)[h, :K], rows(bv)[h, idx]), (g, h)
+            assert np.array_equal(rows(ak)[h, K:], rows(bk)[h, K:]), (g, h)
+    nf = int(st.freed_count.item())
+    assert nf == cfg.groups * (-(-n // ps) - K // ps) == cfg.groups * 4
+    assert sorted(st.freed[:nf].cpu().tolist()) == sorted(pt[:, K // ps:].reshape(-1).tolist())
+    del st
+    free()
+
+
+def test_longgen_inplace_rounds_replayed_by_oracle():
+    """30 rounds compacted in place on one request's 288 lists, replayed by the oracle."""
+    cfg = configs.LONGGEN_INPLACE.small(R=1)
+    say("longgen in-place replay")
+    st = rounds.make_state(cfg, DEV)
+    lists, n, K, D = cfg.lists, cfg.n, cfg.K, cfg.D
+    host_k, host_v = u16(st.k_src), u16(st.v_src)
+    for rnd in range(cfg.rounds):
+        rounds.run_round(st, round_id=rnd)
+        torch.cuda.synchronize()
+        want_s = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, cfg.seed, rnd, False, 0, lists)
+        want_k = oracle.select_topk(want_s, K, cfg.prot)
+        assert np.array_equal(st.kept.cpu().numpy(), want_k), rnd
+        kd = np.zeros((lists, K, D), np.uint16)
+        vd = np.zeros_like(kd)
+        oracle.compact({"list_stride": n * D}, host_k, host_v, {"list_stride": K * D}, kd, vd,
+                       want_k, K, D, cfg.H, 0, cfg.groups, ipg=cfg.H)
+        gk, gv = u16(st.k_src), u16(st.v_src)
+        assert np.array_equal(gk[:, :K], kd), rnd
+        assert np.array_equal(gv[:, :K], vd), rnd
+        rounds.append_tokens(st, rnd)
+        torch.cuda.synchronize()
+        host_k, host_v = u16(st.k_src), u16(st.v_src)
+        rounds.swap(st)
+    assert st.applied_rounds == cfg.rounds and int(st.errors.item()) == 0
+    del st
+    free()
