@@ -287,7 +287,8 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
  * errors  optional device counter: each row whose index is below its slot or
  *         outside the store, or whose page id is invalid, is skipped and adds 1.
  *         Counts outside [0, K] are clamped.
- * Calls on the same store must not overlap.
+ * Limits: num_groups * H < 2^31 and n * head_dim / 8 <= 2^30, else
+ * KVEVICT_ERR_INVALID_ARG.  Calls on the same store must not overlap.
  */
 kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
                                        const int32_t* kept_idx, int64_t kept_ld,

@@ -313,7 +313,7 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
   if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;  // K and V are distinct stores
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
-  if (num_groups > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_compact_inplace(sv, k, v, D, H, kept_idx, kept_ld, kept_count,
                                                     K, n, num_groups, idx_lists_per_group,
                                                     sv.paged ? freed_pages : nullptr,

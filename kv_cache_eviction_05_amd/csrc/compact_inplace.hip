@@ -9,14 +9,17 @@
 //
 // Kept indices are strictly increasing, so idx[j] >= j: a row only moves
 // towards the front, and the unchanged prefix (idx[j] == j: the prompt and the
-// rows before the first eviction) is never touched.  One workgroup per group
-// (all H heads, so paged writes are whole token rows) walks the destination
-// rows in increasing chunks.  Within a chunk a source row may also be a
-// destination of the same chunk, so every thread waits for its loads before a
-// workgroup barrier and only then stores; a later chunk reads only rows at or
-// beyond its own first destination row, which no earlier chunk writes.
-// The first moved row of each index list is found with two rounds of 32
-// samples before the walk starts.
+// rows before the first eviction) is never touched.  Heads own disjoint
+// memory in both layouts, so one workgroup per (group, head) walks that head's
+// destination rows in increasing chunks.  Within a chunk a source row may also
+// be a destination of the same chunk, so every thread waits for its loads
+// before a workgroup barrier and only then stores; a later chunk reads only
+// rows at or beyond its own first destination row, which no earlier chunk
+// writes.  The walk is software-pipelined three deep: while the rows of chunk
+// q are loaded, the page ids of chunk q+1 and the kept indices of chunk q+2
+// are fetched, so each chunk waits on one memory latency, not four.
+// The first moved row of the list is found with one round of 256 samples and
+// a scan of the gap before the first mismatching sample.
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 
@@ -24,9 +27,9 @@ namespace kvevict {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecs = 4;     // 16-byte vectors of K (and of V) per thread per chunk
-constexpr int kTeam = 32;    // threads searching one index list
-constexpr int kMaxTeams = kThreads / kTeam;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kVecs = 8;  // 16-byte vectors of K (and of V) per thread per chunk
+constexpr int32_t kChunk = kThreads * kVecs;
 
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
@@ -43,136 +46,174 @@ struct InplaceArgs {
   uint32_t* errors;
 };
 
-// Vector offset of row t of (group g, head h), or -1 if t or its page id
-// falls outside the store.
-__device__ __forceinline__ int64_t row_offset(const StoreView& s, int64_t g, int32_t h, int32_t H,
-                                              int32_t t, int32_t vpr) {
-  if (t < 0 || (int64_t)t >= s.max_rows) return -1;
-  if (!s.paged) return (g * H + h) * s.list_stride_v + (int64_t)t * vpr;
-  const int32_t page = s.page_table[g * s.pt_ld + (t >> s.page_shift)];
-  if (page < 0 || (int64_t)page >= s.capacity) return -1;
-  const int64_t slot = ((int64_t)page << s.page_shift) + (t & ((1 << s.page_shift) - 1));
-  return (slot * H + h) * vpr;
-}
-
 __device__ __forceinline__ int32_t count_of(const InplaceArgs& a, int64_t idx_list) {
   if (!a.kept_count) return a.K;
   const int32_t c = a.kept_count[idx_list];
   return c < 0 ? 0 : (c > a.K ? a.K : c);
 }
 
-// Bits of the calling thread's 32-lane team in a wave ballot.
-__device__ __forceinline__ uint32_t team_bits(uint64_t ballot) {
-  return (uint32_t)(ballot >> (32 * ((threadIdx.x % kWave) / kTeam)));
+// Smallest thread index whose flag is set, or kThreads (whole workgroup).
+__device__ __forceinline__ int32_t block_first(bool hit, int32_t* s_min) {
+  const int wave = threadIdx.x / kWave;
+  const uint64_t b = __ballot(hit);
+  if (lane_id() == 0) s_min[wave] = b ? wave * kWave + (int32_t)__builtin_ctzll(b) : kThreads;
+  __syncthreads();
+  int32_t r = s_min[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = min(r, s_min[w]);
+  __syncthreads();
+  return r;
 }
 
+// Smallest j < c with idx[j] != j, or c if the list keeps its prefix whole.
+// idx[j] != j is false up to the first moved row and true from there on.
+__device__ int32_t first_moved(const int32_t* __restrict__ idx, int32_t c, int32_t* s_min) {
+  if (c <= 0) return c;
+  const int32_t tid = threadIdx.x;
+  const int32_t step = (c + kThreads - 1) / kThreads;
+  const int32_t s = tid * step;
+  const int32_t q = block_first(s < c && idx[s] != s, s_min);
+  int32_t lo, hi;  // the first moved row lies in [lo, hi], or is c if none
+  if (q < kThreads) {
+    lo = q == 0 ? 0 : (q - 1) * step + 1;
+    hi = q * step;
+  } else {
+    lo = ((c - 1) / step) * step + 1;
+    hi = c - 1;
+  }
+  for (int32_t b = lo; b <= hi; b += kThreads) {
+    const int32_t j = b + tid;
+    const int32_t r = block_first(j <= hi && idx[j] != j, s_min);
+    if (r < kThreads) return b + r;
+  }
+  return c;
+}
+
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void compact_inplace_kernel(InplaceArgs a) {
-  __shared__ int32_t s_first[kMaxTeams];
-  __shared__ int32_t s_cmax[kMaxTeams];
-  const int64_t g = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int team = tid / kTeam, k = tid % kTeam;
-  const int32_t nlists = a.ipg;  // index lists of the group
+  __shared__ int32_t s_min[kWaves];
+  const int32_t H = a.H;
+  const int64_t g = blockIdx.x / H;
+  const int32_t h = (int32_t)(blockIdx.x - g * H);
+  const int32_t tid = threadIdx.x;
+  const int64_t il = g * a.ipg + (a.ipg == 1 ? 0 : h);
+  const int32_t* __restrict__ idx = a.kept_idx + il * a.kept_ld;
+  const int32_t c = count_of(a, il);
+  const int32_t first = first_moved(idx, c, s_min);
+  const int32_t vpr = a.vpr;
+  const int32_t E = (c - first) * vpr;  // vectors of the rows [first, c)
+  const int32_t nq = (E + kChunk - 1) / kChunk;
+  const int32_t* __restrict__ pt = kPaged ? a.st.page_table + g * a.st.pt_ld : nullptr;
+  const int32_t shift = a.st.page_shift, pmask = (1 << shift) - 1;
+  const int64_t cap = a.st.capacity, max_rows = a.st.max_rows;
+  const int64_t list_base = kPaged ? 0 : (g * H + h) * a.st.list_stride_v;
+  vec4u* kb = a.k;
+  vec4u* vb = a.v;
 
-  // --- first moved row and largest count over the group's index lists -------
-  int32_t first = 0x7fffffff, cmax = 0;
-  for (int32_t l0 = 0; l0 < nlists; l0 += kMaxTeams) {
-    const int32_t l = l0 + team;
-    const bool have = l < nlists;  // uniform per team
-    const int64_t il = g * a.ipg + (have ? l : 0);
-    const int32_t c = have ? count_of(a, il) : 0;
-    const int32_t* idx = a.kept_idx + il * a.kept_ld;
-    // round 1: samples 0, step, 2*step, ... (idx[j] != j is false, then true)
-    const int32_t step = c > 0 ? (c + kTeam - 1) / kTeam : 1;
-    const int32_t s = k * step;
-    uint32_t m = team_bits(__ballot(have && s < c && idx[s] != s));
-    int32_t lo, hi;  // the first moved row lies in [lo, hi], or is c if none
-    if (m) {
-      const int32_t kk = __builtin_ctz(m);
-      lo = kk == 0 ? 0 : (kk - 1) * step + 1;
-      hi = kk * step;
-    } else {  // after the last sample below c
-      lo = c > 0 ? ((c - 1) / step) * step + 1 : 0;
-      hi = c - 1;
-    }
-    // round 2: scan [lo, hi] in steps of 32
-    int32_t f = c;
-    for (int32_t b = lo; b <= hi && f == c; b += kTeam) {
-      const int32_t j = b + k;
-      m = team_bits(__ballot(have && j <= hi && j < c && idx[j] != j));
-      if (m) f = b + __builtin_ctz(m);
-    }
-    if (have) {
-      if (f < c) first = min(first, f);  // lists with nothing to move do not count
-      cmax = max(cmax, c);
-    }
-  }
-  if (k == 0) {
-    s_first[team] = first;
-    s_cmax[team] = cmax;
-  }
-  __syncthreads();
+  // row j and kept index t of element u of chunk q (t == j: nothing to move)
+  auto fetch_idx = [&](int32_t q, int32_t (&j)[kVecs], int32_t (&t)[kVecs]) {
 #pragma unroll
-  for (int t = 0; t < kMaxTeams; ++t) {
-    first = min(first, s_first[t]);
-    cmax = max(cmax, s_cmax[t]);
-  }
+    for (int u = 0; u < kVecs; ++u) {
+      const int32_t e = q * kChunk + u * kThreads + tid;
+      j[u] = -1;
+      t[u] = -1;
+      if (e < E) {
+        j[u] = first + e / vpr;
+        t[u] = idx[j[u]];
+      }
+    }
+  };
+  // page ids of the source and destination rows (paged only)
+  auto fetch_pages = [&](const int32_t (&j)[kVecs], const int32_t (&t)[kVecs],
+                         int32_t (&sp)[kVecs], int32_t (&dp)[kVecs]) {
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      sp[u] = -1;
+      dp[u] = -1;
+      if (kPaged && t[u] != j[u]) {
+        if (t[u] > j[u] && (int64_t)t[u] < max_rows) sp[u] = pt[t[u] >> shift];
+        dp[u] = pt[j[u] >> shift];
+      }
+    }
+  };
 
-  // --- move the rows [first, cmax) in chunks, loads before stores -------------
-  const int32_t vpr = a.vpr, H = a.H;
-  const int32_t tok_vecs = H * vpr;
-  const int32_t rows = (kThreads * kVecs) / tok_vecs > 0 ? (kThreads * kVecs) / tok_vecs : 1;
-  for (int32_t j0 = first; j0 < cmax; j0 += rows) {
-    const int32_t nvec = min(rows, cmax - j0) * tok_vecs;
+  int32_t j1[kVecs], t1[kVecs], sp1[kVecs], dp1[kVecs];  // chunk q: ready to move
+  int32_t j2[kVecs], t2[kVecs];                          // chunk q + 1: indices known
+  if (nq > 0) {
+    fetch_idx(0, j1, t1);
+    fetch_idx(1, j2, t2);
+    fetch_pages(j1, t1, sp1, dp1);
+  }
+  for (int32_t q = 0; q < nq; ++q) {
     vec4u kr[kVecs], vr[kVecs];
     int64_t dof[kVecs];
-    for (int32_t base = 0; base < nvec; base += kThreads * kVecs) {
 #pragma unroll
-      for (int u = 0; u < kVecs; ++u) {
-        const int32_t e = base + tid + u * kThreads;
-        dof[u] = -1;
-        if (e >= nvec) continue;
-        const int32_t j = j0 + e / tok_vecs;
-        const int32_t rem = e % tok_vecs;
-        const int32_t h = rem / vpr, col = rem - h * vpr;
-        const int64_t il = g * a.ipg + (a.ipg == 1 ? 0 : h);
-        if (j >= count_of(a, il)) continue;
-        const int32_t t = a.kept_idx[il * a.kept_ld + j];
-        if (t == j) continue;  // unchanged row
-        const int64_t so = t > j ? row_offset(a.st, g, h, H, t, vpr) : -1;
-        const int64_t d = row_offset(a.st, g, h, H, j, vpr);
-        if (so >= 0 && d >= 0) {
-          kr[u] = __builtin_nontemporal_load(a.k + so + col);
-          vr[u] = __builtin_nontemporal_load(a.v + so + col);
-          dof[u] = d + col;
-        } else if (col == 0 && a.errors) {
-          atomicAdd(a.errors, 1u);  // index below its slot, out of range, or bad page
+    for (int u = 0; u < kVecs; ++u) {
+      dof[u] = -1;
+      const int32_t j = j1[u], t = t1[u];
+      if (t == j) continue;  // unchanged row or no element
+      const int32_t col = (q * kChunk + u * kThreads + tid) - (j - first) * vpr;
+      int64_t so = -1, d = -1;
+      if (t > j && (int64_t)t < max_rows) {
+        if (kPaged) {
+          if (sp1[u] >= 0 && sp1[u] < cap && dp1[u] >= 0 && dp1[u] < cap) {
+            so = ((((int64_t)sp1[u] << shift) + (t & pmask)) * H + h) * vpr + col;
+            d = ((((int64_t)dp1[u] << shift) + (j & pmask)) * H + h) * vpr + col;
+          }
+        } else {
+          so = list_base + (int64_t)t * vpr + col;
+          d = list_base + (int64_t)j * vpr + col;
         }
       }
-      // every load of the chunk has returned before any thread stores
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kVecs; ++u) {
-        if (dof[u] >= 0) {
-          __builtin_nontemporal_store(kr[u], a.k + dof[u]);
-          __builtin_nontemporal_store(vr[u], a.v + dof[u]);
-        }
+      if (so >= 0) {
+        kr[u] = __builtin_nontemporal_load(kb + so);
+        vr[u] = __builtin_nontemporal_load(vb + so);
+        dof[u] = d;
+      } else if (col == 0 && a.errors) {
+        atomicAdd(a.errors, 1u);  // index below its slot, out of range, or bad page
       }
+    }
+    int32_t sp2[kVecs], dp2[kVecs], j3[kVecs], t3[kVecs];
+    fetch_pages(j2, t2, sp2, dp2);
+    fetch_idx(q + 2, j3, t3);
+    // every load of the chunk has returned before any thread stores
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      if (dof[u] >= 0) {
+        __builtin_nontemporal_store(kr[u], kb + dof[u]);
+        __builtin_nontemporal_store(vr[u], vb + dof[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVecs; ++u) {
+      j1[u] = j2[u];
+      t1[u] = t2[u];
+      sp1[u] = sp2[u];
+      dp1[u] = dp2[u];
+      j2[u] = j3[u];
+      t2[u] = t3[u];
     }
   }
 
-  // --- paged: return the tail pages of the group to the free list -------------
-  if (a.st.paged && a.freed) {
-    const int32_t ps = 1 << a.st.page_shift;
-    const int32_t keep = (cmax + ps - 1) / ps;
+  // --- paged: the first head's workgroup returns the group's tail pages -------
+  if (kPaged && a.freed && h == 0) {
+    __shared__ int32_t s_cmax;
+    __shared__ uint32_t s_base;
+    if (tid == 0) s_cmax = 0;
+    __syncthreads();
+    int32_t cm = 0;
+    for (int32_t l = tid; l < a.ipg; l += kThreads) cm = max(cm, count_of(a, g * a.ipg + l));
+    atomicMax(&s_cmax, cm);
+    __syncthreads();
+    const int32_t ps = 1 << shift;
+    const int32_t keep = (s_cmax + ps - 1) / ps;
     const int32_t used = (a.n + ps - 1) / ps;
     const int32_t nfree = used > keep ? used - keep : 0;
-    __shared__ uint32_t s_base;
     if (tid == 0 && nfree > 0) s_base = atomicAdd(a.freed_count, (uint32_t)nfree);
     __syncthreads();
-    for (int32_t i = tid; i < nfree; i += kThreads)
-      a.freed[s_base + i] = a.st.page_table[g * a.st.pt_ld + keep + i];
+    for (int32_t i = tid; i < nfree; i += kThreads) a.freed[s_base + i] = pt[keep + i];
   }
 }
 
@@ -183,7 +224,9 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
                                   const int32_t* kept_count, int32_t K, int32_t n,
                                   int64_t num_groups, int32_t ipg, int32_t* freed,
                                   uint32_t* freed_count, uint32_t* errors, hipStream_t stream) {
-  if (num_groups == 0) return hipSuccess;
+  if (num_groups == 0 || H == 0) return hipSuccess;
+  if (num_groups * H > 0x7fffffffLL || (int64_t)n * (D / 8) > (1LL << 30))
+    return hipErrorInvalidValue;
   InplaceArgs a;
   a.st = st;
   a.k = static_cast<vec4u*>(k);
@@ -199,8 +242,11 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
   a.freed = freed;
   a.freed_count = freed_count;
   a.errors = errors;
-  hipLaunchKernelGGL(compact_inplace_kernel, dim3((unsigned)num_groups), dim3(kThreads), 0, stream,
-                     a);
+  const dim3 grid((unsigned)(num_groups * H));
+  if (st.paged)
+    hipLaunchKernelGGL(compact_inplace_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(compact_inplace_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -529,6 +529,8 @@ def keep_sets(lists, n, K, prot, seed, variable=False):
     ("paged", False, False, 128),
     ("paged", True, False, 128),
     ("paged", False, True, 64),
+    ("contig", False, True, 40),   # D / 8 odd: rows straddle chunk boundaries
+    ("paged", True, True, 24),
 ])
 def test_compact_inplace(layout, shared, variable, D):
     groups, H, ps, n, K, prot = 5, 4, 16, 300, 240, 37
