@@ -63,6 +63,8 @@ def describe(cfg) -> str:
                 f"{rule}, {layout}")
     if cfg.inplace:
         layout += ", compacted in place (unchanged prefix stays, freed pages to a list)"
+    if cfg.fused:
+        layout += ", draw + top-K + move in one launch"
     draw = ("shared draw per layer" if cfg.shared else
             "one list per layer by the max of per-head random scores, kept count a multiple of 4"
             if cfg.shared_max else
@@ -99,6 +101,7 @@ class Timer:
 
 def time_workload(torch, rounds, cfg, steps, warmup):
     st = rounds.make_state(cfg, "cuda")
+    phases = rounds.phases(cfg)
     torch.cuda.synchronize()
     round_id = 0
     survival = None
@@ -114,19 +117,16 @@ def time_workload(torch, rounds, cfg, steps, warmup):
             rounds.swap(st)
             round_id += 1
         torch.cuda.synchronize()
-        timer = Timer(torch, ["score", "select", "compact"])
+        timer = Timer(torch, [name for name, _ in phases])
         total_ms = 0.0
         for _ in range(steps):
             t0 = torch.cuda.Event(enable_timing=True)
             t1 = torch.cuda.Event(enable_timing=True)
             t0.record()
             timer.mark()
-            rounds.score(st, round_id)
-            timer.mark()
-            rounds.select(st)
-            timer.mark()
-            rounds.compact(st)
-            timer.mark()
+            for _, fn in phases:
+                fn(st, round_id)
+                timer.mark()
             t1.record()
             st.applied_rounds += 1
             survival.after_round(st)
@@ -141,7 +141,7 @@ def time_workload(torch, rounds, cfg, steps, warmup):
         for _ in range(warmup):
             rounds.restore(st)
             rounds.run_round(st, 0)
-        timer = Timer(torch, ["score", "select", "compact"])
+        timer = Timer(torch, [name for name, _ in phases])
         total_ms = 0.0
         for s in range(steps):
             rounds.restore(st)
@@ -149,12 +149,9 @@ def time_workload(torch, rounds, cfg, steps, warmup):
             t1 = torch.cuda.Event(enable_timing=True)
             t0.record()
             timer.mark()
-            rounds.score(st, s)
-            timer.mark()
-            rounds.select(st)
-            timer.mark()
-            rounds.compact(st)
-            timer.mark()
+            for _, fn in phases:
+                fn(st, s)
+                timer.mark()
             t1.record()
             st.applied_rounds += 1
             torch.cuda.synchronize()
@@ -164,16 +161,13 @@ def time_workload(torch, rounds, cfg, steps, warmup):
         for _ in range(warmup):
             rounds.run_round(st, 0)
         torch.cuda.synchronize()
-        timer = Timer(torch, ["score", "select", "compact"])
+        timer = Timer(torch, [name for name, _ in phases])
         t_start = time.perf_counter()
         for s in range(steps):
             timer.mark()
-            rounds.score(st, s)
-            timer.mark()
-            rounds.select(st)
-            timer.mark()
-            rounds.compact(st)
-            timer.mark()
+            for _, fn in phases:
+                fn(st, s)
+                timer.mark()
             st.applied_rounds += 1
         torch.cuda.synchronize()
         ms_per = (time.perf_counter() - t_start) * 1e3 / steps
@@ -273,7 +267,8 @@ def main():
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
         names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
-                 "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace"]
+                 "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
+                 "paged_fused", "longgen_fused"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None
@@ -283,7 +278,7 @@ def main():
         print(f"# timing {name}", file=sys.stderr, flush=True)
         steps = args.steps if cfg.rounds == 1 else min(args.steps, cfg.rounds)
         r = time_workload(torch, rounds, cfg, steps, args.warmup)
-        comp_ms = r["kernels_ms"]["compact"]
+        comp_ms = r["kernels_ms"]["fused" if cfg.fused else "compact"]
         achieved = r["kv_bytes"] / (comp_ms * 1e-3) / 1e9
         entry = {
             "workload": describe(cfg),

@@ -297,6 +297,34 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
                                        int32_t* freed_pages, uint32_t* freed_count,
                                        uint32_t* errors, hipStream_t stream);
 
+/*
+ * One-launch Random Attention round with in-place compaction ([RA] Algorithm 1:
+ * random scores, the prompt pinned, top-K per KV head, the keep set returned;
+ * [RA] engine paragraph: per-KV-head physical eviction with chronological
+ * compaction; [GS] Sec. 4.3 and Appendix G: kept entries move to the front of
+ * their own pages and the freed tail blocks return to the pool).
+ *
+ * The result equals kvevict_score_random (same seed, round, L and draw mode)
+ * followed by kvevict_select_topk (K, prot) and kvevict_compact_inplace (K, n),
+ * but no score or index buffer is read from or written to memory.
+ * Groups g = req*L + layer for req < num_requests; heads from the store.
+ * kept_idx    optional device int32 out: the keep set of each list, increasing,
+ *             row list*kept_ld (list = g*H + h per head, g when shared), kept_ld >= K.
+ * shared_draw != 0: one keep set per group, the head-0 draw, applied to every head.
+ * freed_pages, freed_count, errors: as in kvevict_compact_inplace (every list
+ *             keeps K, so pages ceil(K / page_size) .. ceil(n / page_size) - 1 are freed).
+ * Requires 0 <= prot <= K <= n <= rows of a list, num_requests < 2^32, L >= 1;
+ * KVEVICT_ERR_UNSUPPORTED when (n - prot) + K > 15360 (keys and indices are held on chip).
+ * Limits of kvevict_compact_inplace apply.  Calls on the same store must not overlap.
+ */
+kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* k, void* v,
+                                           int64_t num_requests, int32_t L, int32_t n, int32_t K,
+                                           int32_t prot, uint64_t seed, uint32_t round,
+                                           int32_t shared_draw, int32_t* kept_idx,
+                                           int64_t kept_ld, int32_t* freed_pages,
+                                           uint32_t* freed_count, uint32_t* errors,
+                                           hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kvevict_status_string(kvevict_status status);
 

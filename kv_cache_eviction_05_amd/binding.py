@@ -29,7 +29,7 @@ LAYOUT_PAGED = 1
 
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
-           "kvevict_score_keydiff", "kvevict_compact_inplace",
+           "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -81,12 +81,15 @@ def load():
     lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
     lib.kvevict_score_keydiff.argtypes = [_p, _i64, ctypes.POINTER(KvDesc), _p, _i64, _i32, _i32,
                                           _p]
+    lib.kvevict_evict_random_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _i64, _i32, _i32,
+                                                 _i32, _i32, _u64, _u32, _i32, _p, _i64, _p, _p,
+                                                 _p, _p]
     lib.kvevict_compact_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _p, _i64, _p, _i32,
                                             _i32, _i64, _i32, _p, _p, _p, _p]
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
-                 "kvevict_compact", "kvevict_compact_inplace"):
+                 "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -310,3 +313,24 @@ def kvevict_compact_inplace(store: KvDesc, k, v, kept_idx, kept_ld, kept_count, 
                                           idx_lists_per_group, _ptr(freed_pages),
                                           _ptr(freed_count), _ptr(errors), _stream(stream)),
            "kvevict_compact_inplace")
+
+
+def kvevict_evict_random_inplace(store: KvDesc, k, v, num_requests, L, n, K, prot, seed, round_id,
+                                 shared_draw, kept_idx=None, kept_ld=0, freed_pages=None,
+                                 freed_count=None, errors=None, stream=None):
+    num_groups = num_requests * L
+    _need(k, torch.bfloat16, _store_elems(store, num_groups), "k")
+    _need(v, torch.bfloat16, _store_elems(store, num_groups), "v")
+    lists = num_groups * (1 if shared_draw else store.heads)
+    _need(kept_idx, torch.int32, _rows(lists, kept_ld, K), "kept_idx")
+    _need(errors, torch.int32, 1, "errors")
+    if store.layout == LAYOUT_PAGED and num_groups > 0:
+        _need(store._pt, torch.int32, num_groups * store.pt_ld, "page table")
+        _need(freed_pages, torch.int32, num_groups * -(-n // store.page_size), "freed_pages")
+        _need(freed_count, torch.int32, 1, "freed_count")
+    _check(load().kvevict_evict_random_inplace(ctypes.byref(store), _ptr(k), _ptr(v), num_requests,
+                                               L, n, K, prot, seed, round_id,
+                                               1 if shared_draw else 0, _ptr(kept_idx), kept_ld,
+                                               _ptr(freed_pages), _ptr(freed_count), _ptr(errors),
+                                               _stream(stream)),
+           "kvevict_evict_random_inplace")

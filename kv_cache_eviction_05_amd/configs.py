@@ -1,6 +1,6 @@
 """Workload shapes of the eviction round.
 
-Five synthetic workloads, each a single-GPU share at its real shape:
+Synthetic workloads, each a single-GPU share at its real shape:
 
   tiny      1 layer x 2 KV heads, D=128, n=1088 (K=1024 + r=64), prot=32,
             per-head random draw, contiguous storage.
@@ -28,6 +28,10 @@ Five synthetic workloads, each a single-GPU share at its real shape:
             the paged and the 30-round workloads compacted in place: kept rows
             move to the front of their own rows or pages, the unchanged prefix
             stays, freed tail pages go to a free list.
+  paged_fused, longgen_fused
+            the same two in-place rounds as one launch per round: random draw,
+            pin, top-K and in-place move per (request, layer, head), with no
+            score or index buffer in memory.
 
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
@@ -56,6 +60,7 @@ class RoundConfig:
     shared: bool = False       # one draw per (request, layer), applied to all heads
     shared_max: bool = False   # one list per (request, layer) ranked by the max over heads
     inplace: bool = False      # compact in place (front of the same rows / pages)
+    fused: bool = False        # draw + select + in-place move in one launch (random, top-K)
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -125,6 +130,9 @@ KEYDIFF = replace(BATCH, name="keydiff", scorer="keydiff")
 # in-place compaction to the front of the same pages, freed tail pages to a pool
 PAGED_INPLACE = replace(PAGED, name="paged_inplace", inplace=True)
 LONGGEN_INPLACE = replace(LONGGEN, name="longgen_inplace", inplace=True)
+PAGED_FUSED = replace(PAGED_INPLACE, name="paged_fused", fused=True)
+LONGGEN_FUSED = replace(LONGGEN_INPLACE, name="longgen_fused", fused=True)
 
 ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
-                           PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE)}
+                           PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE,
+                           PAGED_FUSED, LONGGEN_FUSED)}

@@ -320,6 +320,33 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
                                                     freed_count, errors, stream));
 }
 
+kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* k, void* v,
+                                           int64_t num_requests, int32_t L, int32_t n, int32_t K,
+                                           int32_t prot, uint64_t seed, uint32_t round,
+                                           int32_t shared_draw, int32_t* kept_idx,
+                                           int64_t kept_ld, int32_t* freed_pages,
+                                           uint32_t* freed_count, uint32_t* errors,
+                                           hipStream_t stream) {
+  if (!store) return KVEVICT_ERR_INVALID_ARG;
+  if (num_requests < 0 || num_requests > 0xffffffffll || L < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (prot < 0 || K < prot || n < K) return KVEVICT_ERR_INVALID_ARG;
+  if (kept_idx && kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t num_groups = num_requests * L;
+  const int32_t H = store->heads, D = store->head_dim;
+  kvevict::StoreView sv;
+  const kvevict_status st = check_store(store, k, v, num_groups, &sv);
+  if (st != KVEVICT_OK) return st;
+  if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;
+  if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;
+  if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if ((int64_t)(n - prot) + K > kvevict::kMaxFusedEntries) return KVEVICT_ERR_UNSUPPORTED;
+  return hip_status(kvevict::launch_evict_random_inplace(
+      sv, k, v, D, H, num_groups, L, n, K, prot, seed, round, shared_draw != 0, kept_idx, kept_ld,
+      sv.paged ? freed_pages : nullptr, freed_count, errors, stream));
+}
+
 const char* kvevict_status_string(kvevict_status status) {
   switch (status) {
     case KVEVICT_OK: return "ok";

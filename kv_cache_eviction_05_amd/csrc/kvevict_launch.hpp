@@ -72,4 +72,14 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
                                   int64_t num_groups, int32_t ipg, int32_t* freed,
                                   uint32_t* freed_count, uint32_t* errors, hipStream_t stream);
 
+// Random draw + pin + top-K + in-place compaction of every (group, head) in
+// one launch; (n - prot) + K keys and indices live in LDS.
+constexpr int32_t kMaxFusedEntries = 15360;
+hipError_t launch_evict_random_inplace(const StoreView& st, void* k, void* v, int32_t D,
+                                       int32_t H, int64_t num_groups, int32_t L, int32_t n,
+                                       int32_t K, int32_t prot, uint64_t seed, uint32_t round,
+                                       bool shared_draw, int32_t* kept_idx, int64_t kept_ld,
+                                       int32_t* freed, uint32_t* freed_count, uint32_t* errors,
+                                       hipStream_t stream);
+
 }  // namespace kvevict

@@ -5,20 +5,17 @@
 // list per layer ranked by the larger of its per-head scores).
 //
 // One workgroup (256 threads, 4 waves) per list.  The n - prot candidate keys
-// (rank_key of the score) are staged in LDS; an 8-bit-digit radix select
-// (at most 4 histogram passes, stopping as soon as the chosen bucket is taken
-// whole) finds the threshold key T and how many keys equal to T are kept.
-// The kept indices are then emitted in increasing order with wave ballots and
-// mbcnt prefix counts: a kept entry's output slot is the number of kept
-// entries before it, so ties at T go to the lowest positions.
+// (rank_key of the score) are staged in LDS, then the radix select and the
+// chronological emit of select_lds.hpp write the kept indices in increasing
+// order, ties at the threshold to the lowest positions.
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
+#include "select_lds.hpp"
 
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kThreads = kSelectThreads;
 constexpr int32_t kMaxLdsKeys = 15360;  // 60 KiB of keys (+ ~1 KiB static LDS)
 
 struct TopkArgs {
@@ -39,10 +36,7 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
   const int64_t kept_ld = a.kept_ld, ld = a.ld;
   const int32_t n = a.n, prot = a.prot;
   extern __shared__ uint32_t s_keys[];
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_pick[3];
-  __shared__ uint32_t s_tile[2 * kWaves];
+  __shared__ SelectShared sh;
 
   const int64_t list = blockIdx.x;
   const float* row = scores + list * ld;
@@ -50,7 +44,6 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
   const int32_t m = n - prot;  // candidates
   const int32_t kk = a.L > 0 ? a.kk[(list / a.H) % a.L] : a.K - prot;  // candidates to keep
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
 
   for (int32_t j = tid; j < prot; j += kThreads) out[j] = j;
   if (a.kept_count && tid == 0) a.kept_count[list] = prot + kk;
@@ -64,79 +57,10 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
     return kKeysInLds ? s_keys[i] : rank_key(row[prot + i]);
   };
 
-  // --- radix select of the kk-th largest key --------------------------------
   uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate
-  if (kk < m) {
-    uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)kk;
-    bool whole_bucket = false;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      s_hist[tid] = 0u;
-      __syncthreads();
-      for (int32_t i = tid; i < m; i += kThreads) {
-        const uint32_t k = key_at(i);
-        if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // thread t holds bin 255 - t, so the inclusive scan counts keys in bins >= 255 - t
-      const uint32_t c = s_hist[255 - tid];
-      uint32_t total;
-      const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
-      const uint32_t excl = incl - c;
-      if (excl < remaining && incl >= remaining) {
-        s_pick[0] = 255u - (uint32_t)tid;
-        s_pick[1] = remaining - excl;
-        s_pick[2] = c;
-      }
-      __syncthreads();
-      const uint32_t digit = s_pick[0];
-      const uint32_t cnt = s_pick[2];
-      remaining = s_pick[1];
-      prefix |= digit << shift;
-      mask |= 0xffu << shift;
-      __syncthreads();
-      if (remaining == cnt) {  // the whole bucket is kept: keep every key >= prefix
-        whole_bucket = true;
-        break;
-      }
-    }
-    thr = prefix;
-    need_eq = whole_bucket ? 0xffffffffu : remaining;
-  }
-
-  // --- chronological emit --------------------------------------------------
-  uint32_t carry_gt = 0u, carry_eq = 0u;
-  for (int32_t base = 0; base < m; base += kThreads) {
-    const int32_t i = base + tid;
-    const bool valid = i < m;
-    const uint32_t k = valid ? key_at(i) : 0u;
-    const bool gt = valid && k > thr;
-    const bool eq = valid && k == thr;
-    const uint64_t bg = __ballot(gt);
-    const uint64_t be = __ballot(eq);
-    if (lane_id() == 0) {
-      s_tile[wave] = (uint32_t)__popcll(bg);
-      s_tile[kWaves + wave] = (uint32_t)__popcll(be);
-    }
-    __syncthreads();
-    uint32_t pre_gt = 0u, pre_eq = 0u, tot_gt = 0u, tot_eq = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t g = s_tile[w], e = s_tile[kWaves + w];
-      pre_gt += (w < wave) ? g : 0u;
-      pre_eq += (w < wave) ? e : 0u;
-      tot_gt += g;
-      tot_eq += e;
-    }
-    __syncthreads();
-    const uint32_t gt_before = carry_gt + pre_gt + count_below(bg);
-    const uint32_t eq_before = carry_eq + pre_eq + count_below(be);
-    if (gt || (eq && eq_before < need_eq)) {
-      const uint32_t slot = (uint32_t)prot + gt_before + min(eq_before, need_eq);
-      out[slot] = prot + i;
-    }
-    carry_gt += tot_gt;
-    carry_eq += tot_eq;
-  }
+  if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
+  emit_kept(key_at, m, thr, need_eq, sh,
+            [&](uint32_t slot, int32_t i) { out[prot + slot] = prot + i; });
 }
 
 }  // namespace

@@ -6,6 +6,7 @@ problem statement for the global budget):
 
     random draw:   kvevict_score_random -> kvevict_select_topk -> kvevict_compact
     weighted:      kvevict_score_weighted -> kvevict_select_global -> kvevict_compact
+    fused:         kvevict_evict_random_inplace (draw, pin, top-K, in-place move)
 
 Buffers are torch tensors used only as device memory; every step of the round
 runs in the HIP library.  The repeated-round driver (persistent budget K,
@@ -109,6 +110,9 @@ def _desc_pair(cfg: RoundConfig, n_src: int, cap_dst: int, device, seed: int):
 
 def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) -> RoundState:
     device = torch.device(device)
+    if cfg.fused and not (cfg.inplace and cfg.scorer == "random" and cfg.select == "topk"
+                          and not cfg.shared_max):
+        raise ValueError("the fused round is the random draw, top-K and in-place move")
     n = cfg.n
     cap_dst = n if cfg.select in ("global", "layers") else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
     if cfg.inplace:
@@ -203,10 +207,29 @@ def compact(st: RoundState, stream=None):
                       st.kept.shape[1], count, K, c.groups, ipg, st.errors, stream)
 
 
+def fused_round(st: RoundState, round_id: int, stream=None):
+    """Random draw, pin, top-K and in-place compaction of every list in one launch."""
+    c = st.cfg
+    B.kvevict_evict_random_inplace(st.src_desc, st.k_src, st.v_src, c.R, c.L, st.n, c.K, c.prot,
+                                   c.seed, round_id, c.shared, st.kept, st.kept.shape[1], st.freed,
+                                   st.freed_count, st.errors, stream)
+
+
+def phases(cfg: RoundConfig):
+    """The launches of one round as (name, fn(st, round_id)) in order."""
+    if cfg.fused:
+        return [("fused", fused_round)]
+    return [("score", score), ("select", lambda st, rid: select(st)),
+            ("compact", lambda st, rid: compact(st))]
+
+
 def run_round(st: RoundState, round_id: int = 0, stream=None):
-    score(st, round_id, stream)
-    select(st, stream)
-    compact(st, stream)
+    if st.cfg.fused:
+        fused_round(st, round_id, stream)
+    else:
+        score(st, round_id, stream)
+        select(st, stream)
+        compact(st, stream)
     st.applied_rounds += 1
 
 

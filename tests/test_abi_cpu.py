@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                           "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                           "kvevict_reduce_max_heads", "kvevict_score_keydiff",
-                          "kvevict_compact_inplace", "kvevict_select_global", "kvevict_compact",
+                          "kvevict_compact_inplace", "kvevict_evict_random_inplace",
+                          "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
@@ -206,3 +207,54 @@ def test_score_keydiff_validation():
     assert st(d, 1088, 4, 1088, 1089) == B.KVEVICT_ERR_INVALID_ARG     # prot > n
     assert st(d, 1088, -1, 1088, 0) == B.KVEVICT_ERR_INVALID_ARG
     assert status("kvevict_score_keydiff", FAKE, 1088, None, FAKE, 4, 1088, 0, None) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_compact_inplace_validation():
+    D, H = 128, 8
+    c = B.contig_desc(D, H, 1088)
+    pg = B.KvDesc(B.LAYOUT_PAGED, D, H, 16, 1000, 0, FAKE, 68)
+
+    def call(d=c, k=FAKE, v=FAKE * 2, K=1024, n=1088, kept_ld=1024, groups=4, ipg=H, freed=FAKE * 3,
+             fcount=FAKE * 4):
+        return status("kvevict_compact_inplace", ctypes.byref(d), k, v, FAKE, kept_ld, None, K, n,
+                      groups, ipg, freed, fcount, None, None)
+
+    assert call(n=1000) == B.KVEVICT_ERR_INVALID_ARG            # n < K
+    assert call(kept_ld=1000) == B.KVEVICT_ERR_INVALID_ARG      # kept_ld < K
+    assert call(ipg=3) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(v=FAKE) == B.KVEVICT_ERR_INVALID_ARG            # K and V alias
+    assert call(n=1089) == B.KVEVICT_ERR_INVALID_ARG            # n beyond the store
+    assert call(k=FAKE + 8) == B.KVEVICT_ERR_ALIGNMENT
+    assert call(d=pg, freed=None) == B.KVEVICT_ERR_INVALID_ARG  # paged needs the free list
+    assert call(d=pg, fcount=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(d=pg, n=1089) == B.KVEVICT_ERR_INVALID_ARG      # 68 pages x 16 = 1088 rows
+    assert call(groups=-1) == B.KVEVICT_ERR_INVALID_ARG
+    huge = B.contig_desc(1 << 16, 1, 1 << 18)                   # n * D / 8 = 2^31 > 2^30
+    assert call(d=huge, K=16, n=1 << 18, kept_ld=16, groups=1, ipg=1) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_evict_random_inplace_validation():
+    D, H = 128, 8
+    c = B.contig_desc(D, H, 4096)
+    pg = B.KvDesc(B.LAYOUT_PAGED, D, H, 16, 1000, 0, FAKE, 132)
+
+    def call(d=c, k=FAKE, v=FAKE * 2, R=4, L=36, n=1088, K=1024, prot=128, shared=0, kept=FAKE * 5,
+             kept_ld=1024, freed=FAKE * 3, fcount=FAKE * 4):
+        return status("kvevict_evict_random_inplace", ctypes.byref(d), k, v, R, L, n, K, prot, 0, 0,
+                      shared, kept, kept_ld, freed, fcount, None, None)
+
+    assert call(prot=1025) == B.KVEVICT_ERR_INVALID_ARG         # prot > K
+    assert call(K=1089) == B.KVEVICT_ERR_INVALID_ARG            # K > n
+    assert call(prot=-1) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(L=0) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(R=-1) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(R=1 << 32) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(kept_ld=1000) == B.KVEVICT_ERR_INVALID_ARG      # kept_ld < K with an output
+    assert call(v=FAKE) == B.KVEVICT_ERR_INVALID_ARG            # K and V alias
+    assert call(n=4097) == B.KVEVICT_ERR_INVALID_ARG            # n beyond the store
+    assert call(k=FAKE + 8) == B.KVEVICT_ERR_ALIGNMENT
+    assert call(d=pg, freed=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(d=pg, n=2113, K=2048, prot=1024, kept_ld=2048) == B.KVEVICT_ERR_INVALID_ARG
+    # candidates and kept indices must fit on chip: (n - prot) + K <= 15360
+    big = B.contig_desc(D, H, 16384)
+    assert call(d=big, n=9000, K=8000, prot=0, kept_ld=8000) == B.KVEVICT_ERR_UNSUPPORTED

@@ -522,6 +522,61 @@ def keep_sets(lists, n, K, prot, seed, variable=False):
     return np.ascontiguousarray(kept), counts
 
 
+def make_store(layout, groups, H, D, n, ps, seed):
+    """A seeded K/V store (contiguous lists of n rows, or a pool with a shuffled page table)."""
+    if layout == "contig":
+        shape, desc, pt = (groups * H, n, D), B.contig_desc(D, H, n), None
+    else:
+        pool = groups * (n // ps + 1) + 3
+        per = -(-n // ps)
+        rng = np.random.default_rng(seed)
+        pt = rng.permutation(pool)[: groups * per].astype(np.int32).reshape(groups, per)
+        shape = (pool, ps, H, D)
+        desc = B.paged_desc(D, H, ps, pool, torch.from_numpy(pt).to(DEV))
+    ks, vs = rand_bits(shape, seed + 40), rand_bits(shape, seed + 41)
+    return desc, pt, ks, vs, bf16_from_bits(ks), bf16_from_bits(vs)
+
+
+def check_inplace(layout, ks, vs, k, v, kept, counts, groups, H, ipg, pt, ps, n, K, D, freed, fcount):
+    """K/V after an in-place compaction against the oracle's gather of the original, rows past
+    each count untouched, and (paged) the freed pages as a set."""
+    shared = ipg == 1
+    gk, gv = u16(k), u16(v)
+    if layout == "contig":
+        kd = np.zeros((groups * H, K, D), np.uint16)
+        vd = np.zeros_like(kd)
+        oracle.compact({"list_stride": n * D}, ks, vs, {"list_stride": K * D}, kd, vd, kept, K, D,
+                       H, 0, groups, ipg=ipg, kept_count=counts)
+        for lst in range(groups * H):
+            c = K if counts is None else counts[(lst // H) * ipg + (0 if shared else lst % H)]
+            assert np.array_equal(gk[lst, :c], kd[lst, :c]), lst
+            assert np.array_equal(gv[lst, :c], vd[lst, :c]), lst
+            assert np.array_equal(gk[lst, c:], ks[lst, c:]), lst  # rows past the count untouched
+            assert np.array_equal(gv[lst, c:], vs[lst, c:]), lst
+        assert int(fcount.item()) == 0
+        return
+    per = pt.shape[1]
+    want_free = []
+    for g in range(groups):
+        il = np.arange(g * ipg, g * ipg + ipg)
+        cs = np.full(ipg, K) if counts is None else counts[il]
+        before_k = np.stack([ks[pt[g, t // ps], t % ps] for t in range(n)], 1)  # [H][n][D]
+        after_k = np.stack([gk[pt[g, t // ps], t % ps] for t in range(n)], 1)
+        before_v = np.stack([vs[pt[g, t // ps], t % ps] for t in range(n)], 1)
+        after_v = np.stack([gv[pt[g, t // ps], t % ps] for t in range(n)], 1)
+        for h in range(H):
+            li = 0 if shared else h
+            c = cs[li]
+            idx = kept[g * ipg + li, :c]
+            assert np.array_equal(after_k[h, :c], before_k[h, idx]), (g, h)
+            assert np.array_equal(after_v[h, :c], before_v[h, idx]), (g, h)
+            assert np.array_equal(after_k[h, c:], before_k[h, c:]), (g, h)
+        keep = -(-int(cs.max()) // ps)
+        want_free += list(pt[g, keep:per])
+    got_free = to_np(freed)[: int(fcount.item())]
+    assert sorted(got_free) == sorted(want_free)  # freed blocks verified against the pool
+
+
 @pytest.mark.parametrize("layout,shared,variable,D", [
     ("contig", False, False, 128),
     ("contig", True, False, 64),
@@ -537,19 +592,7 @@ def test_compact_inplace(layout, shared, variable, D):
     say(f"compact_inplace {layout} shared={shared} variable={variable} D={D}")
     ipg = 1 if shared else H
     kept, counts = keep_sets(groups * ipg, n, K, prot, seed=D + n, variable=variable)
-    pool = groups * (n // ps + 1) + 3
-    if layout == "contig":
-        shape = (groups * H, n, D)
-        desc = B.contig_desc(D, H, n)
-        pt = None
-    else:
-        shape = (pool, ps, H, D)
-        rng = np.random.default_rng(4)
-        per = -(-n // ps)
-        pt = rng.permutation(pool)[: groups * per].astype(np.int32).reshape(groups, per)
-        desc = B.paged_desc(D, H, ps, pool, torch.from_numpy(pt).to(DEV))
-    ks, vs = rand_bits(shape, 40), rand_bits(shape, 41)
-    k, v = bf16_from_bits(ks), bf16_from_bits(vs)
+    desc, pt, ks, vs, k, v = make_store(layout, groups, H, D, n, ps, seed=4)
     freed = torch.full((groups * (n // ps + 1),), -5, dtype=torch.int32, device=DEV)
     fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -558,43 +601,41 @@ def test_compact_inplace(layout, shared, variable, D):
                               groups, ipg, freed, fcount, err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    # want: the oracle's out-of-place compaction of the original, below each count
-    if layout == "contig":
-        kd = np.zeros((groups * H, K, D), np.uint16)
-        vd = np.zeros_like(kd)
-        oracle.compact({"list_stride": n * D}, ks, vs, {"list_stride": K * D}, kd, vd, kept, K, D,
-                       H, 0, groups, ipg=ipg, kept_count=counts if variable else None)
-        gk, gv = u16(k), u16(v)
-        for lst in range(groups * H):
-            c = counts[(lst // H) * ipg + (0 if shared else lst % H)]
-            assert np.array_equal(gk[lst, :c], kd[lst, :c]), lst
-            assert np.array_equal(gv[lst, :c], vd[lst, :c]), lst
-            assert np.array_equal(gk[lst, c:], ks[lst, c:]), lst  # rows past the count untouched
-            assert np.array_equal(gv[lst, c:], vs[lst, c:]), lst
-        assert int(fcount.item()) == 0
-    else:
-        gk, gv = u16(k), u16(v)
-        per = pt.shape[1]
-        want_free = []
-        for g in range(groups):
-            il = np.arange(g * ipg, g * ipg + ipg)
-            cs = counts[il] if variable else np.full(ipg, K)
-            # rows of the group as [H][n][D], before and after
-            before_k = np.stack([ks[pt[g, t // ps], t % ps] for t in range(n)], 1)  # [H][n][D]
-            after_k = np.stack([gk[pt[g, t // ps], t % ps] for t in range(n)], 1)
-            before_v = np.stack([vs[pt[g, t // ps], t % ps] for t in range(n)], 1)
-            after_v = np.stack([gv[pt[g, t // ps], t % ps] for t in range(n)], 1)
-            for h in range(H):
-                li = 0 if shared else h
-                c = cs[li]
-                idx = kept[g * ipg + li, :c]
-                assert np.array_equal(after_k[h, :c], before_k[h, idx]), (g, h)
-                assert np.array_equal(after_v[h, :c], before_v[h, idx]), (g, h)
-                assert np.array_equal(after_k[h, c:], before_k[h, c:]), (g, h)
-            keep = -(-int(cs.max()) // ps)
-            want_free += list(pt[g, keep:per])
-        got_free = to_np(freed)[: int(fcount.item())]
-        assert sorted(got_free) == sorted(want_free)  # freed blocks verified against the pool
+    check_inplace(layout, ks, vs, k, v, kept, counts if variable else None, groups, H, ipg, pt, ps,
+                  n, K, D, freed, fcount)
+
+
+@pytest.mark.parametrize("layout,shared,D,n,K,prot", [
+    ("contig", False, 128, 300, 240, 37),
+    ("contig", True, 40, 300, 240, 0),
+    ("paged", False, 128, 300, 240, 37),
+    ("paged", True, 64, 300, 256, 100),
+    ("paged", False, 24, 1100, 1030, 3),
+    ("contig", False, 64, 200, 200, 10),   # K == n: nothing is evicted, nothing moves
+    ("paged", False, 64, 200, 50, 50),     # prot == K: only the prompt stays
+])
+def test_evict_random_inplace(layout, shared, D, n, K, prot):
+    """The one-launch round equals the oracle's random score, top-K and gather, bit for bit."""
+    R, L, H, ps, seed, rnd = 2, 3, 4, 16, 11, 5
+    say(f"evict_random_inplace {layout} shared={shared} D={D} n={n} K={K} prot={prot}")
+    groups = R * L
+    ipg = 1 if shared else H
+    lists = groups * ipg
+    kept = oracle.select_topk(oracle.score_random(L, H, n, prot, seed, rnd, shared, 0, lists), K, prot)
+    desc, pt, ks, vs, k, v = make_store(layout, groups, H, D, n, ps, seed=7)
+    freed = torch.full((groups * (n // ps + 1),), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = torch.full((lists, K + 3), -9, dtype=torch.int32, device=DEV)
+    B.kvevict_evict_random_inplace(desc, k, v, R, L, n, K, prot, seed, rnd, shared, got, K + 3,
+                                   freed, fcount, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    g = to_np(got)
+    assert np.array_equal(g[:, :K], kept)
+    assert np.all(g[:, K:] == -9)
+    check_inplace(layout, ks, vs, k, v, np.ascontiguousarray(kept), None, groups, H, ipg, pt, ps, n,
+                  K, D, freed, fcount)
 
 
 def test_compact_inplace_rejects_bad_indices():

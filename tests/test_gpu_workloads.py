@@ -350,12 +350,14 @@ def test_keydiff_round_sampled():
     free()
 
 
-def test_paged_inplace_round_sampled():
-    """Paged round compacted in place: on sampled groups every head's first K rows are the kept
-    rows of the cache before the round and the rows past K are untouched; every group returns
-    its 4 tail pages (132 -> 128) and the free list holds exactly those pages."""
-    cfg = configs.PAGED_INPLACE.small(R=8)
-    say("paged in-place round: allocating")
+@pytest.mark.parametrize("base", [configs.PAGED_INPLACE, configs.PAGED_FUSED], ids=lambda c: c.name)
+def test_paged_inplace_round_sampled(base):
+    """Paged round compacted in place (three launches, or the one-launch fused round): on
+    sampled groups every head's first K rows are the kept rows of the cache before the round and
+    the rows past K are untouched; every group returns its 4 tail pages (132 -> 128) and the
+    free list holds exactly those pages."""
+    cfg = base.small(R=8)
+    say(f"{cfg.name} round: allocating")
     st = rounds.make_state(cfg, DEV)
     ps, H, D, n, K = cfg.page_size, cfg.H, cfg.D, cfg.n, cfg.K
     pt = st.src_pt.cpu().numpy()
@@ -385,10 +387,12 @@ def test_paged_inplace_round_sampled():
     free()
 
 
-def test_longgen_inplace_rounds_replayed_by_oracle():
+@pytest.mark.parametrize("base", [configs.LONGGEN_INPLACE, configs.LONGGEN_FUSED],
+                         ids=lambda c: c.name)
+def test_longgen_inplace_rounds_replayed_by_oracle(base):
     """30 rounds compacted in place on one request's 288 lists, replayed by the oracle."""
-    cfg = configs.LONGGEN_INPLACE.small(R=1)
-    say("longgen in-place replay")
+    cfg = base.small(R=1)
+    say(f"{cfg.name} replay")
     st = rounds.make_state(cfg, DEV)
     lists, n, K, D = cfg.lists, cfg.n, cfg.K, cfg.D
     host_k, host_v = u16(st.k_src), u16(st.v_src)
