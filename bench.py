@@ -65,6 +65,11 @@ def describe(cfg) -> str:
         layout += ", compacted in place (unchanged prefix stays, freed pages to a list)"
     if cfg.fused:
         layout += ", draw + top-K + move in one launch"
+    if cfg.page_draw:
+        return (f"{cfg.name}: {cfg.R} requests x {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, "
+                f"n={cfg.n}, K={cfg.K}, prot={cfg.prot}, paged {cfg.page_size}-token pages, "
+                f"one random draw per page and (request, layer), whole pages kept, compaction "
+                f"as page-table edits (no K/V bytes move)")
     draw = ("shared draw per layer" if cfg.shared else
             "one list per layer by the max of per-head random scores, kept count a multiple of 4"
             if cfg.shared_max else
@@ -268,7 +273,7 @@ def main():
     if names == ["all"]:
         names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
                  "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
-                 "paged_fused", "longgen_fused"]
+                 "paged_fused", "longgen_fused", "paged_pages"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None
@@ -278,7 +283,8 @@ def main():
         print(f"# timing {name}", file=sys.stderr, flush=True)
         steps = args.steps if cfg.rounds == 1 else min(args.steps, cfg.rounds)
         r = time_workload(torch, rounds, cfg, steps, args.warmup)
-        comp_ms = r["kernels_ms"]["fused" if cfg.fused else "compact"]
+        main_phase = "pages" if cfg.page_draw else "fused" if cfg.fused else "compact"
+        comp_ms = r["kernels_ms"][main_phase]
         achieved = r["kv_bytes"] / (comp_ms * 1e-3) / 1e9
         entry = {
             "workload": describe(cfg),
@@ -287,13 +293,17 @@ def main():
             "kernel_ms": {k: round(v, 4) for k, v in r["kernels_ms"].items()},
             "kv_bytes_per_round": r["kv_bytes"],
             "kv_gbps_round": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
-            "compact_gbps": achieved,
-            "compact_frac_of_peak": achieved / PEAK_HBM_GBPS,
+            "compact_gbps": achieved if not cfg.page_draw else None,
+            "compact_frac_of_peak": achieved / PEAK_HBM_GBPS if not cfg.page_draw else None,
             "applied_rounds": r["applied_rounds"],
             "bad_rows": r["errors"],
         }
         if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
+        if cfg.page_draw:
+            P, Kp = cfg.n // cfg.page_size, cfg.K // cfg.page_size
+            entry["pages_evicted_per_round"] = cfg.groups * (P - Kp)
+            entry["table_bytes_per_round"] = cfg.groups * (P * 4 * 2 + (P - Kp) * 4)
         if r["survival"] is not None:
             entry["survival"] = r["survival"]
         if name == "batch":

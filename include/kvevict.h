@@ -325,6 +325,45 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
                                            uint32_t* freed_count, uint32_t* errors,
                                            hipStream_t stream);
 
+/*
+ * Page-granular Random Attention eviction applied as page-table edits ([RA]
+ * Algorithm 1 over the blocks of a paged cache: a random score per block, the
+ * prompt pinned, the top blocks kept; [GS] Sec. 4.3: one block table per
+ * attention layer over a shared pool, freed blocks back to the pool).
+ *
+ * For the paged layout of kvevict_kv_desc (token-major pages of page_size
+ * slots holding every KV head), one list per group g = req*L + layer over its
+ * P = n / page_size pages:
+ *   score of page b   = the shared (head-0) kvevict_score_random draw of slot
+ *                       b*page_size of group g (same seed, round);
+ *   kept pages        = pages 0 .. ceil(prot/page_size)-1 (they hold the prompt)
+ *                       plus the K/page_size - ceil(prot/page_size) other pages
+ *                       with the largest scores, ties to the lower page, in
+ *                       increasing order;
+ *   page_table row g  : entry j < K/page_size becomes the old entry of the
+ *                       j-th kept page, entries K/page_size .. P-1 become -1,
+ *                       entries >= P are untouched (edited in place);
+ *   freed_pages       : the old entries of the evicted pages, in page order,
+ *                       appended at an offset taken with an atomic add on
+ *                       *freed_count (not reset by the call; groups may land in
+ *                       any order).  Room: num_groups * (P - K/page_size).
+ * Token slot t of a kept page keeps its offset t % page_size, so no K/V byte
+ * moves: reading the store through the new table equals the token gather of the
+ * kept pages' slots.
+ * page_table  device int32 [num_groups][pt_ld], pt_ld >= P.
+ * kept_pages  optional device int32 out [num_groups][kept_ld], kept_ld >= K/page_size.
+ * Requires page_size >= 1, n and K multiples of page_size, 0 <= prot <= K <= n,
+ * num_requests < 2^32, L >= 1; KVEVICT_ERR_UNSUPPORTED when
+ * (P - ceil(prot/page_size)) + 2P + K/page_size > 15360 (the group is held on chip).
+ * Calls on the same table must not overlap.
+ */
+kvevict_status kvevict_evict_pages_random(int32_t* page_table, int64_t pt_ld, int32_t page_size,
+                                         int64_t num_requests, int32_t L, int32_t n, int32_t K,
+                                         int32_t prot, uint64_t seed, uint32_t round,
+                                         int32_t* kept_pages, int64_t kept_ld,
+                                         int32_t* freed_pages, uint32_t* freed_count,
+                                         hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* kvevict_status_string(kvevict_status status);
 

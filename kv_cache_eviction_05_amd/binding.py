@@ -30,6 +30,7 @@ LAYOUT_PAGED = 1
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
+           "kvevict_evict_pages_random",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -81,6 +82,8 @@ def load():
     lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
     lib.kvevict_score_keydiff.argtypes = [_p, _i64, ctypes.POINTER(KvDesc), _p, _i64, _i32, _i32,
                                           _p]
+    lib.kvevict_evict_pages_random.argtypes = [_p, _i64, _i32, _i64, _i32, _i32, _i32, _i32, _u64,
+                                               _u32, _p, _i64, _p, _p, _p]
     lib.kvevict_evict_random_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _i64, _i32, _i32,
                                                  _i32, _i32, _u64, _u32, _i32, _p, _i64, _p, _p,
                                                  _p, _p]
@@ -89,7 +92,8 @@ def load():
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
-                 "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace"):
+                 "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
+                 "kvevict_evict_pages_random"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -334,3 +338,19 @@ def kvevict_evict_random_inplace(store: KvDesc, k, v, num_requests, L, n, K, pro
                                                _ptr(freed_pages), _ptr(freed_count), _ptr(errors),
                                                _stream(stream)),
            "kvevict_evict_random_inplace")
+
+
+def kvevict_evict_pages_random(page_table, pt_ld, page_size, num_requests, L, n, K, prot, seed,
+                               round_id, kept_pages=None, kept_ld=0, freed_pages=None,
+                               freed_count=None, stream=None):
+    groups = num_requests * L
+    P, Kp = n // page_size if page_size > 0 else 0, K // page_size if page_size > 0 else 0
+    _need(page_table, torch.int32, _rows(groups, pt_ld, P), "page_table")
+    _need(kept_pages, torch.int32, _rows(groups, kept_ld, Kp), "kept_pages")
+    _need(freed_pages, torch.int32, groups * (P - Kp), "freed_pages")
+    _need(freed_count, torch.int32, 1, "freed_count")
+    _check(load().kvevict_evict_pages_random(_ptr(page_table), pt_ld, page_size, num_requests, L,
+                                             n, K, prot, seed, round_id, _ptr(kept_pages), kept_ld,
+                                             _ptr(freed_pages), _ptr(freed_count),
+                                             _stream(stream)),
+           "kvevict_evict_pages_random")

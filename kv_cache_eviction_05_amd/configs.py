@@ -32,6 +32,10 @@ Synthetic workloads, each a single-GPU share at its real shape:
             the same two in-place rounds as one launch per round: random draw,
             pin, top-K and in-place move per (request, layer, head), with no
             score or index buffer in memory.
+  paged_pages
+            the paged round with one random draw per 16-token page (the
+            shared draw of its first slot): whole pages are kept or evicted,
+            so compaction is a page-table edit and no K/V byte moves.
 
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
@@ -61,6 +65,7 @@ class RoundConfig:
     shared_max: bool = False   # one list per (request, layer) ranked by the max over heads
     inplace: bool = False      # compact in place (front of the same rows / pages)
     fused: bool = False        # draw + select + in-place move in one launch (random, top-K)
+    page_draw: bool = False    # one draw per page; compaction as page-table edits (paged)
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -132,7 +137,8 @@ PAGED_INPLACE = replace(PAGED, name="paged_inplace", inplace=True)
 LONGGEN_INPLACE = replace(LONGGEN, name="longgen_inplace", inplace=True)
 PAGED_FUSED = replace(PAGED_INPLACE, name="paged_fused", fused=True)
 LONGGEN_FUSED = replace(LONGGEN_INPLACE, name="longgen_fused", fused=True)
+PAGED_PAGES = replace(PAGED_INPLACE, name="paged_pages", page_draw=True)
 
 ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
                            PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE,
-                           PAGED_FUSED, LONGGEN_FUSED)}
+                           PAGED_FUSED, LONGGEN_FUSED, PAGED_PAGES)}

@@ -347,6 +347,28 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
       sv.paged ? freed_pages : nullptr, freed_count, errors, stream));
 }
 
+kvevict_status kvevict_evict_pages_random(int32_t* page_table, int64_t pt_ld, int32_t page_size,
+                                         int64_t num_requests, int32_t L, int32_t n, int32_t K,
+                                         int32_t prot, uint64_t seed, uint32_t round,
+                                         int32_t* kept_pages, int64_t kept_ld,
+                                         int32_t* freed_pages, uint32_t* freed_count,
+                                         hipStream_t stream) {
+  if (num_requests < 0 || num_requests > 0xffffffffll || L < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (page_size < 1 || prot < 0 || K < prot || n < K) return KVEVICT_ERR_INVALID_ARG;
+  if (n % page_size != 0 || K % page_size != 0) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t num_groups = num_requests * L;
+  if (num_groups > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  const int32_t P = n / page_size, Kp = K / page_size, pp = (prot + page_size - 1) / page_size;
+  if (pt_ld < P) return KVEVICT_ERR_INVALID_ARG;
+  if (kept_pages && kept_ld < Kp) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!page_table || !freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
+  if (kvevict::evict_pages_lds_bytes(P, pp, Kp) > (size_t)kvevict::kMaxFusedEntries * 4)
+    return KVEVICT_ERR_UNSUPPORTED;
+  return hip_status(kvevict::launch_evict_pages(page_table, pt_ld, page_size, num_groups, L, n, K,
+                                                prot, seed, round, kept_pages, kept_ld,
+                                                freed_pages, freed_count, stream));
+}
+
 const char* kvevict_status_string(kvevict_status status) {
   switch (status) {
     case KVEVICT_OK: return "ok";

@@ -72,6 +72,14 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
                                   int64_t num_groups, int32_t ipg, int32_t* freed,
                                   uint32_t* freed_count, uint32_t* errors, hipStream_t stream);
 
+// Page-granular draw + pin + top pages, applied as page-table edits; the
+// draws, old table row and kept pages of a group live in LDS.
+size_t evict_pages_lds_bytes(int32_t P, int32_t pp, int32_t Kp);
+hipError_t launch_evict_pages(int32_t* page_table, int64_t pt_ld, int32_t page_size,
+                              int64_t num_groups, int32_t L, int32_t n, int32_t K, int32_t prot,
+                              uint64_t seed, uint32_t round, int32_t* kept_pages, int64_t kept_ld,
+                              int32_t* freed, uint32_t* freed_count, hipStream_t stream);
+
 // Random draw + pin + top-K + in-place compaction of every (group, head) in
 // one launch; (n - prot) + K keys and indices live in LDS.
 constexpr int32_t kMaxFusedEntries = 15360;

@@ -7,6 +7,7 @@ problem statement for the global budget):
     random draw:   kvevict_score_random -> kvevict_select_topk -> kvevict_compact
     weighted:      kvevict_score_weighted -> kvevict_select_global -> kvevict_compact
     fused:         kvevict_evict_random_inplace (draw, pin, top-K, in-place move)
+    page draw:     kvevict_evict_pages_random (draw per page, page-table edits)
 
 Buffers are torch tensors used only as device memory; every step of the round
 runs in the HIP library.  The repeated-round driver (persistent budget K,
@@ -59,6 +60,7 @@ class RoundState:
     v_pristine: torch.Tensor | None = None
     freed: torch.Tensor | None = None        # in place, paged: the free-page list
     freed_count: torch.Tensor | None = None
+    pt_pristine: torch.Tensor | None = None  # page draw, one round: the table before the round
 
     @property
     def idx_lists(self) -> int:
@@ -68,6 +70,8 @@ class RoundState:
         """Read + write bytes of the kept K and V rows of one round (in place: of the rows
         that move, those whose kept index differs from their slot)."""
         c = self.cfg
+        if c.page_draw:
+            return 0  # whole pages stay where they are: only table entries change
         if c.inplace:
             K = c.kept_shared if c.shared_max else c.K
             j = torch.arange(K, device=self.kept.device, dtype=self.kept.dtype)
@@ -113,6 +117,10 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
     if cfg.fused and not (cfg.inplace and cfg.scorer == "random" and cfg.select == "topk"
                           and not cfg.shared_max):
         raise ValueError("the fused round is the random draw, top-K and in-place move")
+    if cfg.page_draw and not (cfg.inplace and cfg.layout == "paged" and cfg.scorer == "random"
+                              and cfg.rounds == 1 and cfg.n % cfg.page_size == 0
+                              and cfg.K % cfg.page_size == 0):
+        raise ValueError("the page draw edits one paged round's tables in place")
     n = cfg.n
     cap_dst = n if cfg.select in ("global", "layers") else (cfg.K + cfg.r if cfg.rounds > 1 else cfg.K)
     if cfg.inplace:
@@ -121,6 +129,8 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
     lists = cfg.lists if cfg.select == "topk" else cfg.groups * cfg.H
     scores = torch.empty((lists, n), dtype=torch.float32, device=device)
     kept_cols = n if cfg.select in ("global", "layers") else cfg.K
+    if cfg.page_draw:
+        lists, kept_cols = cfg.groups, cfg.K // cfg.page_size  # kept pages per (request, layer)
     kept = torch.zeros((lists, kept_cols), dtype=torch.int32, device=device)
     st = RoundState(cfg, device, ks, vs, kd, vd, scores, kept, sd, dd,
                     torch.zeros(1, dtype=torch.int32, device=device), src_pt=spt, dst_pt=dpt, n=n)
@@ -128,11 +138,13 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
         st.head_scores = torch.empty((cfg.groups * cfg.H, n), dtype=torch.float32, device=device)
     if cfg.inplace:
         st.k_dst, st.v_dst, st.dst_desc, st.dst_pt = st.k_src, st.v_src, st.src_desc, st.src_pt
-        if cfg.rounds == 1:
+        if cfg.rounds == 1 and not cfg.page_draw:
             st.k_pristine, st.v_pristine = ks.clone(), vs.clone()
         if cfg.layout == "paged":
             st.freed = torch.empty(cfg.groups * spt.shape[1], dtype=torch.int32, device=device)
             st.freed_count = torch.zeros(1, dtype=torch.int32, device=device)
+        if cfg.page_draw:
+            st.pt_pristine = spt.clone()
     if cfg.select == "layers":
         st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
         st.layer_budget = B.kvevict_layer_power_budget(synth.layer_gates(cfg.L, synth.SEED_GATES),
@@ -215,8 +227,18 @@ def fused_round(st: RoundState, round_id: int, stream=None):
                                    st.freed_count, st.errors, stream)
 
 
+def pages_round(st: RoundState, round_id: int, stream=None):
+    """One draw per page (shared draw of its first slot), top pages, page-table edits."""
+    c = st.cfg
+    B.kvevict_evict_pages_random(st.src_pt, st.src_pt.shape[1], c.page_size, c.R, c.L, st.n, c.K,
+                                 c.prot, c.seed, round_id, st.kept, st.kept.shape[1], st.freed,
+                                 st.freed_count, stream)
+
+
 def phases(cfg: RoundConfig):
     """The launches of one round as (name, fn(st, round_id)) in order."""
+    if cfg.page_draw:
+        return [("pages", pages_round)]
     if cfg.fused:
         return [("fused", fused_round)]
     return [("score", score), ("select", lambda st, rid: select(st)),
@@ -224,7 +246,9 @@ def phases(cfg: RoundConfig):
 
 
 def run_round(st: RoundState, round_id: int = 0, stream=None):
-    if st.cfg.fused:
+    if st.cfg.page_draw:
+        pages_round(st, round_id, stream)
+    elif st.cfg.fused:
         fused_round(st, round_id, stream)
     else:
         score(st, round_id, stream)
@@ -247,8 +271,11 @@ def append_tokens(st: RoundState, round_id: int):
 
 def restore(st: RoundState):
     """In place, one round: put the cache back as it was before the round (input set-up)."""
-    st.k_src.copy_(st.k_pristine)
-    st.v_src.copy_(st.v_pristine)
+    if st.pt_pristine is not None:
+        st.src_pt.copy_(st.pt_pristine)  # the K/V bytes never change under page edits
+    else:
+        st.k_src.copy_(st.k_pristine)
+        st.v_src.copy_(st.v_pristine)
     if st.freed_count is not None:
         st.freed_count.zero_()
 

@@ -296,3 +296,45 @@ def score_keydiff(keys: np.ndarray, prot: int) -> np.ndarray:
             v = np.float32(-cos)
             out[l, i] = v if v != 0 else np.float32(0.0)  # -0 written as +0
     return out
+
+
+# ---------------------------------------------------------------------------
+# Page-granular random eviction: one draw per page, compaction as page-table
+# edits (Random Attention blog summary, Algorithm 1 applied to blocks of a
+# paged cache; GateSight Sec. 4.3: one block table per layer over a shared
+# pool, freed blocks back to the pool)
+# ---------------------------------------------------------------------------
+
+def page_keep_sets(L: int, n: int, K: int, prot: int, ps: int, seed: int, round_id: int,
+                   group_begin: int, group_end: int) -> np.ndarray:
+    """Kept pages int32 [groups][K/ps] of groups (request*L + layer) in [group_begin, group_end).
+
+    A page holds ps token slots of every KV head, so the draw is one per (request, layer, page):
+    the shared (head-0) random score of the page's first slot.  Pages holding any prompt slot
+    (the first ceil(prot/ps)) are kept; among the others the K/ps - ceil(prot/ps) with the
+    largest scores, ties to the lower page; the kept pages are listed in increasing order.
+    """
+    if n % ps or K % ps:
+        raise ValueError("n and K must be whole pages")
+    pp, Kp = -(-prot // ps), K // ps
+    if pp > Kp:
+        raise ValueError("the prompt pages do not fit the budget")
+    s = score_random(L, 1, n, prot, seed, round_id, True, group_begin, group_end)
+    page_scores = np.ascontiguousarray(s[:, ::ps])  # slot b*ps of each page b
+    page_scores[:, :pp] = np.inf                    # a page with a prompt slot is pinned whole
+    return select_topk(page_scores, Kp, pp)
+
+
+def page_table_edit(pt: np.ndarray, kept_pages: np.ndarray, P: int):
+    """(new table, freed ids per group): kept pages' physical ids move to the front in order,
+    entries Kp..P-1 become -1, and the ids of the evicted pages are freed (ascending page
+    order).  Entries at and beyond P are left as they were."""
+    new = np.array(pt, dtype=np.int32, copy=True)
+    Kp = kept_pages.shape[1]
+    freed = []
+    for g in range(pt.shape[0]):
+        new[g, :Kp] = pt[g, kept_pages[g]]
+        new[g, Kp:P] = -1
+        keep = set(int(b) for b in kept_pages[g])
+        freed.append([int(pt[g, b]) for b in range(P) if b not in keep])
+    return new, freed

@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol():
                           "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                           "kvevict_reduce_max_heads", "kvevict_score_keydiff",
                           "kvevict_compact_inplace", "kvevict_evict_random_inplace",
+                          "kvevict_evict_pages_random",
                           "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
@@ -258,3 +259,24 @@ def test_evict_random_inplace_validation():
     # candidates and kept indices must fit on chip: (n - prot) + K <= 15360
     big = B.contig_desc(D, H, 16384)
     assert call(d=big, n=9000, K=8000, prot=0, kept_ld=8000) == B.KVEVICT_ERR_UNSUPPORTED
+
+
+def test_evict_pages_random_validation():
+    def call(pt=FAKE, pt_ld=132, ps=16, R=4, L=36, n=2112, K=2048, prot=1024, kept=FAKE * 2,
+             kept_ld=128, freed=FAKE * 3, fcount=FAKE * 4):
+        return status("kvevict_evict_pages_random", pt, pt_ld, ps, R, L, n, K, prot, 0, 0, kept,
+                      kept_ld, freed, fcount, None)
+
+    assert call(n=2100) == B.KVEVICT_ERR_INVALID_ARG        # n not whole pages
+    assert call(K=2040) == B.KVEVICT_ERR_INVALID_ARG        # K not whole pages
+    assert call(prot=2049) == B.KVEVICT_ERR_INVALID_ARG     # prot > K
+    assert call(K=2128) == B.KVEVICT_ERR_INVALID_ARG        # K > n
+    assert call(pt_ld=131) == B.KVEVICT_ERR_INVALID_ARG     # table shorter than n / page_size
+    assert call(kept_ld=127) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(ps=0) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(pt=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(freed=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(L=0) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(R=-1) == B.KVEVICT_ERR_INVALID_ARG
+    # 8192 pages of one slot do not fit on chip
+    assert call(ps=1, n=8192, K=4096, prot=0, pt_ld=8192, kept_ld=4096) == B.KVEVICT_ERR_UNSUPPORTED

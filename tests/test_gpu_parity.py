@@ -652,3 +652,51 @@ def test_compact_inplace_rejects_bad_indices():
     assert int(err.item()) == 1
     gk = u16(k)
     assert np.array_equal(gk[0, :K], ks[0, 5:K + 5])
+
+
+# ---------------------------------------------------------------------------
+# page-granular eviction as page-table edits
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,L,n,K,prot,ps", [
+    (2, 3, 2112, 2048, 1024, 16),   # the paged workload's pages
+    (1, 4, 3136, 3072, 557, 16),    # the prompt ends inside a page
+    (3, 2, 160, 64, 0, 16),
+    (1, 2, 4096, 2048, 0, 1),       # one-slot pages: 4096 candidates, several radix passes
+    (2, 2, 256, 256, 16, 16),       # K == n: nothing is evicted
+    (2, 2, 256, 32, 32, 16),        # only the prompt pages stay
+])
+def test_evict_pages_random(R, L, n, K, prot, ps):
+    seed, rnd = 3, 7
+    say(f"evict_pages_random R={R} L={L} n={n} K={K} prot={prot} ps={ps}")
+    groups, P, Kp = R * L, n // ps, K // ps
+    pt_ld = P + 3
+    rng = np.random.default_rng(n + K)
+    pool = groups * P + 5
+    pt = np.full((groups, pt_ld), 99, dtype=np.int32)
+    pt[:, :P] = rng.permutation(pool)[: groups * P].reshape(groups, P)
+    want_kept = oracle.page_keep_sets(L, n, K, prot, ps, seed, rnd, 0, groups)
+    want_pt, want_freed = oracle.page_table_edit(pt, want_kept, P)
+    dpt = torch.from_numpy(pt).to(DEV)
+    kept = torch.full((groups, Kp + 2), -9, dtype=torch.int32, device=DEV)
+    freed = torch.full((groups * (P - Kp) + 1,), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_evict_pages_random(dpt, pt_ld, ps, R, L, n, K, prot, seed, rnd, kept, Kp + 2, freed,
+                                 fcount)
+    torch.cuda.synchronize()
+    got = to_np(kept)
+    assert np.array_equal(got[:, :Kp], want_kept)
+    assert np.all(got[:, Kp:] == -9)
+    assert np.array_equal(to_np(dpt), want_pt)
+    nf = int(fcount.item())
+    assert nf == groups * (P - Kp)
+    got_freed = to_np(freed)
+    assert got_freed[nf] == -5
+    # each group's evicted ids form one run, in page order; the runs may come in any order
+    runs = {tuple(f) for f in want_freed if f}
+    pos = 0
+    while pos < nf:
+        run = next(r for r in runs if tuple(got_freed[pos:pos + len(r)]) == r)
+        runs.remove(run)
+        pos += len(run)
+    assert not runs

@@ -416,3 +416,38 @@ def test_longgen_inplace_rounds_replayed_by_oracle(base):
     assert st.applied_rounds == cfg.rounds and int(st.errors.item()) == 0
     del st
     free()
+
+
+def test_paged_pages_round():
+    """Page-granular round at the paged workload's full shape (2304 groups x 132 pages): kept
+    pages and edited tables equal the oracle's on sampled groups, every group frees 4 pages,
+    the free list holds exactly the evicted ids, and reading the unchanged store through the
+    new table equals the gather of the kept pages' slots through the old one."""
+    cfg = configs.PAGED_PAGES
+    say("paged page-draw round: allocating")
+    st = rounds.make_state(cfg, DEV)
+    ps, H, D, n, K = cfg.page_size, cfg.H, cfg.D, cfg.n, cfg.K
+    P, Kp = n // ps, K // ps
+    old_pt = st.src_pt.cpu().numpy().copy()
+    rounds.run_round(st, round_id=4)
+    torch.cuda.synchronize()
+    new_pt = st.src_pt.cpu().numpy()
+    kept = st.kept.cpu().numpy()
+    assert np.all(np.diff(kept, axis=1) > 0)
+    assert np.all(kept[:, :cfg.prot // ps] == np.arange(cfg.prot // ps))
+    for g in sample_lists(cfg.groups, 16, seed=5):
+        want = oracle.page_keep_sets(cfg.L, n, K, cfg.prot, ps, cfg.seed, 4, g, g + 1)
+        assert np.array_equal(kept[g:g + 1], want), g
+        want_pt, _ = oracle.page_table_edit(old_pt[g:g + 1], want, P)
+        assert np.array_equal(new_pt[g:g + 1], want_pt), g
+        # the store through the new table = the kept pages' slots through the old table
+        k_new = u16(st.k_src[torch.from_numpy(new_pt[g, :Kp].astype(np.int64)).to(DEV)])
+        k_old = u16(st.k_src[torch.from_numpy(old_pt[g, kept[g]].astype(np.int64)).to(DEV)])
+        assert np.array_equal(k_new, k_old), g
+    nf = int(st.freed_count.item())
+    assert nf == cfg.groups * (P - Kp)
+    evicted = [old_pt[g, b] for g in range(cfg.groups) for b in sorted(set(range(P)) - set(kept[g]))]
+    assert sorted(st.freed[:nf].cpu().tolist()) == sorted(int(x) for x in evicted)
+    assert st.kv_bytes_moved() == 0
+    del st
+    free()
