@@ -300,6 +300,8 @@ def main():
         }
         if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
+        if cfg.select == "layers":
+            entry["vs_global_top_b"] = rounds.compare_with_global(r["state"])
         if cfg.page_draw:
             P, Kp = cfg.n // cfg.page_size, cfg.K // cfg.page_size
             entry["pages_evicted_per_round"] = cfg.groups * (P - Kp)

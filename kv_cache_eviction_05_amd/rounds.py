@@ -290,6 +290,38 @@ def swap(st: RoundState):
     st.src_desc, st.dst_desc = st.dst_desc, st.src_desc
 
 
+# --- measurement: per-layer budgets against the model-wide top-B ---------------------
+
+def compare_with_global(st: RoundState) -> dict:
+    """Measurement only, outside the timed round: the model-wide top-B (global select) on the
+    same scores at the same total, against the per-layer allocation the round just kept.
+    Reports both totals, the non-prompt entries each rule keeps per layer, and the fraction of
+    kept non-prompt entries the two rules share."""
+    c = st.cfg
+    lists, n = st.scores.shape
+    kept_g = torch.zeros_like(st.kept)
+    cnt_g = torch.zeros_like(st.kept_count)
+    ws_bytes = B.kvevict_select_global_workspace(lists, n, c.prot, p=c.p)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=st.device)
+    total_g = B.kvevict_select_global(kept_g, kept_g.shape[1], cnt_g, st.scores, n, lists, n,
+                                      c.prot, c.p, ws, ws_bytes)
+
+    def kept_mask(kept, cnt):
+        m = torch.zeros((lists, n), dtype=torch.bool, device=st.device)
+        valid = torch.arange(kept.shape[1], device=st.device)[None, :] < cnt[:, None]
+        rows = torch.arange(lists, device=st.device)[:, None].expand_as(kept)
+        m[rows[valid], kept[valid].long()] = True
+        return m[:, c.prot:]
+
+    ml, mg = kept_mask(st.kept, st.kept_count), kept_mask(kept_g, cnt_g)
+    total_l = int(ml.sum().item())
+    per_l = (st.kept_count - c.prot).view(c.R, c.L, c.H).sum(dim=(0, 2))
+    per_g = (cnt_g - c.prot).view(c.R, c.L, c.H).sum(dim=(0, 2))
+    return {"total_kept_layers": total_l, "total_kept_global": int(total_g),
+            "kept_overlap": int((ml & mg).sum().item()) / max(total_l, 1),
+            "per_layer_kept_layers": per_l.tolist(), "per_layer_kept_global": per_g.tolist()}
+
+
 # --- measurement: survival of entries across repeated rounds ------------------------
 
 class SurvivalTracker:

@@ -321,9 +321,24 @@ def test_layers_round():
     rounds.select(st)
     torch.cuda.synchronize()
     got = st.kept.cpu().numpy()
+    want_l = np.zeros((lists, cfg.n), bool)
     for lst in range(lists):
         K = cfg.prot + want_b[lst // cfg.H]
-        assert np.array_equal(got[lst, :K], oracle.select_topk(s[lst:lst + 1], K, cfg.prot)[0]), lst
+        want_k = oracle.select_topk(s[lst:lst + 1], K, cfg.prot)[0]
+        assert np.array_equal(got[lst, :K], want_k), lst
+        want_l[lst, want_k] = True
+    say("layers round: against the global top-B at the same total")
+    cmp = rounds.compare_with_global(st)
+    kg, cg, total_g = oracle.select_global(s, cfg.prot, cfg.p)
+    want_g = np.zeros((lists, cfg.n), bool)
+    for lst in range(lists):
+        want_g[lst, kg[lst, :cg[lst]]] = True
+    body = slice(cfg.prot, cfg.n)
+    assert cmp["total_kept_global"] == total_g == cmp["total_kept_layers"] == sum(want_b) * cfg.H
+    assert cmp["per_layer_kept_layers"] == [b * cfg.H for b in want_b]
+    assert cmp["per_layer_kept_global"] == list((cg - cfg.prot).reshape(cfg.L, cfg.H).sum(1))
+    inter = int((want_l[:, body] & want_g[:, body]).sum())
+    assert cmp["kept_overlap"] == inter / cmp["total_kept_layers"]
     del st
     free()
 
