@@ -143,7 +143,7 @@ kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* be
  * cos = 0; a zero score is written as +0.  A paged row whose page id falls
  * outside the pool reads as zeros.
  * Requires D = head_dim in {8, 16, 32, ..., 512}, 0 <= prot <= n <= rows of a
- * list, ld >= n.  KVEVICT_ERR_UNSUPPORTED for other D.
+ * list, n * D / 8 < 2^31, ld >= n.  KVEVICT_ERR_UNSUPPORTED for other D.
  */
 kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv_desc* keys,
                                      const void* k_cache, int64_t num_groups, int32_t n,

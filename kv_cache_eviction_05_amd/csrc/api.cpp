@@ -126,6 +126,7 @@ kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv
   const int32_t vpr = D / 8;
   if (vpr > 64 || (vpr & (vpr - 1)) != 0) return KVEVICT_ERR_UNSUPPORTED;  // D in {8, 16, ..., 512}
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if ((int64_t)n * vpr > kInt32Max) return KVEVICT_ERR_INVALID_ARG;  // 32-bit row offsets
   const int64_t lists = num_groups * H;
   if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
   if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;

@@ -5,14 +5,19 @@
 //   score[list][i] = -cos(k_i, mean_j k_j)   (mean over all n keys of the list),
 //   +inf for i < prot; a zero norm gives cos = 0; zero is written as +0.
 //
-// One workgroup of 256 threads per list, two passes over the list's keys.
-// A row of D bf16 is VPR = D/8 16-byte vectors; thread t owns vector column
-// t % VPR of rows t / VPR + k * (256 / VPR).  Pass 1 accumulates the column
-// sums in binary64 (exact for bf16 inputs of moderate range, and in a fixed
-// order), reduces them through LDS into the mean and its squared norm.  Pass 2
-// re-reads the keys (largely from the caches), forms each row's dot product
-// with the mean and its squared norm in binary64, adds the VPR partials of a
-// row with lane shuffles, and rounds -dot/(|k||mean|) once to fp32.
+// The mean needs every key before any cosine, and a list (1088 keys of 256 B
+// at D = 128: 278 KB) is larger than a CU's share of L2 and of the Infinity
+// Cache, so a second pass over the keys would go back to HBM.  One workgroup
+// of 1024 threads per list therefore keeps the list's first rows on chip: a
+// row of D bf16 is VPR = D/8 16-byte vectors, thread t owns vector column
+// t % VPR of rows t / VPR + k * (1024 / VPR); its first 8 such rows stay in
+// registers and the next 7 or 8 in LDS (128 KB of the CU's 160 KB), so 1024
+// rows at D = 128 are read once and only rows beyond them are read twice.
+// Pass 1 accumulates the column sums in binary64 in a fixed order (lanes of a
+// column with shuffles, then the 16 waves in a tree through LDS) into the mean
+// and its squared norm.  Pass 2 forms each row's dot product with the mean and
+// its squared norm in binary64, adds the VPR partials of a row with DPP lane
+// moves, and rounds -dot * rsqrt(|k|^2) / |mean| once to fp32.
 #include <cmath>
 
 #include "kvevict_device.hpp"
@@ -21,8 +26,14 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kReg = 8;     // rows per thread held in registers
+constexpr int kUnroll = 2;  // rows per thread in flight for the streamed tail
+
+// rows per thread held in LDS: 16 KB each, next to 8*D + D doubles of sums
+template <int VPR>
+constexpr int lds_rows() { return VPR >= 64 ? 7 : 8; }
 
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
@@ -36,9 +47,10 @@ struct KeydiffArgs {
 
 // Vector offset of row t < n of list (g, h), or -1 if its page id falls
 // outside the pool (such a row reads as zeros).
+template <bool kPaged>
 __device__ __forceinline__ int64_t key_row(const KeydiffArgs& a, int64_t list, int32_t t,
                                            int32_t vpr) {
-  if (!a.keys.paged) return list * a.keys.list_stride_v + (int64_t)t * vpr;
+  if (!kPaged) return list * a.keys.list_stride_v + (int64_t)t * vpr;
   const int64_t g = list / a.H;
   const int32_t h = (int32_t)(list - g * a.H);
   const int32_t page = a.keys.page_table[g * a.keys.pt_ld + (t >> a.keys.page_shift)];
@@ -47,10 +59,23 @@ __device__ __forceinline__ int64_t key_row(const KeydiffArgs& a, int64_t list, i
   return (slot * a.H + h) * vpr;
 }
 
+template <bool kPaged>
 __device__ __forceinline__ vec4u load_key(const KeydiffArgs& a, int64_t list, int32_t t,
                                           int32_t vpr, int32_t col) {
-  const int64_t off = key_row(a, list, t, vpr);
+  const int64_t off = key_row<kPaged>(a, list, t, vpr);
   return off >= 0 ? a.k[off + col] : vec4u{0u, 0u, 0u, 0u};
+}
+
+// Vector `col` of row t of a list, or zeros for t >= n; contiguous rows are
+// addressed from the list's (uniform) base with a 32-bit offset and read
+// without a branch (a row past n reads row n - 1, n >= 1, then is zeroed).
+template <int VPR, bool kPaged>
+__device__ __forceinline__ vec4u load_row(const KeydiffArgs& a, const vec4u* __restrict__ lb,
+                                          int64_t list, int32_t t, int32_t n, int32_t col) {
+  if (kPaged) return (t < n) ? load_key<true>(a, list, t, VPR, col) : vec4u{0u, 0u, 0u, 0u};
+  const int32_t tt = t < n ? t : n - 1;
+  const vec4u v = lb[tt * VPR + col];
+  return t < n ? v : vec4u{0u, 0u, 0u, 0u};
 }
 
 // The eight bf16 of a 16-byte vector as binary64 (exact).
@@ -62,17 +87,70 @@ __device__ __forceinline__ void unpack8(vec4u v, double* x) {
   }
 }
 
-template <int VPR>
+// Sum of a binary64 value over aligned groups of W consecutive lanes (W a power
+// of two <= 64), every lane of a group receiving the sum: DPP moves within the
+// 16-lane rows (pair swap, quad swap, half-row mirror, row mirror), lane
+// shuffles across rows.
+template <int W>
+__device__ __forceinline__ double group_sum(double v) {
+  auto dpp = [](double x, int ctrl) -> double {
+    const uint64_t b = __double_as_longlong(x);
+    const int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+    int rlo, rhi;
+    switch (ctrl) {  // the DPP control must be a constant
+      case 0: rlo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
+              rhi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
+      case 1: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
+              rhi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
+      case 2: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
+              rhi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
+      default: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
+               rhi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+    }
+    return __longlong_as_double((int64_t)(((uint64_t)(uint32_t)rhi << 32) | (uint32_t)rlo));
+  };
+  if (W >= 2) v += dpp(v, 0);   // lanes 2i <-> 2i+1
+  if (W >= 4) v += dpp(v, 1);   // lanes i <-> i^2 within a quad
+  if (W >= 8) v += dpp(v, 2);   // lane i <-> 7-i within 8 lanes: quad 0 <-> quad 1
+  if (W >= 16) v += dpp(v, 3);  // lane i <-> 15-i within 16 lanes: half 0 <-> half 1
+  if (W >= 32) v += __shfl_xor(v, 16, kWave);
+  if (W >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// 1 / sqrt(x) for x > 0: the hardware estimate and one Newton step (relative
+// error far below the fp32 rounding of the score).
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  const double y = __builtin_amdgcn_rsq(x);
+  return y * fma(-0.5 * x * y, y, 1.5);
+}
+
+// Partial dot with the mean and squared norm of one 16-byte vector.
+__device__ __forceinline__ void dot_norm(vec4u v, const double* mu, double& dot, double& kk) {
+  double x[8];
+  unpack8(v, x);
+  dot = 0.0;
+  kk = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    dot = fma(x[e], mu[e], dot);
+    kk = fma(x[e], x[e], kk);
+  }
+}
+
+template <int VPR, bool kPaged>
 __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) {
-  __shared__ double s_part[kThreads * 8];  // pass-1 partial column sums
-  __shared__ double s_mean[kThreads * 8];  // the mean key, D <= 2048 entries
-  __shared__ double s_red[kThreads / kWave];
-  const int32_t vpr = VPR ? VPR : a.vpr;
-  const int32_t D = vpr * 8;
-  const int32_t rpi = kThreads / vpr;  // rows per iteration
+  constexpr int32_t rpi = kThreads / VPR;  // rows per iteration
+  constexpr int32_t D = VPR * 8;
+  constexpr int kLds = lds_rows<VPR>();
+  constexpr int32_t kCap = (kReg + kLds) * rpi;  // rows held on chip
+  __shared__ vec4u s_keys[kLds][kThreads];
+  __shared__ double s_part[kWaves / 2][D];   // column sums of the upper half of the waves
+  __shared__ double s_mean[D];
+  __shared__ double s_mm;
   const int tid = threadIdx.x;
-  const bool active = tid < rpi * vpr;
-  const int32_t col = tid % vpr, r0 = tid / vpr;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int32_t col = tid % VPR, r0 = tid / VPR;
   const int64_t list = blockIdx.x;
   const int32_t n = a.n;
   float* out = a.scores + list * a.ld;
@@ -80,84 +158,141 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
     for (int32_t i = tid; i < n; i += kThreads) out[i] = INFINITY;
     return;
   }
+  const vec4u* __restrict__ lb = kPaged ? a.k : a.k + list * a.keys.list_stride_v;
 
-  // --- pass 1: column sums ---------------------------------------------------
+  // --- load the rows held on chip; pass 1: column sums ---------------------------
+  vec4u reg[kReg];
+#pragma unroll
+  for (int k = 0; k < kReg; ++k) {
+    const int32_t t = r0 + k * rpi;
+    reg[k] = load_row<VPR, kPaged>(a, lb, list, t, n, col);
+  }
   double sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.0;
-  if (active) {
-    for (int32_t base = r0; base < n; base += rpi * kUnroll) {
-      vec4u v[kUnroll];
+  auto add = [&](vec4u v) {
+    double x[8];
+    unpack8(v, x);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int32_t t = base + u * rpi;
-        v[u] = (t < n) ? load_key(a, list, t, vpr, col) : vec4u{0u, 0u, 0u, 0u};
-      }
+    for (int e = 0; e < 8; ++e) sum[e] += x[e];
+  };
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        double x[8];
-        unpack8(v[u], x);
+  for (int k0 = 0; k0 < kLds; k0 += 4) {  // staged into LDS four rows at a time
+    vec4u stage[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum[e] += x[e];
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int32_t t = r0 + (kReg + k0 + k) * rpi;
+      stage[k] = (k0 + k < kLds) ? load_row<VPR, kPaged>(a, lb, list, t, n, col)
+                                 : vec4u{0u, 0u, 0u, 0u};
+    }
+    if (k0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kReg; ++k) add(reg[k]);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_part[r0 * D + col * 8 + e] = sum[e];
+    for (int k = 0; k < 4; ++k) {
+      if (k0 + k < kLds) {
+        s_keys[k0 + k][tid] = stage[k];  // read back by this thread only
+        add(stage[k]);
+      }
+    }
   }
-  __syncthreads();
-  double mm_part = 0.0;
-  for (int32_t d = tid; d < D; d += kThreads) {
-    double s = 0.0;
-    for (int32_t r = 0; r < rpi; ++r) s += s_part[r * D + d];  // fixed order
-    const double mean = s / (double)n;
-    s_mean[d] = mean;
-    mm_part += mean * mean;
-  }
-  // |mean|^2: wave sums, then the waves in order
-  for (int off = kWave / 2; off > 0; off >>= 1) mm_part += __shfl_xor(mm_part, off, kWave);
-  if (lane_id() == 0) s_red[tid / kWave] = mm_part;
-  __syncthreads();
-  double mm = 0.0;
+  for (int32_t base = kCap + r0; base < n; base += rpi * kUnroll) {  // streamed tail
+    vec4u v[kUnroll];
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) mm += s_red[w];
-  const double mnorm = sqrt(mm);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t t = base + u * rpi;
+      v[u] = load_row<VPR, kPaged>(a, lb, list, t, n, col);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) add(v[u]);
+  }
+  // the lanes of one column in a wave (col, col + VPR, ...), then the waves in a tree
+#pragma unroll
+  for (int off = VPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] += __shfl_xor(sum[e], off, kWave);
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half && lane < VPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_part[wave - half][col * 8 + e] = sum[e];
+    }
+    __syncthreads();
+    if (wave < half && lane < VPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] += s_part[wave][col * 8 + e];
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    double mm_part = 0.0;
+    if (lane < VPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double mean = sum[e] / (double)n;
+        s_mean[col * 8 + e] = mean;
+        mm_part += mean * mean;
+      }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) mm_part += __shfl_xor(mm_part, off, kWave);
+    if (lane == 0) s_mm = mm_part;
+  }
+  __syncthreads();
+  const double mm = s_mm;
+  const double inv_mnorm = mm > 0.0 ? 1.0 / sqrt(mm) : 0.0;
+  // Hide the held rows' values from the compiler between the passes, so it
+  // converts them again rather than keeping 64 binary64 values of pass 1 live
+  // (which would spill).
+#pragma unroll
+  for (int k = 0; k < kReg; ++k)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(reg[k][q]));
   double mu[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mu[e] = active ? s_mean[col * 8 + e] : 0.0;
+  for (int e = 0; e < 8; ++e) mu[e] = s_mean[col * 8 + e];
 
-  // --- pass 2: per-row dot with the mean and squared norm ----------------------
-  for (int32_t b0 = 0; b0 < n; b0 += rpi * kUnroll) {
+  // --- pass 2: per-row dot with the mean and squared norm ------------------------
+  auto finish = [&](int32_t t, double dot, double kk) {
+    // add the VPR partials of the row (consecutive lanes, VPR a power of two <= 64)
+    dot = group_sum<VPR>(dot);
+    kk = group_sum<VPR>(kk);
+    if (col == 0 && t < n) {
+      float sc = INFINITY;
+      if (t >= a.prot) {
+        sc = (kk > 0.0 && mm > 0.0) ? (float)(-(dot * rsqrt_nr(kk)) * inv_mnorm) : 0.0f;
+        if (sc == 0.0f) sc = 0.0f;  // -0 written as +0
+      }
+      out[t] = sc;
+    }
+  };
+  // one row at a time: interleaving the rows' binary64 temporaries would spill
+#pragma unroll
+  for (int k = 0; k < kReg; ++k) {
+    double dot, kk;
+    dot_norm(reg[k], mu, dot, kk);
+    finish(r0 + k * rpi, dot, kk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int k = 0; k < kLds; ++k) {
+    double dot, kk;
+    dot_norm(s_keys[k][tid], mu, dot, kk);
+    finish(r0 + (kReg + k) * rpi, dot, kk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int32_t b0 = kCap; b0 < n; b0 += rpi * kUnroll) {  // the streamed tail again
     vec4u v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int32_t t = b0 + r0 + u * rpi;
-      v[u] = (active && t < n) ? load_key(a, list, t, vpr, col) : vec4u{0u, 0u, 0u, 0u};
+      v[u] = load_row<VPR, kPaged>(a, lb, list, t, n, col);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      double x[8];
-      unpack8(v[u], x);
-      double dot = 0.0, kk = 0.0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dot = fma(x[e], mu[e], dot);
-        kk = fma(x[e], x[e], kk);
-      }
-      // add the VPR partials of the row (consecutive lanes, VPR a power of two <= 64)
-      for (int off = vpr / 2; off > 0; off >>= 1) {
-        dot += __shfl_xor(dot, off, kWave);
-        kk += __shfl_xor(kk, off, kWave);
-      }
-      const int32_t t = b0 + r0 + u * rpi;
-      if (active && col == 0 && t < n) {
-        float sc = INFINITY;
-        if (t >= a.prot) {
-          const double den = sqrt(kk) * mnorm;
-          sc = (den > 0.0) ? (float)(-(dot / den)) : 0.0f;
-          if (sc == 0.0f) sc = 0.0f;  // -0 written as +0
-        }
-        out[t] = sc;
-      }
+      double dot, kk;
+      dot_norm(v[u], mu, dot, kk);
+      finish(b0 + r0 + u * rpi, dot, kk);
     }
   }
 }
@@ -178,17 +313,25 @@ hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys
   a.prot = prot;
   a.vpr = D / 8;
   const dim3 grid((unsigned)num_lists), block(kThreads);
+#define KVEVICT_KEYDIFF_CASE(V)                                                       \
+  case V:                                                                             \
+    if (keys.paged)                                                                   \
+      hipLaunchKernelGGL((score_keydiff_kernel<V, true>), grid, block, 0, stream, a);  \
+    else                                                                              \
+      hipLaunchKernelGGL((score_keydiff_kernel<V, false>), grid, block, 0, stream, a); \
+    break;
   switch (a.vpr) {
-    case 16:
-      hipLaunchKernelGGL(score_keydiff_kernel<16>, grid, block, 0, stream, a);
-      break;
-    case 32:
-      hipLaunchKernelGGL(score_keydiff_kernel<32>, grid, block, 0, stream, a);
-      break;
+    KVEVICT_KEYDIFF_CASE(1)
+    KVEVICT_KEYDIFF_CASE(2)
+    KVEVICT_KEYDIFF_CASE(4)
+    KVEVICT_KEYDIFF_CASE(8)
+    KVEVICT_KEYDIFF_CASE(16)
+    KVEVICT_KEYDIFF_CASE(32)
+    KVEVICT_KEYDIFF_CASE(64)
     default:
-      hipLaunchKernelGGL(score_keydiff_kernel<0>, grid, block, 0, stream, a);
-      break;
+      return hipErrorInvalidValue;  // D/8 must be a power of two <= 64
   }
+#undef KVEVICT_KEYDIFF_CASE
   return hipGetLastError();
 }
 

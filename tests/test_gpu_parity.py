@@ -465,6 +465,10 @@ def assert_keydiff_close(got, want):
     (2, 3, 777, 256, 5, 800),       # ragged, padded rows, D = 256
     (2, 2, 70, 64, 70, 70),         # every slot protected
     (1, 2, 1, 128, 0, 4),           # one key per list
+    (1, 2, 600, 512, 10, 600),      # D = 512: 240 rows on chip, the rest streamed twice
+    (2, 2, 3000, 8, 3, 3000),       # D = 8: every row on chip
+    (1, 3, 5000, 128, 0, 5000),     # a long streamed tail
+    (2, 2, 300, 32, 17, 310),
 ])
 def test_score_keydiff_contig(groups, H, n, D, prot, cap):
     say(f"score_keydiff contig groups={groups} H={H} n={n} D={D} prot={prot}")
