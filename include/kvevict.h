@@ -163,6 +163,21 @@ kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const flo
                                    int32_t prot, hipStream_t stream);
 
 /*
+ * Random scores and per-list top-K in one launch ([RA] Algorithm 1: a random
+ * score per entry, the prompt pinned, top-K per KV head, the keep set
+ * returned).  kept_idx equals what kvevict_score_random (same seed, round, L,
+ * H and draw mode) followed by kvevict_select_topk (K, prot) produce, but the
+ * scores are drawn on chip and never stored.
+ * kept_idx  device int32 out [lists][kept_ld], kept_ld >= K; lists and their
+ *           numbering as in kvevict_score_random.
+ * Requires 0 <= prot <= K <= n, num_requests < 2^32, L >= 1, H >= 1.
+ */
+kvevict_status kvevict_select_random(int32_t* kept_idx, int64_t kept_ld, int64_t num_requests,
+                                     int32_t L, int32_t H, int32_t n, int32_t K, int32_t prot,
+                                     uint64_t seed, uint32_t round, int32_t shared_draw,
+                                     hipStream_t stream);
+
+/*
  * Pin + per-layer top-K_l (GateSight Sec. 4.2 and Appendix G: every KV head of
  * attention layer l keeps the protected prefix plus K_l entries, so a layer's
  * kept cache is a dense prefix of K_l + prot rows per head).

@@ -30,7 +30,7 @@ LAYOUT_PAGED = 1
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
-           "kvevict_evict_pages_random",
+           "kvevict_evict_pages_random", "kvevict_select_random",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -82,6 +82,8 @@ def load():
     lib.kvevict_reduce_max_heads.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _p]
     lib.kvevict_score_keydiff.argtypes = [_p, _i64, ctypes.POINTER(KvDesc), _p, _i64, _i32, _i32,
                                           _p]
+    lib.kvevict_select_random.argtypes = [_p, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _u64, _u32,
+                                          _i32, _p]
     lib.kvevict_evict_pages_random.argtypes = [_p, _i64, _i32, _i64, _i32, _i32, _i32, _i32, _u64,
                                                _u32, _p, _i64, _p, _p, _p]
     lib.kvevict_evict_random_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _i64, _i32, _i32,
@@ -93,7 +95,7 @@ def load():
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
                  "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
-                 "kvevict_evict_pages_random"):
+                 "kvevict_evict_pages_random", "kvevict_select_random"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -354,3 +356,12 @@ def kvevict_evict_pages_random(page_table, pt_ld, page_size, num_requests, L, n,
                                              _ptr(freed_pages), _ptr(freed_count),
                                              _stream(stream)),
            "kvevict_evict_pages_random")
+
+
+def kvevict_select_random(kept_idx, kept_ld, num_requests, L, H, n, K, prot, seed, round_id,
+                          shared_draw, stream=None):
+    lists = num_requests * L * (1 if shared_draw else H)
+    _need(kept_idx, torch.int32, _rows(lists, kept_ld, K), "kept_idx")
+    _check(load().kvevict_select_random(_ptr(kept_idx), kept_ld, num_requests, L, H, n, K, prot,
+                                        seed, round_id, 1 if shared_draw else 0, _stream(stream)),
+           "kvevict_select_random")

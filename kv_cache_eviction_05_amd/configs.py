@@ -37,6 +37,10 @@ Synthetic workloads, each a single-GPU share at its real shape:
             shared draw of its first slot): whole pages are kept or evicted,
             so compaction is a page-table edit and no K/V byte moves.
 
+The random top-K rounds compacted out of place draw their scores inside the
+select (kvevict_select_random: one launch, no score buffer) unless fuse_draw
+is off; the standalone scorer stays available and tested.
+
 Budget and trigger follow the Random Attention blog summary (persistent budget
 K, recent buffer r=64, evict when the buffer is full) and the GateSight
 problem statement (B = L*H*round(p*(n-prot)), prot <= 256).
@@ -66,6 +70,7 @@ class RoundConfig:
     inplace: bool = False      # compact in place (front of the same rows / pages)
     fused: bool = False        # draw + select + in-place move in one launch (random, top-K)
     page_draw: bool = False    # one draw per page; compaction as page-table edits (paged)
+    fuse_draw: bool = True     # random top-K out of place: draw the scores inside the select
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -73,6 +78,12 @@ class RoundConfig:
     Hg: int = 48               # GDN heads per layer
     win_width: int = 6         # GDN layers read by one attention layer
     n_override: int = 0        # n when it is not K + r (global mode)
+
+    @property
+    def fused_select(self) -> bool:
+        """Random draw and top-K in one launch (out-of-place random top-K rounds)."""
+        return (self.fuse_draw and self.scorer == "random" and self.select == "topk"
+                and not self.shared_max and not self.inplace)
 
     @property
     def n(self) -> int:

@@ -348,6 +348,19 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
       sv.paged ? freed_pages : nullptr, freed_count, errors, stream));
 }
 
+kvevict_status kvevict_select_random(int32_t* kept_idx, int64_t kept_ld, int64_t num_requests,
+                                     int32_t L, int32_t H, int32_t n, int32_t K, int32_t prot,
+                                     uint64_t seed, uint32_t round, int32_t shared_draw,
+                                     hipStream_t stream) {
+  if (num_requests < 0 || num_requests > 0xffffffffll || L < 1 || H < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (prot < 0 || K < prot || n < K || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_requests * L * (shared_draw ? 1 : H);
+  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (lists > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_draw_select(kept_idx, kept_ld, lists, L, H, n, K, prot, seed,
+                                                round, shared_draw != 0, stream));
+}
+
 kvevict_status kvevict_evict_pages_random(int32_t* page_table, int64_t pt_ld, int32_t page_size,
                                          int64_t num_requests, int32_t L, int32_t n, int32_t K,
                                          int32_t prot, uint64_t seed, uint32_t round,

@@ -72,6 +72,11 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
                                   int64_t num_groups, int32_t ipg, int32_t* freed,
                                   uint32_t* freed_count, uint32_t* errors, hipStream_t stream);
 
+// Random draw + pin + top-K per list, the keys drawn in LDS (no score buffer).
+hipError_t launch_draw_select(int32_t* kept_idx, int64_t kept_ld, int64_t num_lists, int32_t L,
+                              int32_t H, int32_t n, int32_t K, int32_t prot, uint64_t seed,
+                              uint32_t round, bool shared_draw, hipStream_t stream);
+
 // Page-granular draw + pin + top pages, applied as page-table edits; the
 // draws, old table row and kept pages of a group live in LDS.
 size_t evict_pages_lds_bytes(int32_t P, int32_t pp, int32_t Kp);

@@ -21,6 +21,10 @@
 // partial sums are added through LDS in a fixed order and the fp32 score is
 // stored.  The LDS tiles are double-buffered, so each step needs one barrier.
 //
+// Each thread's offsets within a full tile are computed once; a step adds only
+// the GDN layer and pass offsets.  The log table holds {ln c, 1/c} pairs, so a
+// log makes one 16-byte LDS read.
+//
 // Precision: the product beta*|v| of two floats is exact in binary64; its
 // natural log is taken in binary64 (table-driven reduction to [-2^-8, 2^-8]
 // and a degree-7 series, within a few binary64 ulps; zero, infinities, NaN
@@ -71,15 +75,15 @@ struct WeightedArgs {
 // ln(1 + r) = r - r^2/2 + ... + r^7/7.  Only the high word of x carries e and
 // i, so m and c are built from it.  *special is set when x is not a positive
 // normal number (zero, subnormal, infinite, NaN or negative).
-__device__ __forceinline__ double ln_fast(double x, const double* lnc, const double* inv,
-                                          bool* special) {
+__device__ __forceinline__ double ln_fast(double x, const double2* tab, bool* special) {
   const uint32_t hi = (uint32_t)__double2hiint(x);
   const uint32_t ex = hi >> 20;  // sign and biased exponent
   *special = ex - 1u >= 0x7feu;
   const uint32_t i = (hi >> 13) & (kLnTable - 1);
   const double m = __hiloint2double((int)((hi & 0x000fffffu) | 0x3ff00000u), __double2loint(x));
   const double c = __hiloint2double((int)((hi & 0x000fe000u) | 0x3ff01000u), 0);
-  const double r = (m - c) * inv[i];
+  const double2 tc = tab[i];  // {ln c, 1/c}
+  const double r = (m - c) * tc.y;
   double p = 1.0 / 7.0;
   p = fma(p, r, -1.0 / 6.0);
   p = fma(p, r, 1.0 / 5.0);
@@ -87,7 +91,7 @@ __device__ __forceinline__ double ln_fast(double x, const double* lnc, const dou
   p = fma(p, r, 1.0 / 3.0);
   p = fma(p, r, -0.5);
   p = fma(p, r, 1.0);
-  return fma((double)((int32_t)ex - 1023), M_LN2, fma(p, r, lnc[i]));
+  return fma((double)((int32_t)ex - 1023), M_LN2, fma(p, r, tc.x));
 }
 
 // The library log, out of line, for the arguments ln_fast does not take.
@@ -120,20 +124,27 @@ template <int VW, bool kFull>
 __device__ __forceinline__ void load_tile(const WeightedArgs& a, const float* __restrict__ beta,
                                           const float* __restrict__ vnorm,
                                           const float* __restrict__ wts, int32_t g, int32_t p,
-                                          int32_t t0, Tile<VW>& r) {
+                                          int32_t t0, Tile<VW>& r, const int64_t* off) {
   const int32_t j0 = p * kJPass;
   const int32_t jn = kFull ? kJPass : min(kJPass, a.Hg - j0);
+  const int64_t base = (int64_t)g * a.sg + (int64_t)j0 * a.sj;
 #pragma unroll
   for (int k = 0; k < Tile<VW>::kVecs; ++k) {
-    int32_t tok, j;
-    tile_pos<VW, kFull>(k, jn, &tok, &j);
 #pragma unroll
     for (int c = 0; c < VW; ++c) {
       r.b[k][c] = 1.0f;
       r.v[k][c] = 1.0f;
     }
-    if ((!kFull && tok >= kTok) || t0 + tok >= a.n) continue;
-    const int64_t e = (int64_t)g * a.sg + (int64_t)(t0 + tok) * a.st + (int64_t)(j0 + j) * a.sj;
+    int64_t e;
+    if (kFull) {
+      if (off[k] < 0) continue;
+      e = base + off[k];
+    } else {
+      int32_t tok, j;
+      tile_pos<VW, kFull>(k, jn, &tok, &j);
+      if (tok >= kTok || t0 + tok >= a.n) continue;
+      e = base + (int64_t)(t0 + tok) * a.st + (int64_t)j * a.sj;
+    }
     if (VW == 2) {
       const float2 x = *reinterpret_cast<const float2*>(beta + e);
       const float2 y = *reinterpret_cast<const float2*>(vnorm + e);
@@ -161,7 +172,7 @@ __device__ __forceinline__ void load_tile(const WeightedArgs& a, const float* __
 // binary64, into w.
 template <int VW, bool kFull>
 __device__ __forceinline__ void stage_tile(const Tile<VW>& r, int32_t jn, double* x, double* w,
-                                           const double* lnc, const double* inv) {
+                                           const double2* tab) {
   double y[Tile<VW>::kVecs][VW];
   bool any_special = false;
 #pragma unroll
@@ -169,7 +180,7 @@ __device__ __forceinline__ void stage_tile(const Tile<VW>& r, int32_t jn, double
 #pragma unroll
     for (int c = 0; c < VW; ++c) {
       bool sp;
-      y[k][c] = ln_fast((double)r.b[k][c] * (double)r.v[k][c], lnc, inv, &sp);
+      y[k][c] = ln_fast((double)r.b[k][c] * (double)r.v[k][c], tab, &sp);
       any_special |= sp;
     }
   if (any_special) {  // zero, infinite, NaN or negative signals: the library log
@@ -201,8 +212,7 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
                                                                   const float* __restrict__ beta,
                                                                   const float* __restrict__ vnorm,
                                                                   float* __restrict__ scores) {
-  __shared__ double s_lnc[kLnTable];
-  __shared__ double s_inv[kLnTable];
+  __shared__ double2 s_tab[kLnTable];
   __shared__ double s_x[2][kJPass * kXStride];
   __shared__ double s_w[2][kWRow];
   __shared__ double s_red[kWaves][kHB][kTok];
@@ -228,8 +238,7 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
 
   if (tid < kLnTable) {
     const double c = 1.0 + ((double)tid + 0.5) * (1.0 / kLnTable);
-    s_lnc[tid] = log(c);
-    s_inv[tid] = 1.0 / c;
+    s_tab[tid] = make_double2(log(c), 1.0 / c);
   }
 
   const int32_t passes = (a.Hg + kJPass - 1) / kJPass;
@@ -241,11 +250,19 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) acc[hh][s] = 0.0;
 
+  // offsets of this thread's vectors within a full tile (-1 past the last token)
+  int64_t off[Tile<VW>::kVecs];
+#pragma unroll
+  for (int k = 0; k < Tile<VW>::kVecs; ++k) {
+    int32_t tok, j;
+    tile_pos<VW, true>(k, kJPass, &tok, &j);
+    off[k] = (t0 + tok < a.n) ? (int64_t)(t0 + tok) * a.st + (int64_t)j * a.sj : -1;
+  }
   Tile<VW> regs;
   if (full)
-    load_tile<VW, true>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs);
+    load_tile<VW, true>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
   else
-    load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs);
+    load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
   __syncthreads();  // the ln table
   for (int32_t step = 0; step < steps; ++step) {
     const int32_t g = a.g_lo + step / passes;
@@ -254,16 +271,16 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
     double* x = s_x[step & 1];
     double* w = s_w[step & 1];
     if (full)
-      stage_tile<VW, true>(regs, jn, x, w, s_lnc, s_inv);
+      stage_tile<VW, true>(regs, jn, x, w, s_tab);
     else
-      stage_tile<VW, false>(regs, jn, x, w, s_lnc, s_inv);
+      stage_tile<VW, false>(regs, jn, x, w, s_tab);
     if (step + 1 < steps) {  // the next tile streams in while this one is folded
       const int32_t g2 = a.g_lo + (step + 1) / passes;
       const int32_t p2 = step + 1 - (g2 - a.g_lo) * passes;
       if (full)
-        load_tile<VW, true>(a, beta, vnorm, wts, g2, p2, t0, regs);
+        load_tile<VW, true>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
       else
-        load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs);
+        load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
     }
     __syncthreads();
 

@@ -1,5 +1,6 @@
 // Pin + per-head top-K ("Random Attention" blog summary, Algorithm 1: prompt
-// pinned to +inf, top-K per KV head, return the keep set), with the per-layer
+// pinned to +inf, top-K per KV head, return the keep set; also fused with the
+// random draw itself), with the per-layer
 // budgets of GateSight (Sec. 4.2, Appendix G: every head of layer l keeps its
 // prompt plus K_l entries), and the shared list of a layer (Appendix H: one
 // list per layer ranked by the larger of its per-head scores).
@@ -96,6 +97,64 @@ hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_
 
 namespace {
 
+struct DrawArgs {
+  int32_t* kept_idx;
+  int64_t kept_ld;
+  int32_t L, H, n, K, prot, shared_draw;
+  uint64_t seed;
+  uint32_t round;
+};
+
+// The random scorer and the per-list top-K in one launch: list `blockIdx.x`
+// draws its candidates' Philox scores (the stream of kvevict_score_random) as
+// rank keys straight into LDS, or, for lists longer than LDS holds, draws them
+// again on every pass; no score buffer is written or read.
+template <bool kKeysInLds>
+__global__ __launch_bounds__(kThreads) void draw_select_kernel(DrawArgs a) {
+  extern __shared__ uint32_t s_keys[];
+  __shared__ SelectShared sh;
+  const int64_t list = blockIdx.x;
+  const int32_t n = a.n, prot = a.prot, m = n - prot, kk = a.K - prot;
+  int32_t* out = a.kept_idx + list * a.kept_ld;
+  const int tid = threadIdx.x;
+  uint64_t request, layer, head;
+  if (a.shared_draw) {
+    request = (uint64_t)(list / a.L);
+    layer = (uint64_t)(list % a.L);
+    head = 0;
+  } else {
+    const int64_t lh = (int64_t)a.L * a.H;
+    request = (uint64_t)(list / lh);
+    layer = (uint64_t)((list / a.H) % a.L);
+    head = (uint64_t)(list % a.H);
+  }
+  const uint64_t ctr2 = (request << 32) | a.round;
+
+  for (int32_t j = tid; j < prot; j += kThreads) out[j] = j;
+  if (kk <= 0) return;
+  if (kKeysInLds) {
+    for (int32_t c = prot / 4 + tid; 4 * c < n; c += kThreads) {
+      const Philox4x64 r = philox4x64_10((uint64_t)c, head, layer, ctr2, a.seed, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int32_t i = 4 * c + q;
+        if (i >= prot && i < n) s_keys[i - prot] = rank_key(unit_from_word(r.w[q]));
+      }
+    }
+    __syncthreads();
+  }
+  auto key_at = [&](int32_t i) -> uint32_t {
+    if (kKeysInLds) return s_keys[i];
+    const int32_t slot = prot + i;
+    const Philox4x64 r = philox4x64_10((uint64_t)(slot >> 2), head, layer, ctr2, a.seed, 0);
+    return rank_key(unit_from_word(r.w[slot & 3]));
+  };
+  uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate
+  if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
+  emit_kept(key_at, m, thr, need_eq, sh,
+            [&](uint32_t slot, int32_t i) { out[prot + slot] = prot + i; });
+}
+
 // Shared score of each (group, position): the score of the head whose
 // rank_key is largest, the lowest head among equals (its bits are kept).
 __global__ __launch_bounds__(kThreads) void reduce_max_heads_kernel(
@@ -119,6 +178,33 @@ __global__ __launch_bounds__(kThreads) void reduce_max_heads_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_draw_select(int32_t* kept_idx, int64_t kept_ld, int64_t num_lists, int32_t L,
+                              int32_t H, int32_t n, int32_t K, int32_t prot, uint64_t seed,
+                              uint32_t round, bool shared_draw, hipStream_t stream) {
+  if (num_lists == 0) return hipSuccess;
+  DrawArgs a;
+  a.kept_idx = kept_idx;
+  a.kept_ld = kept_ld;
+  a.L = L;
+  a.H = H;
+  a.n = n;
+  a.K = K;
+  a.prot = prot;
+  a.shared_draw = shared_draw ? 1 : 0;
+  a.seed = seed;
+  a.round = round;
+  const int32_t m = n - prot;
+  if (m <= kMaxLdsKeys) {
+    const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL(draw_select_kernel<true>, dim3((unsigned)num_lists), dim3(kThreads), lds,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL(draw_select_kernel<false>, dim3((unsigned)num_lists), dim3(kThreads), 0,
+                       stream, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_reduce_max_heads(float* out, int64_t out_ld, const float* scores, int64_t ld,
                                    int64_t num_groups, int32_t H, int32_t n, hipStream_t stream) {

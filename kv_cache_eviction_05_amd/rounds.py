@@ -4,7 +4,8 @@ A round is the sequence of C-ABI calls the pages describe ("Random Attention"
 blog summary, Algorithm 1 and the engine's chronological compaction; GateSight
 problem statement for the global budget):
 
-    random draw:   kvevict_score_random -> kvevict_select_topk -> kvevict_compact
+    random draw:   kvevict_select_random (draw + top-K) -> kvevict_compact
+                   (or kvevict_score_random -> kvevict_select_topk -> kvevict_compact)
     weighted:      kvevict_score_weighted -> kvevict_select_global -> kvevict_compact
     fused:         kvevict_evict_random_inplace (draw, pin, top-K, in-place move)
     page draw:     kvevict_evict_pages_random (draw per page, page-table edits)
@@ -235,8 +236,17 @@ def pages_round(st: RoundState, round_id: int, stream=None):
                                  st.freed_count, stream)
 
 
+def draw_select(st: RoundState, round_id: int, stream=None):
+    """Random scores drawn on chip and the per-list top-K, in one launch."""
+    c = st.cfg
+    B.kvevict_select_random(st.kept, st.kept.shape[1], c.R, c.L, c.H, st.n, c.K, c.prot, c.seed,
+                            round_id, c.shared, stream)
+
+
 def phases(cfg: RoundConfig):
     """The launches of one round as (name, fn(st, round_id)) in order."""
+    if cfg.fused_select:
+        return [("draw_select", draw_select), ("compact", lambda st, rid: compact(st))]
     if cfg.page_draw:
         return [("pages", pages_round)]
     if cfg.fused:
@@ -246,7 +256,10 @@ def phases(cfg: RoundConfig):
 
 
 def run_round(st: RoundState, round_id: int = 0, stream=None):
-    if st.cfg.page_draw:
+    if st.cfg.fused_select:
+        draw_select(st, round_id, stream)
+        compact(st, stream)
+    elif st.cfg.page_draw:
         pages_round(st, round_id, stream)
     elif st.cfg.fused:
         fused_round(st, round_id, stream)

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
                           "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                           "kvevict_reduce_max_heads", "kvevict_score_keydiff",
                           "kvevict_compact_inplace", "kvevict_evict_random_inplace",
-                          "kvevict_evict_pages_random",
+                          "kvevict_evict_pages_random", "kvevict_select_random",
                           "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
@@ -280,3 +280,17 @@ def test_evict_pages_random_validation():
     assert call(R=-1) == B.KVEVICT_ERR_INVALID_ARG
     # 8192 pages of one slot do not fit on chip
     assert call(ps=1, n=8192, K=4096, prot=0, pt_ld=8192, kept_ld=4096) == B.KVEVICT_ERR_UNSUPPORTED
+
+
+def test_select_random_validation():
+    def call(kept=FAKE, kept_ld=1024, R=4, L=36, H=8, n=1088, K=1024, prot=128, shared=0):
+        return status("kvevict_select_random", kept, kept_ld, R, L, H, n, K, prot, 0, 0, shared, None)
+
+    assert call(prot=1025) == B.KVEVICT_ERR_INVALID_ARG   # prot > K
+    assert call(K=1089) == B.KVEVICT_ERR_INVALID_ARG      # K > n
+    assert call(kept_ld=1023) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(kept=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(L=0) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(H=0) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(R=1 << 32) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(R=1 << 20, L=64, H=64) == B.KVEVICT_ERR_INVALID_ARG  # 2^32 lists

@@ -704,3 +704,28 @@ def test_evict_pages_random(R, L, n, K, prot, ps):
         runs.remove(run)
         pos += len(run)
     assert not runs
+
+
+# ---------------------------------------------------------------------------
+# random draw + top-K in one launch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,L,H,n,K,prot,shared", [
+    (2, 3, 4, 1088, 1024, 128, False),   # the batch shape's lists
+    (2, 3, 4, 2112, 2048, 1024, True),   # shared draw: one list per (request, layer)
+    (1, 2, 2, 20000, 5000, 100, False),  # 19900 candidates: more than LDS holds, drawn per pass
+    (1, 2, 3, 301, 301, 5, False),       # K == n
+    (1, 2, 3, 300, 40, 40, False),       # prot == K
+    (3, 1, 2, 777, 300, 0, False),       # no prompt, ragged
+])
+def test_select_random(R, L, H, n, K, prot, shared):
+    seed, rnd = 17, 9
+    say(f"select_random R={R} L={L} H={H} n={n} K={K} prot={prot} shared={shared}")
+    lists = R * L * (1 if shared else H)
+    want = oracle.select_topk(oracle.score_random(L, H, n, prot, seed, rnd, shared, 0, lists), K, prot)
+    got = torch.full((lists, K + 2), -9, dtype=torch.int32, device=DEV)
+    B.kvevict_select_random(got, K + 2, R, L, H, n, K, prot, seed, rnd, shared)
+    torch.cuda.synchronize()
+    g = to_np(got)
+    assert np.array_equal(g[:, :K], want)
+    assert np.all(g[:, K:] == -9)

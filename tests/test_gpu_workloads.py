@@ -82,7 +82,8 @@ def test_tiny_round_full():
     cfg = configs.TINY
     say("tiny round")
     st = rounds.make_state(cfg, DEV)
-    rounds.run_round(st, round_id=0)
+    rounds.run_round(st, round_id=0)  # draw + top-K in one launch, then the gather
+    rounds.score(st, 0)               # the standalone scorer, for its own parity
     torch.cuda.synchronize()
     want_s = oracle.score_random(cfg.L, cfg.H, cfg.n, cfg.prot, cfg.seed, 0, False, 0, cfg.lists)
     assert np.array_equal(st.scores.cpu().numpy(), want_s)
@@ -111,6 +112,8 @@ def test_batch_round_sampled_and_deterministic():
     check_contig_gather(st, cfg.K)
     assert int(st.errors.item()) == 0
     say("batch round: sampled oracle parity")
+    rounds.score(st, 0)  # the standalone scorer (the round drew its scores on chip)
+    torch.cuda.synchronize()
     for l in sample_lists(cfg.lists, 24, seed=2):
         want_s = oracle.score_random(cfg.L, cfg.H, cfg.n, cfg.prot, cfg.seed, 0, False, l, l + 1)
         assert np.array_equal(st.scores[l:l + 1].cpu().numpy(), want_s), l
@@ -147,6 +150,8 @@ def test_paged_round_sampled(cfg):
     ps, H, D = cfg.page_size, cfg.H, cfg.D
     src_pt, dst_pt = st.src_pt.cpu().numpy(), st.dst_pt.cpu().numpy()
     say(f"paged round {cfg.name}: sampled oracle parity")
+    rounds.score(st, 3)  # the standalone scorer (the round drew its scores on chip)
+    torch.cuda.synchronize()
     for g in sample_lists(cfg.groups, 10, seed=3):
         l0 = g if cfg.shared else g * H
         l1 = l0 + (1 if cfg.shared else H)
@@ -465,4 +470,23 @@ def test_paged_pages_round():
     assert sorted(st.freed[:nf].cpu().tolist()) == sorted(int(x) for x in evicted)
     assert st.kv_bytes_moved() == 0
     del st
+    free()
+
+
+def test_fused_and_three_launch_rounds_agree():
+    """The batch round with the draw inside the select and with the standalone scorer and
+    select (three launches) keeps the same entries and writes the same bytes."""
+    fused = configs.BATCH.small(R=4)
+    plain = configs.BATCH.small(R=4, fuse_draw=False)
+    assert fused.fused_select and not plain.fused_select
+    say("batch round: fused vs three launches")
+    a = rounds.make_state(fused, DEV)
+    b = rounds.make_state(plain, DEV)
+    rounds.run_round(a, round_id=6)
+    rounds.run_round(b, round_id=6)
+    torch.cuda.synchronize()
+    assert torch.equal(a.kept, b.kept)
+    assert torch.equal(a.k_dst, b.k_dst) and torch.equal(a.v_dst, b.v_dst)
+    assert int(a.errors.item()) == 0 and int(b.errors.item()) == 0
+    del a, b
     free()
