@@ -39,8 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads", default="batch",
-                    help="comma list of batch,paged,paged_shared,global,longgen,layers,"
-                         "paged_shared_max (or 'all')")
+                    help="comma list of workload names from configs.ALL (or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,6 +101,19 @@ class Timer:
             for i in range(k):
                 tot[i] += self.marks[base + i].elapsed_time(self.marks[base + i + 1])
         return {n: t / steps for n, t in zip(self.names, tot)}
+
+    def step_ms(self, steps):
+        """Duration of each round, first launch to last, from the same events."""
+        k = len(self.names)
+        return [self.marks[s * (k + 1)].elapsed_time(self.marks[s * (k + 1) + k])
+                for s in range(steps)]
+
+
+def percentiles(xs):
+    """p10, p50 and p90 of a list (nearest rank)."""
+    ys = sorted(xs)
+    pick = lambda q: ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
 def time_workload(torch, rounds, cfg, steps, warmup):
@@ -177,9 +189,11 @@ def time_workload(torch, rounds, cfg, steps, warmup):
         torch.cuda.synchronize()
         ms_per = (time.perf_counter() - t_start) * 1e3 / steps
     kern = timer.per_step_ms(steps)
+    dist = percentiles(timer.step_ms(steps))
     kv_bytes = st.kv_bytes_moved()
     errors = int(st.errors.item())
     out = {"state": st, "ms_per_step": ms_per, "kernels_ms": kern, "kv_bytes": kv_bytes,
+           "round_ms_dist": dist, "algorithmic_bytes": st.algorithmic_bytes(),
            "errors": errors, "applied_rounds": st.applied_rounds - warmup,
            "budget": st.budget, "survival": survival.report(st) if survival else None}
     return out
@@ -241,6 +255,29 @@ def cpu_baseline(torch, cfg, st, seconds):
                       f"compact) x {reps} repetitions in {el:.1f} s on {threads} threads"}
 
 
+def dtod_copy(torch, kv_bytes, gather_gbps, reps=5):
+    """A plain device-to-device copy moving the same bytes as the gather (half read, half
+    written): the ceiling a gather of contiguous rows could reach, and the gather's ratio."""
+    half = kv_bytes // 2
+    a = torch.empty(half, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = 2 * half / (ms * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * half, "ms": round(ms, 4), "gbps": gbps,
+            "gather_vs_copy": gather_gbps / gbps}
+
+
 def copy_calibration(torch):
     """A plain device-to-device copy of 4 GiB: reference for scaling FETCH/WRITE counters."""
     n = 4 << 30
@@ -271,7 +308,7 @@ def main():
     binding.load()
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
-        names = ["batch", "paged", "paged_shared", "global", "longgen", "layers",
+        names = ["batch", "tiny", "paged", "paged_shared", "global", "longgen", "layers",
                  "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
                  "paged_fused", "longgen_fused", "paged_pages"]
     if "batch" not in names:
@@ -295,6 +332,8 @@ def main():
             "kv_gbps_round": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
             "compact_gbps": achieved if not cfg.page_draw else None,
             "compact_frac_of_peak": achieved / PEAK_HBM_GBPS if not cfg.page_draw else None,
+            "round_ms_p10_p50_p90": [round(r["round_ms_dist"][q], 4) for q in ("p10", "p50", "p90")],
+            "algorithmic_bytes_per_round": r["algorithmic_bytes"],
             "applied_rounds": r["applied_rounds"],
             "bad_rows": r["errors"],
         }
@@ -309,6 +348,7 @@ def main():
         if r["survival"] is not None:
             entry["survival"] = r["survival"]
         if name == "batch":
+            entry["dtod_copy"] = dtod_copy(torch, r["kv_bytes"], achieved)
             head = (cfg, r, entry)
             if not args.no_cpu_baseline:
                 print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -349,6 +389,9 @@ def main():
             "traffic": traffic_for(e["kv_bytes_per_round"]),
             "algorithmic_bytes": e["kv_bytes_per_round"],
         },
+        "round_ms_p10_p50_p90": e["round_ms_p10_p50_p90"],
+        "algorithmic_bytes_per_round": e["algorithmic_bytes_per_round"],
+        "dtod_copy": e["dtod_copy"],
         "cpu_baseline": e.get("cpu"),
         "bad_rows": e["bad_rows"],
     }

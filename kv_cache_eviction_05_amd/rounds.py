@@ -88,6 +88,39 @@ class RoundState:
         return rows * c.row_bytes * 2 * 2
 
 
+    def algorithmic_bytes(self) -> dict:
+        """Bytes one round must move at minimum, by kind: the K/V rows (kv_bytes_moved), the
+        scores written once and read once (none when drawn inside the select), the kept
+        indices written once and read once by the gather, and the inputs a scorer reads
+        (GDN signals, or the keys for KeyDiff), or the page-table entries a page draw edits."""
+        c = self.cfg
+        n, K = self.n, c.K
+        out = {"kv": self.kv_bytes_moved(), "scores": 0, "indices": 0, "inputs": 0}
+        if c.page_draw:
+            P, Kp = n // c.page_size, K // c.page_size
+            out["inputs"] = c.groups * (P * 4 * 2 + (P - Kp) * 4)
+            out["indices"] = c.groups * Kp * 4
+            return out
+        if c.select in ("global", "layers"):
+            lists = c.L * c.H * c.R
+            out["scores"] = lists * n * 4 * 2
+            out["indices"] = int(self.kept_count.sum().item()) * 4 * 2 + lists * 4 * 2
+            out["inputs"] = 2 * c.G * n * c.Hg * 4
+            return out
+        kept_lists = c.lists
+        kk = c.kept_shared if c.shared_max else K
+        out["indices"] = kept_lists * kk * 4 * (1 if c.fused else 2)
+        if c.fused or c.fused_select:
+            return out
+        if c.shared_max:
+            out["scores"] = (c.groups * c.H + c.groups) * n * 4 * 2
+        else:
+            out["scores"] = kept_lists * n * 4 * 2
+        if c.scorer == "keydiff":
+            out["inputs"] = c.groups * c.H * n * c.D * 2
+        return out
+
+
 def _desc_pair(cfg: RoundConfig, n_src: int, cap_dst: int, device, seed: int):
     """Allocate K/V source and destination stores and their descriptors."""
     D, H, G = cfg.D, cfg.H, cfg.groups
