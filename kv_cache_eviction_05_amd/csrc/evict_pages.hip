@@ -38,7 +38,7 @@ struct PagesArgs {
 
 __global__ __launch_bounds__(kThreads) void evict_pages_kernel(PagesArgs a) {
   extern __shared__ int32_t s_dyn[];  // keys [P - pp], old row [P], kept [Kp], kept flag [P]
-  __shared__ SelectShared sh;
+  __shared__ SelectShared<> sh;
   __shared__ uint32_t s_scan[kThreads / kWave];
   __shared__ uint32_t s_base;
   const int32_t P = a.P, pp = a.pp, Kp = a.Kp, ps = a.ps;
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void evict_pages_kernel(PagesArgs a) {
     const int64_t i = (int64_t)b * ps;  // first slot of page b
     const Philox4x64 r =
         philox4x64_10((uint64_t)(i >> 2), 0u, layer, (request << 32) | a.round, a.seed, 0);
-    s_keys[b - pp] = rank_key(unit_from_word(r.w[i & 3]));
+    const uint64_t w = (i & 2) ? ((i & 1) ? r.w[3] : r.w[2]) : ((i & 1) ? r.w[1] : r.w[0]);
+    s_keys[b - pp] = rank_key(unit_from_word(w));  // word i % 4, with constant indices
   }
   for (int32_t b = tid; b < P; b += kThreads) {
     s_old[b] = row[b];

@@ -1,4 +1,5 @@
-// Top-k of a list of 32-bit rank keys held by one 256-thread workgroup
+// Top-k of a list of 32-bit rank keys held by one workgroup of NT threads
+// (NT a multiple of 64, at least 256)
 // ("Random Attention" blog summary, Algorithm 1: top-K per KV head; ties go to
 // the lower position).
 //
@@ -16,33 +17,36 @@ namespace kvevict {
 
 constexpr int kSelectThreads = 256;
 
+template <int NT = kSelectThreads>
 struct SelectShared {
+  static_assert(NT % kWave == 0 && NT >= 256, "one thread per histogram bin");
   uint32_t hist[256];
-  uint32_t scan[kSelectThreads / kWave];
+  uint32_t scan[NT / kWave];
   uint32_t pick[3];
-  uint32_t tile[2 * (kSelectThreads / kWave)];
+  uint32_t tile[2 * (NT / kWave)];
 };
 
 // Keep kk of the m keys key_at(0..m-1), 0 < kk < m: every key > thr, and the
 // first need_eq keys == thr (need_eq = 0xffffffff: every key == thr).
-template <class KeyAt>
-__device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared& sh,
+template <int NT, class KeyAt>
+__device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared<NT>& sh,
                              uint32_t& thr, uint32_t& need_eq) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)kk;
   bool whole_bucket = false;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    sh.hist[tid] = 0u;
+    if (tid < 256) sh.hist[tid] = 0u;
     __syncthreads();
-    for (int32_t i = tid; i < m; i += kSelectThreads) {
+    for (int32_t i = tid; i < m; i += NT) {
       const uint32_t k = key_at(i);
       if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // thread t holds bin 255 - t, so the inclusive scan counts keys in bins >= 255 - t
-    const uint32_t c = sh.hist[255 - tid];
+    // thread t < 256 holds bin 255 - t (the others count 0), so the inclusive scan
+    // counts keys in bins >= 255 - t
+    const uint32_t c = tid < 256 ? sh.hist[255 - tid] : 0u;
     uint32_t total;
-    const uint32_t incl = block_inclusive_scan<kSelectThreads>(c, sh.scan, &total);
+    const uint32_t incl = block_inclusive_scan<NT>(c, sh.scan, &total);
     const uint32_t excl = incl - c;
     if (excl < remaining && incl >= remaining) {
       sh.pick[0] = 255u - (uint32_t)tid;
@@ -67,14 +71,14 @@ __device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared& 
 
 // Calls out(slot, i) for every kept key i (key > thr, or == thr among the
 // first need_eq such), slot = number of kept keys before position i.
-template <class KeyAt, class Out>
+template <int NT, class KeyAt, class Out>
 __device__ void emit_kept(KeyAt key_at, int32_t m, uint32_t thr, uint32_t need_eq,
-                          SelectShared& sh, Out out) {
-  constexpr int kWaves = kSelectThreads / kWave;
+                          SelectShared<NT>& sh, Out out) {
+  constexpr int kWaves = NT / kWave;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   uint32_t carry_gt = 0u, carry_eq = 0u;
-  for (int32_t base = 0; base < m; base += kSelectThreads) {
+  for (int32_t base = 0; base < m; base += NT) {
     const int32_t i = base + tid;
     const bool valid = i < m;
     const uint32_t k = valid ? key_at(i) : 0u;

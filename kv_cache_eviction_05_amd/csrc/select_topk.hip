@@ -17,7 +17,9 @@ namespace kvevict {
 namespace {
 
 constexpr int kThreads = kSelectThreads;
-constexpr int32_t kMaxLdsKeys = 15360;  // 60 KiB of keys (+ ~1 KiB static LDS)
+constexpr int kBigThreads = 1024;           // workgroup for lists longer than kMaxLdsKeys
+constexpr int32_t kMaxLdsKeys = 15360;      // 60 KiB of keys (+ ~1 KiB static LDS)
+constexpr int32_t kMaxBigLdsKeys = 38912;   // 152 KiB of keys, within gfx950's 160 KiB
 
 struct TopkArgs {
   int32_t* kept_idx;
@@ -30,14 +32,14 @@ struct TopkArgs {
   int32_t kk[kMaxBudgetLayers];       // candidates kept per head in each layer
 };
 
-template <bool kKeysInLds>
-__global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
+template <bool kKeysInLds, int NT>
+__global__ __launch_bounds__(NT) void select_topk_kernel(TopkArgs a) {
   int32_t* __restrict__ kept_idx = a.kept_idx;
   const float* __restrict__ scores = a.scores;
   const int64_t kept_ld = a.kept_ld, ld = a.ld;
   const int32_t n = a.n, prot = a.prot;
   extern __shared__ uint32_t s_keys[];
-  __shared__ SelectShared sh;
+  __shared__ SelectShared<NT> sh;
 
   const int64_t list = blockIdx.x;
   const float* row = scores + list * ld;
@@ -46,12 +48,12 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
   const int32_t kk = a.L > 0 ? a.kk[(list / a.H) % a.L] : a.K - prot;  // candidates to keep
   const int tid = threadIdx.x;
 
-  for (int32_t j = tid; j < prot; j += kThreads) out[j] = j;
+  for (int32_t j = tid; j < prot; j += NT) out[j] = j;
   if (a.kept_count && tid == 0) a.kept_count[list] = prot + kk;
   if (kk <= 0) return;
 
   if (kKeysInLds) {
-    for (int32_t i = tid; i < m; i += kThreads) s_keys[i] = rank_key(row[prot + i]);
+    for (int32_t i = tid; i < m; i += NT) s_keys[i] = rank_key(row[prot + i]);
     __syncthreads();
   }
   auto key_at = [&](int32_t i) -> uint32_t {
@@ -62,6 +64,20 @@ __global__ __launch_bounds__(kThreads) void select_topk_kernel(TopkArgs a) {
   if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
   emit_kept(key_at, m, thr, need_eq, sh,
             [&](uint32_t slot, int32_t i) { out[prot + slot] = prot + i; });
+}
+
+// True if a list of m keys fits the big kernel's dynamic LDS on the current
+// device (gfx950: 160 KiB per workgroup), after raising the kernel's limit.
+bool big_lds_ok(int32_t m, const void* kernel) {
+  if (m > kMaxBigLdsKeys) return false;
+  int dev = 0, limit = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&limit, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return false;
+  const size_t need = (size_t)m * sizeof(uint32_t) + sizeof(SelectShared<kBigThreads>);
+  if (need > (size_t)limit) return false;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)(m * sizeof(uint32_t))) == hipSuccess;
 }
 
 }  // namespace
@@ -84,12 +100,15 @@ hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_
   a.H = H;
   for (int32_t l = 0; l < kMaxBudgetLayers; ++l) a.kk[l] = (layer_kk && l < L) ? layer_kk[l] : 0;
   const int32_t m = n - prot;
+  const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(select_topk_kernel<true>, dim3((unsigned)num_lists), dim3(kThreads), lds,
-                       stream, a);
+    hipLaunchKernelGGL((select_topk_kernel<true, kThreads>), grid, dim3(kThreads), lds, stream, a);
+  } else if (big_lds_ok(m, reinterpret_cast<const void*>(&select_topk_kernel<true, kBigThreads>))) {
+    hipLaunchKernelGGL((select_topk_kernel<true, kBigThreads>), grid, dim3(kBigThreads),
+                       (size_t)m * sizeof(uint32_t), stream, a);
   } else {
-    hipLaunchKernelGGL(select_topk_kernel<false>, dim3((unsigned)num_lists), dim3(kThreads), 0,
+    hipLaunchKernelGGL((select_topk_kernel<false, kBigThreads>), grid, dim3(kBigThreads), 0,
                        stream, a);
   }
   return hipGetLastError();
@@ -109,10 +128,10 @@ struct DrawArgs {
 // draws its candidates' Philox scores (the stream of kvevict_score_random) as
 // rank keys straight into LDS, or, for lists longer than LDS holds, draws them
 // again on every pass; no score buffer is written or read.
-template <bool kKeysInLds>
-__global__ __launch_bounds__(kThreads) void draw_select_kernel(DrawArgs a) {
+template <bool kKeysInLds, int NT>
+__global__ __launch_bounds__(NT) void draw_select_kernel(DrawArgs a) {
   extern __shared__ uint32_t s_keys[];
-  __shared__ SelectShared sh;
+  __shared__ SelectShared<NT> sh;
   const int64_t list = blockIdx.x;
   const int32_t n = a.n, prot = a.prot, m = n - prot, kk = a.K - prot;
   int32_t* out = a.kept_idx + list * a.kept_ld;
@@ -130,10 +149,10 @@ __global__ __launch_bounds__(kThreads) void draw_select_kernel(DrawArgs a) {
   }
   const uint64_t ctr2 = (request << 32) | a.round;
 
-  for (int32_t j = tid; j < prot; j += kThreads) out[j] = j;
+  for (int32_t j = tid; j < prot; j += NT) out[j] = j;
   if (kk <= 0) return;
   if (kKeysInLds) {
-    for (int32_t c = prot / 4 + tid; 4 * c < n; c += kThreads) {
+    for (int32_t c = prot / 4 + tid; 4 * c < n; c += NT) {
       const Philox4x64 r = philox4x64_10((uint64_t)c, head, layer, ctr2, a.seed, 0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -147,7 +166,9 @@ __global__ __launch_bounds__(kThreads) void draw_select_kernel(DrawArgs a) {
     if (kKeysInLds) return s_keys[i];
     const int32_t slot = prot + i;
     const Philox4x64 r = philox4x64_10((uint64_t)(slot >> 2), head, layer, ctr2, a.seed, 0);
-    return rank_key(unit_from_word(r.w[slot & 3]));
+    // word slot % 4, chosen with constant indices (a variable index would place r in memory)
+    const uint64_t w = (slot & 2) ? ((slot & 1) ? r.w[3] : r.w[2]) : ((slot & 1) ? r.w[1] : r.w[0]);
+    return rank_key(unit_from_word(w));
   };
   uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate
   if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
@@ -195,12 +216,15 @@ hipError_t launch_draw_select(int32_t* kept_idx, int64_t kept_ld, int64_t num_li
   a.seed = seed;
   a.round = round;
   const int32_t m = n - prot;
+  const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(draw_select_kernel<true>, dim3((unsigned)num_lists), dim3(kThreads), lds,
-                       stream, a);
+    hipLaunchKernelGGL((draw_select_kernel<true, kThreads>), grid, dim3(kThreads), lds, stream, a);
+  } else if (big_lds_ok(m, reinterpret_cast<const void*>(&draw_select_kernel<true, kBigThreads>))) {
+    hipLaunchKernelGGL((draw_select_kernel<true, kBigThreads>), grid, dim3(kBigThreads),
+                       (size_t)m * sizeof(uint32_t), stream, a);
   } else {
-    hipLaunchKernelGGL(draw_select_kernel<false>, dim3((unsigned)num_lists), dim3(kThreads), 0,
+    hipLaunchKernelGGL((draw_select_kernel<false, kBigThreads>), grid, dim3(kBigThreads), 0,
                        stream, a);
   }
   return hipGetLastError();
