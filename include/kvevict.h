@@ -302,7 +302,8 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
  * errors  optional device counter: each row whose index is below its slot or
  *         outside the store, or whose page id is invalid, is skipped and adds 1.
  *         Counts outside [0, K] are clamped.
- * Limits: num_groups * H < 2^31 and n * head_dim / 8 <= 2^30, else
+ * Limits: num_groups * H < 2^31, n * head_dim / 8 <= 2^30 and, paged,
+ * num_groups * ceil(n / page_size) < 2^32 (free-list offsets), else
  * KVEVICT_ERR_INVALID_ARG.  Calls on the same store must not overlap.
  */
 kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
@@ -369,7 +370,8 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
  * kept_pages  optional device int32 out [num_groups][kept_ld], kept_ld >= K/page_size.
  * Requires page_size >= 1, n and K multiples of page_size, 0 <= prot <= K <= n,
  * num_requests < 2^32, L >= 1; KVEVICT_ERR_UNSUPPORTED when
- * (P - ceil(prot/page_size)) + 2P + K/page_size > 15360 (the group is held on chip).
+ * (P - ceil(prot/page_size)) + 2P + K/page_size > 15360 (the group is held on chip);
+ * KVEVICT_ERR_INVALID_ARG when num_groups * (P - K/page_size) >= 2^32.
  * Calls on the same table must not overlap.
  */
 kvevict_status kvevict_evict_pages_random(int32_t* page_table, int64_t pt_ld, int32_t page_size,

@@ -16,6 +16,7 @@
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kUint32Max = 4294967295LL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -315,6 +316,8 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if (sv.paged && num_groups * ((n + store->page_size - 1) / store->page_size) > kUint32Max)
+    return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit
   return hip_status(kvevict::launch_compact_inplace(sv, k, v, D, H, kept_idx, kept_ld, kept_count,
                                                     K, n, num_groups, idx_lists_per_group,
                                                     sv.paged ? freed_pages : nullptr,
@@ -343,6 +346,8 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
   if ((int64_t)(n - prot) + K > kvevict::kMaxFusedEntries) return KVEVICT_ERR_UNSUPPORTED;
+  if (sv.paged && num_groups * ((n + store->page_size - 1) / store->page_size) > kUint32Max)
+    return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit
   return hip_status(kvevict::launch_evict_random_inplace(
       sv, k, v, D, H, num_groups, L, n, K, prot, seed, round, shared_draw != 0, kept_idx, kept_ld,
       sv.paged ? freed_pages : nullptr, freed_count, errors, stream));
@@ -376,6 +381,7 @@ kvevict_status kvevict_evict_pages_random(int32_t* page_table, int64_t pt_ld, in
   if (pt_ld < P) return KVEVICT_ERR_INVALID_ARG;
   if (kept_pages && kept_ld < Kp) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups > 0 && (!page_table || !freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups * (int64_t)(P - Kp) > kUint32Max) return KVEVICT_ERR_INVALID_ARG;  // 32-bit offsets
   if (kvevict::evict_pages_lds_bytes(P, pp, Kp) > (size_t)kvevict::kMaxFusedEntries * 4)
     return KVEVICT_ERR_UNSUPPORTED;
   return hip_status(kvevict::launch_evict_pages(page_table, pt_ld, page_size, num_groups, L, n, K,

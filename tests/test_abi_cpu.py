@@ -280,6 +280,8 @@ def test_evict_pages_random_validation():
     assert call(R=-1) == B.KVEVICT_ERR_INVALID_ARG
     # 8192 pages of one slot do not fit on chip
     assert call(ps=1, n=8192, K=4096, prot=0, pt_ld=8192, kept_ld=4096) == B.KVEVICT_ERR_UNSUPPORTED
+    # 2^32 freed page ids or more overflow the free-list offsets
+    assert call(R=1 << 24, L=64, n=64, K=0, prot=0, pt_ld=4, kept_ld=0) == B.KVEVICT_ERR_INVALID_ARG
 
 
 def test_select_random_validation():
