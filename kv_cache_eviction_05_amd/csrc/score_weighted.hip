@@ -26,8 +26,8 @@
 // log makes one 16-byte LDS read.
 //
 // Precision: the product beta*|v| of two floats is exact in binary64; its
-// natural log is taken in binary64 (table-driven reduction to [-2^-8, 2^-8]
-// and a degree-7 series, within a few binary64 ulps; zero, infinities, NaN
+// natural log is taken in binary64 (table-driven reduction to [-2^-9, 2^-9]
+// and a degree-6 series, within a few binary64 ulps; zero, infinities, NaN
 // and negative products go through the library log); accumulation is
 // binary64 and the result is rounded once to fp32.
 #include <cmath>
@@ -48,7 +48,7 @@ constexpr int kHB = 4;                      // KV heads per launch
 constexpr int kSlots = 2;                   // accumulator slots
 constexpr int kLayersPerLaunch = 16;
 constexpr int kPlanLayers = 64;             // GDN layers one launch spans
-constexpr int kLnTable = 128;               // ln table: centres of [1, 2) in steps of 1/128
+constexpr int kLnTable = 256;               // ln table: centres of [1, 2) in steps of 1/256
 constexpr int kXStride = kTok + 1;          // doubles per staged GDN head (padding)
 constexpr int kElems = kTok * kJPass / kThreads;  // tile elements per thread
 constexpr int kWRow = kSlots * kHB * kJPass;      // weights of one (GDN layer, pass)
@@ -70,22 +70,20 @@ struct WeightedArgs {
 };
 
 // ln(x) in binary64 for a positive normal x: x = 2^e * m, m in [1, 2);
-// c = 1 + (i + 1/2)/128 is the centre of m's slot, r = (m - c)/c with
-// |r| <= 2^-8, and ln x = e ln 2 + ln c + ln(1 + r) with
-// ln(1 + r) = r - r^2/2 + ... + r^7/7.  Only the high word of x carries e and
-// i, so m and c are built from it.  *special is set when x is not a positive
+// c = 1 + (i + 1/2)/256 is the centre of m's slot, r = m/c - 1 (one fma with
+// the tabulated 1/c: absolute error ~2^-53) with |r| <= 2^-9, and
+// ln x = e ln 2 + ln c + ln(1 + r) with ln(1 + r) = r - r^2/2 + ... - r^6/6
+// (truncation below 2^-66).  Only the high word of x carries e and i.  *special is set when x is not a positive
 // normal number (zero, subnormal, infinite, NaN or negative).
 __device__ __forceinline__ double ln_fast(double x, const double2* tab, bool* special) {
   const uint32_t hi = (uint32_t)__double2hiint(x);
   const uint32_t ex = hi >> 20;  // sign and biased exponent
   *special = ex - 1u >= 0x7feu;
-  const uint32_t i = (hi >> 13) & (kLnTable - 1);
+  const uint32_t i = (hi >> 12) & (kLnTable - 1);
   const double m = __hiloint2double((int)((hi & 0x000fffffu) | 0x3ff00000u), __double2loint(x));
-  const double c = __hiloint2double((int)((hi & 0x000fe000u) | 0x3ff01000u), 0);
   const double2 tc = tab[i];  // {ln c, 1/c}
-  const double r = (m - c) * tc.y;
-  double p = 1.0 / 7.0;
-  p = fma(p, r, -1.0 / 6.0);
+  const double r = fma(m, tc.y, -1.0);
+  double p = -1.0 / 6.0;
   p = fma(p, r, 1.0 / 5.0);
   p = fma(p, r, -0.25);
   p = fma(p, r, 1.0 / 3.0);
