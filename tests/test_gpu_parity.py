@@ -729,3 +729,50 @@ def test_select_random(R, L, H, n, K, prot, shared):
     g = to_np(got)
     assert np.array_equal(g[:, :K], want)
     assert np.all(g[:, K:] == -9)
+
+
+# ---------------------------------------------------------------------------
+# degenerate shapes of the fused and page-granular entry points
+# ---------------------------------------------------------------------------
+
+def test_fused_entry_points_on_empty_batches():
+    """No request: every entry point returns without touching its outputs."""
+    kept = torch.full((4, 8), -3, dtype=torch.int32, device=DEV)
+    B.kvevict_select_random(kept, 8, 0, 2, 2, 8, 4, 1, 0, 0, False)
+    desc = B.contig_desc(64, 2, 16)
+    k = torch.zeros((4, 16, 64), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    B.kvevict_evict_random_inplace(desc, k, v, 0, 2, 16, 8, 2, 0, 0, False, kept, 8)
+    pt = torch.zeros((2, 4), dtype=torch.int32, device=DEV)
+    freed = torch.full((8,), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_evict_pages_random(pt, 4, 16, 0, 2, 64, 32, 0, 0, 0, kept, 8, freed, fcount)
+    torch.cuda.synchronize()
+    assert torch.all(kept == -3) and torch.all(freed == -5) and int(fcount.item()) == 0
+    assert torch.all(pt == 0)
+
+
+@pytest.mark.parametrize("n,K,prot", [(1, 1, 0), (1, 1, 1), (5, 3, 2), (7, 4, 3), (9, 9, 0)])
+def test_select_random_tiny_lists(n, K, prot):
+    """Lists of a few entries, prompts ending inside a Philox block, against the oracle."""
+    R, L, H, seed, rnd = 2, 2, 3, 21, 4
+    lists = R * L * H
+    want = oracle.select_topk(oracle.score_random(L, H, n, prot, seed, rnd, False, 0, lists), K, prot)
+    got = torch.full((lists, K), -9, dtype=torch.int32, device=DEV)
+    B.kvevict_select_random(got, K, R, L, H, n, K, prot, seed, rnd, False)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(got), want)
+
+
+def test_evict_random_inplace_tiny_lists():
+    """Lists of 6 rows keeping 4 with a 3-row prompt, contiguous: rows and keep sets."""
+    R, L, H, D, n, K, prot = 2, 1, 2, 16, 6, 4, 3
+    groups = R * L
+    kept = oracle.select_topk(oracle.score_random(L, H, n, prot, 1, 2, False, 0, groups * H), K, prot)
+    desc, pt, ks, vs, k, v = make_store("contig", groups, H, D, n, 16, seed=9)
+    got = torch.full((groups * H, K), -9, dtype=torch.int32, device=DEV)
+    B.kvevict_evict_random_inplace(desc, k, v, R, L, n, K, prot, 1, 2, False, got, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(got), kept)
+    check_inplace("contig", ks, vs, k, v, np.ascontiguousarray(kept), None, groups, H, H, pt, 16, n,
+                  K, D, None, torch.zeros(1, dtype=torch.int32, device=DEV))
