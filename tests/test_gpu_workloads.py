@@ -267,7 +267,7 @@ def test_longgen_rounds_replayed_by_oracle():
 def test_paged_shared_max_round_sampled():
     """Paged round with one list per (request, layer) by the max of the per-head scores and a
     kept count rounded down to a multiple of four: sampled groups against the oracle."""
-    cfg = configs.PAGED_SHARED_MAX.small(R=8)
+    cfg = configs.PAGED_SHARED_MAX
     say("paged shared-max round: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st, round_id=5)
@@ -351,7 +351,7 @@ def test_layers_round():
 def test_keydiff_round_sampled():
     """The batch round scored by KeyDiff: sampled lists against the oracle's scores (two fp32
     ulps), selection given the GPU's scores, and the whole gather."""
-    cfg = configs.KEYDIFF.small(R=16)
+    cfg = configs.KEYDIFF
     say("keydiff round: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st)
@@ -376,7 +376,7 @@ def test_paged_inplace_round_sampled(base):
     sampled groups every head's first K rows are the kept rows of the cache before the round and
     the rows past K are untouched; every group returns its 4 tail pages (132 -> 128) and the
     free list holds exactly those pages."""
-    cfg = base.small(R=8)
+    cfg = base
     say(f"{cfg.name} round: allocating")
     st = rounds.make_state(cfg, DEV)
     ps, H, D, n, K = cfg.page_size, cfg.H, cfg.D, cfg.n, cfg.K
@@ -489,4 +489,37 @@ def test_fused_and_three_launch_rounds_agree():
     assert torch.equal(a.k_dst, b.k_dst) and torch.equal(a.v_dst, b.v_dst)
     assert int(a.errors.item()) == 0 and int(b.errors.item()) == 0
     del a, b
+    free()
+
+
+@pytest.mark.parametrize("base", [configs.LONGGEN, configs.LONGGEN_INPLACE, configs.LONGGEN_FUSED],
+                         ids=lambda c: c.name)
+def test_longgen_full_size_two_rounds_sampled(base):
+    """The 30-round workload at its full size (36,864 lists of 3136 rows): two rounds of the
+    driver exactly as the benchmark runs them; sampled lists against the oracle (kept indices
+    from its scores, rows from its gather of the cache before the round), properties on every
+    list."""
+    cfg = base
+    say(f"{cfg.name} full size: allocating")
+    st = rounds.make_state(cfg, DEV)
+    n, K, D = cfg.n, cfg.K, cfg.D
+    samples = sample_lists(cfg.lists, 10, seed=11)
+    idx = torch.tensor(samples, device=DEV)
+    for rnd in range(2):
+        before_k, before_v = u16(st.k_src[idx]), u16(st.v_src[idx])
+        rounds.run_round(st, round_id=rnd)
+        torch.cuda.synchronize()
+        assert int(st.errors.item()) == 0
+        check_kept_properties(st.kept, K, cfg.prot, n)
+        out_k, out_v = u16(st.k_dst[idx][:, :K]), u16(st.v_dst[idx][:, :K])
+        for a, l in enumerate(samples):
+            want_s = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, cfg.seed, rnd, False, l, l + 1)
+            want_k = oracle.select_topk(want_s, K, cfg.prot)[0]
+            assert np.array_equal(st.kept[l].cpu().numpy(), want_k), (rnd, l)
+            assert np.array_equal(out_k[a], before_k[a][want_k]), (rnd, l)
+            assert np.array_equal(out_v[a], before_v[a][want_k]), (rnd, l)
+        say(f"{cfg.name} full size: round {rnd} ok")
+        rounds.append_tokens(st, rnd)
+        rounds.swap(st)
+    del st
     free()
