@@ -32,9 +32,11 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+static_assert(2048 / kThreads <= 8 && 1024 % kThreads == 0, "resolve: at most 8 bins per thread");
 constexpr int kWaves = kThreads / kWave;
-constexpr int32_t kChunk = 4096;
+constexpr int32_t kChunk = 8192;  // 16 keys per thread (same-process A/B: 52 us against
+                                  // 62 us for 4096-key items on 256 threads)
 
 // workspace layout (uint32 words)
 constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
@@ -136,7 +138,7 @@ __device__ void resolve_level(uint32_t* ws, int lvl, uint32_t prefix, uint32_t m
   const int tid = threadIdx.x;
   const Level L = level_of(lvl);
   const uint32_t* hist = ws + L.off;
-  const uint32_t per = L.bins / kThreads;             // 8 or 4 bins per thread, top first
+  const uint32_t per = L.bins / kThreads;             // bins per thread (<= 8), top first
   const uint32_t top = L.bins - per * (uint32_t)tid;  // exclusive upper bin
   uint32_t h[8];
   uint32_t c = 0u;
