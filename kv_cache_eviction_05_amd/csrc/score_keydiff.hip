@@ -7,14 +7,17 @@
 //
 // The mean needs every key before any cosine, and a list (1088 keys of 256 B
 // at D = 128: 278 KB) is larger than a CU's share of L2 and of the Infinity
-// Cache, so a second pass over the keys would go back to HBM.  One workgroup
-// of 1024 threads per list therefore keeps the list's first rows on chip: a
-// row of D bf16 is VPR = D/8 16-byte vectors, thread t owns vector column
-// t % VPR of rows t / VPR + k * (1024 / VPR); its first 8 such rows stay in
-// registers and the next 7 or 8 in LDS (128 KB of the CU's 160 KB), so 1024
-// rows at D = 128 are read once and only rows beyond them are read twice.
+// Cache, so a second pass over the keys goes back to HBM.  One workgroup of
+// 512 threads per list keeps the list's first rows on chip between the two
+// passes: a row of D bf16 is VPR = D/8 16-byte vectors, thread t owns vector
+// column t % VPR of rows t / VPR + k * (512 / VPR); its first 8 such rows stay
+// in registers and the next 7 or 8 in LDS (64 KB), which at D = 128 holds 512
+// of 1088 rows; the rest are read twice.  Two such workgroups fit a CU, so one
+// list's loads overlap the other's binary64 work: measured against one
+// 1024-thread workgroup per CU holding 1024 rows (1.04x traffic, no overlap),
+// 14% faster at ~1.5x traffic.
 // Pass 1 accumulates the column sums in binary64 in a fixed order (lanes of a
-// column with shuffles, then the 16 waves in a tree through LDS) into the mean
+// column with shuffles, then the waves in a tree through LDS) into the mean
 // and its squared norm.  Pass 2 forms each row's dot product with the mean and
 // its squared norm in binary64, adds the VPR partials of a row with DPP lane
 // moves, and rounds -dot * rsqrt(|k|^2) / |mean| once to fp32.
@@ -26,7 +29,7 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kReg = 8;     // rows per thread held in registers
 constexpr int kUnroll = 2;  // rows per thread in flight for the streamed tail
