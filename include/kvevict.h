@@ -267,8 +267,9 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
  * src, dst     host descriptors (see kvevict_kv_desc), same D and H.
  * k_src ...    device bf16 stores, 16-byte aligned.
  * errors       optional device uint32 counter; each row whose index or page
- *              id falls outside its store (or whose count is outside [0, K])
- *              is skipped and adds 1.  May be NULL.
+ *              id falls outside its store is skipped and adds 1, and each
+ *              index list whose count is outside [0, K] adds 1 and is clamped
+ *              to that range.  May be NULL.
  * Requires K <= dst rows per list, kept_ld >= K.
  */
 kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,

@@ -3,29 +3,30 @@
 // (layer, head, token) scores).
 //
 // The candidates of each list ([prot, n)) are cut into items of kChunk
-// positions, item f = list * chunks + chunk in flat order; one workgroup owns
-// one item in every kernel below.
+// positions, item f = list * chunks + chunk in flat order.
 //   init      prompt indices and kept_count = prot for every list; zeroes the
-//             histograms, counters and state of the workspace
+//             histograms and the done counter
 //   hist x3   radix histograms of the 11/11/10-bit digits of rank_key(score),
-//             restricted to the keys matching the digits chosen so far; the
-//             last workgroup to finish resolves the digit from the finished
-//             histogram and stores it (later levels are skipped once a bucket
-//             is taken whole)
-//   count     per-item counts of keys > T and == T (T the threshold key)
-//   emit      the item's offset from the counts of the items before it in
-//             flat order (ties at T go to the lowest list*n + i), the per-list
-//             kept counts, and a ballot/mbcnt chronological emit of the item.
-//             With many items the last count workgroup scans the counts once
-//             instead and emit reads the offsets.
+//             restricted to the keys matching the digits chosen so far.  Each
+//             workgroup of level l derives those digits itself from the
+//             finished histograms of levels < l (the same computation in every
+//             workgroup, so no workgroup has to wait for another); it returns
+//             at once if an earlier level took its bucket whole.
+//   count     per-item counts of keys > T and == T, T the threshold key
+//             derived from the three histograms; with many items the last
+//             count workgroup scans them once into per-item offsets
+//   emit      the item's offset (ties at T go to the lowest list*n + i): the
+//             sums over the items before it, or the scanned offset; the
+//             per-list kept counts; a ballot/mbcnt chronological emit.
 // All counts are integer atomics or scans, so the result is deterministic.
 //
-// Every workspace word is written and read only with device-scope atomics
-// (ld_dev, st_dev, fetch-add), which take effect at the device's coherence
-// point: words passed between workgroups inside a kernel need no cache flush
-// (a device-scope fence would write back and invalidate every XCD's L2), and
-// no plain access can meet a stale copy of a word that an atomic wrote, in
-// this call or an earlier one on the same workspace.
+// Words passed between workgroups of one kernel (the per-item counts and the
+// done counter read by the last count workgroup) are written and read only
+// with device-scope atomics, which take effect at the device's coherence point
+// and need no cache flush (a device-scope fence would write back and
+// invalidate every XCD's L2).  Words read only by later kernels of the call
+// (histograms, per-item counts, offsets) are read with plain loads: the kernel
+// boundary makes them visible.
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 
@@ -33,7 +34,9 @@ namespace kvevict {
 namespace {
 
 constexpr int kThreads = 512;
-static_assert(2048 / kThreads <= 8 && 1024 % kThreads == 0, "resolve: at most 8 bins per thread");
+constexpr int kBinsPerThread = 2048 / kThreads;
+static_assert(kBinsPerThread >= 1 && 2048 % kThreads == 0 && 1024 % kThreads == 0,
+              "resolve: whole bins per thread");
 constexpr int kWaves = kThreads / kWave;
 constexpr int32_t kChunk = 8192;  // 16 keys per thread (same-process A/B: 52 us against
                                   // 62 us for 4096-key items on 256 threads)
@@ -42,8 +45,7 @@ constexpr int32_t kChunk = 8192;  // 16 keys per thread (same-process A/B: 52 us
 constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
 constexpr int64_t kHist1 = 2048;    // 2048 bins, key bits [10, 21)
 constexpr int64_t kHist2 = 4096;    // 1024 bins, key bits [0, 10)
-constexpr int64_t kState = 5120;    // {prefix, mask, remaining, whole bucket}
-constexpr int64_t kDone = 5184;     // per-kernel counters of finished workgroups (4 words)
+constexpr int64_t kDone = 5184;     // finished workgroups of the count kernel
 constexpr int64_t kArrays = 5248;   // gt[M], eq[M], eqx[M], S[M+1]
 
 enum Mode : int32_t { kNormal = 0, kNone = 1, kAll = 2 };
@@ -65,6 +67,9 @@ __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
 __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // True in every thread of the workgroup that finishes last among the grid's
 // workgroups (counter `done`).  Each wave first waits until all its memory
@@ -75,9 +80,7 @@ __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
 __device__ bool last_workgroup(uint32_t* done, uint32_t* s_flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
-    *s_flag = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              gridDim.x - 1u;
+  if (threadIdx.x == 0) *s_flag = add_dev(done, 1u) == gridDim.x - 1u;
   __syncthreads();
   return *s_flag != 0u;
 }
@@ -119,205 +122,132 @@ __device__ __forceinline__ void load_keys(const float* row, int32_t i0, int32_t 
   }
 }
 
+// Bins of the levels below `levels` held by this thread, top bins first:
+// thread t holds bins [top - per, top) of a level, top = bins - per * t.
+struct HistRegs {
+  uint32_t h[3][kBinsPerThread];
+};
+__device__ __forceinline__ void load_hists(const uint32_t* ws, int levels, HistRegs* r) {
+#pragma unroll
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    const Level L = level_of(lvl);
+    const uint32_t per = L.bins / kThreads;
+    const uint32_t top = L.bins - per * threadIdx.x;
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b)
+      r->h[lvl][b] = (lvl < levels && b < per) ? ws[L.off + top - 1u - b] : 0u;
+  }
+}
+
+// The digits chosen by levels [0, levels): prefix and mask of the bucket that
+// holds the budget-th best key, how many keys of that bucket are still to be
+// kept, and whether the bucket is kept whole (later levels are then skipped).
+struct Thr {
+  uint32_t prefix, mask, remaining, whole;
+};
+// s_state holds one 4-word slot per level, so no slot is rewritten while
+// another thread may still read it.
+__device__ Thr resolve_levels(const HistRegs& r, int levels, uint32_t budget, uint32_t* s_scan,
+                              uint32_t (*s_state)[4]) {
+  Thr t{0u, 0u, budget, 0u};
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    if (lvl >= levels || t.whole) break;
+    const Level L = level_of(lvl);
+    const uint32_t per = L.bins / kThreads;
+    const uint32_t top = L.bins - per * (uint32_t)tid;
+    uint32_t c = 0u;
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) c += r.h[lvl][b];
+    uint32_t* st = s_state[lvl];
+    if (tid == 0) {  // kept if no bin crosses (cannot happen: the bucket holds >= remaining)
+      st[0] = t.prefix;
+      st[1] = t.mask;
+      st[2] = t.remaining;
+      st[3] = t.whole;
+    }
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
+    const uint32_t excl = incl - c;
+    if (excl < t.remaining && incl >= t.remaining) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) {
+        const uint32_t h = r.h[lvl][b];
+        if (b < per && acc < t.remaining && acc + h >= t.remaining) {
+          const uint32_t left = t.remaining - acc;
+          st[0] = t.prefix | ((top - 1u - b) << L.shift);
+          st[1] = t.mask | ((L.bins - 1u) << L.shift);
+          st[2] = left;
+          st[3] = (left == h) ? 1u : 0u;  // the bucket is kept whole
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();  // thread 0's write came before the scan's barriers, the crossing one's after
+    t = Thr{st[0], st[1], st[2], st[3]};
+  }
+  return t;
+}
+
+// Threshold key T and how many keys equal to T are kept.
+__device__ __forceinline__ void threshold_of(const GlobalArgs& a, const Thr& t, uint32_t* thr,
+                                             uint32_t* need_eq) {
+  if (a.mode == kAll) {
+    *thr = 0u;
+    *need_eq = 0xffffffffu;
+  } else {
+    *thr = t.prefix;
+    *need_eq = t.whole ? 0xffffffffu : t.remaining;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void global_init_kernel(GlobalArgs a) {
   const int64_t list = blockIdx.x;
   int32_t* out = a.kept_idx + list * a.kept_ld;
   for (int32_t j = threadIdx.x; j < a.prot; j += kThreads) out[j] = j;
   if (threadIdx.x == 0) a.kept_count[list] = a.prot;
-  if (list == 0) {
-    for (int32_t b = threadIdx.x; b < (int32_t)kArrays; b += kThreads)
-      st_dev(a.ws + b, (b == kState + 2) ? a.budget : 0u);  // remaining = B before level 0
-  }
-}
-
-// Resolves the digit of level lvl (run by one workgroup): walks the finished
-// histogram from the top bin down to the bin holding the remaining-th best key
-// among those matching the digits chosen so far, and stores the new state.
-__device__ void resolve_level(uint32_t* ws, int lvl, uint32_t prefix, uint32_t mask,
-                              uint32_t remaining, uint32_t* s_scan) {
-  const int tid = threadIdx.x;
-  const Level L = level_of(lvl);
-  const uint32_t* hist = ws + L.off;
-  const uint32_t per = L.bins / kThreads;             // bins per thread (<= 8), top first
-  const uint32_t top = L.bins - per * (uint32_t)tid;  // exclusive upper bin
-  uint32_t h[8];
-  uint32_t c = 0u;
-#pragma unroll
-  for (uint32_t b = 0; b < 8; ++b) {
-    h[b] = (b < per) ? ld_dev(hist + top - 1u - b) : 0u;
-    c += h[b];
-  }
-  uint32_t total;
-  const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
-  const uint32_t excl = incl - c;
-  if (excl < remaining && incl >= remaining) {
-    uint32_t acc = excl;
-#pragma unroll
-    for (uint32_t b = 0; b < 8; ++b) {
-      if (b < per && acc < remaining && acc + h[b] >= remaining) {
-        const uint32_t digit = top - 1u - b;
-        const uint32_t left = remaining - acc;
-        st_dev(ws + kState + 0, prefix | (digit << L.shift));
-        st_dev(ws + kState + 1, mask | ((L.bins - 1u) << L.shift));
-        st_dev(ws + kState + 2, left);
-        st_dev(ws + kState + 3, left == h[b] ? 1u : 0u);  // the bucket is kept whole
-      }
-      acc += h[b];
-    }
-  }
+  for (int64_t b = list * kThreads + threadIdx.x; b < kArrays; b += gridDim.x * kThreads)
+    st_dev(a.ws + b, 0u);
 }
 
 __global__ __launch_bounds__(kThreads) void global_hist_kernel(GlobalArgs a, int lvl) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_flag;
+  __shared__ uint32_t s_state[3][4];
   int64_t list;
   int32_t i0, i1;
   item_range(a, blockIdx.x, &list, &i0, &i1);
+  HistRegs r;
+  load_hists(a.ws, lvl, &r);
   uint32_t keys[kKeysPerThread];
-  load_keys(a.scores + list * a.ld, i0, i1, keys);  // in flight with the state loads
-  const uint32_t whole = ld_dev(a.ws + kState + 3);
-  const uint32_t prefix = ld_dev(a.ws + kState + 0), mask = ld_dev(a.ws + kState + 1);
-  if (whole) return;  // an earlier level took its bucket whole
+  load_keys(a.scores + list * a.ld, i0, i1, keys);  // in flight while the digits resolve
+  const Thr t = resolve_levels(r, lvl, a.budget, s_scan, s_state);
+  if (t.whole) return;  // an earlier level took its bucket whole
   const Level L = level_of(lvl);
   for (uint32_t b = threadIdx.x; b < L.bins; b += kThreads) s_hist[b] = 0u;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kKeysPerThread; ++u) {
     const uint32_t k = keys[u];
-    if (i0 + (int32_t)threadIdx.x + u * kThreads < i1 && (k & mask) == prefix)
+    if (i0 + (int32_t)threadIdx.x + u * kThreads < i1 && (k & t.mask) == t.prefix)
       atomicAdd(&s_hist[(k >> L.shift) & (L.bins - 1u)], 1u);
   }
   __syncthreads();
   for (uint32_t b = threadIdx.x; b < L.bins; b += kThreads) {
     const uint32_t h = s_hist[b];
-    if (h) __hip_atomic_fetch_add(a.ws + L.off + b, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (last_workgroup(a.ws + kDone + lvl, &s_flag))
-    resolve_level(a.ws, lvl, prefix, mask, ld_dev(a.ws + kState + 2), s_scan);
-}
-
-// Threshold key T and how many keys equal to T are kept.
-__device__ __forceinline__ void threshold(const GlobalArgs& a, uint32_t* thr, uint32_t* need_eq) {
-  if (a.mode == kAll) {
-    *thr = 0u;
-    *need_eq = 0xffffffffu;
-  } else {
-    *thr = ld_dev(a.ws + kState + 0);
-    *need_eq = ld_dev(a.ws + kState + 3) ? 0xffffffffu : ld_dev(a.ws + kState + 2);
+    if (h) add_dev(a.ws + L.off + b, h);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a) {
-  __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_flag;
-  uint32_t thr, need_eq;
-  threshold(a, &thr, &need_eq);
-  const int64_t f = blockIdx.x;
-  const int64_t M = a.num_lists * a.chunks;
-  uint32_t* gt_arr = a.ws + kArrays;
-  uint32_t* eq_arr = gt_arr + M;
-  uint32_t* eqx = gt_arr + 2 * M;
-  uint32_t* S = gt_arr + 3 * M;
-  int64_t list;
-  int32_t i0, i1;
-  item_range(a, f, &list, &i0, &i1);
-  uint32_t keys[kKeysPerThread];
-  load_keys(a.scores + list * a.ld, i0, i1, keys);
-  uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-  for (int u = 0; u < kKeysPerThread; ++u) {
-    const bool valid = i0 + (int32_t)threadIdx.x + u * kThreads < i1;
-    gt += (valid && keys[u] > thr) ? 1u : 0u;
-    eq += (valid && keys[u] == thr) ? 1u : 0u;
-  }
-  gt = block_sum<kThreads>(gt, s_scan);
-  eq = block_sum<kThreads>(eq, s_scan);
-  if (threadIdx.x == 0) {
-    st_dev(gt_arr + f, gt);
-    st_dev(eq_arr + f, eq);
-  }
-  if (M <= kDirectPrefixItems || !last_workgroup(a.ws + kDone + 3, &s_flag)) return;
-
-  // the last workgroup: scans in flat order and per-list counts
-  const int tid = threadIdx.x;
-  uint32_t carry = 0u;
-  for (int64_t base = 0; base < M; base += kThreads) {
-    const int64_t g = base + tid;
-    const uint32_t e = (g < M) ? ld_dev(eq_arr + g) : 0u;
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan<kThreads>(e, s_scan, &total);
-    if (g < M) st_dev(eqx + g, carry + incl - e);
-    carry += total;
-  }
-  __syncthreads();
-  carry = 0u;
-  for (int64_t base = 0; base < M; base += kThreads) {
-    const int64_t g = base + tid;
-    uint32_t k = 0u;
-    if (g < M) {
-      const uint32_t x = ld_dev(eqx + g);
-      const uint32_t room = (need_eq > x) ? need_eq - x : 0u;
-      k = ld_dev(gt_arr + g) + min(ld_dev(eq_arr + g), room);
-    }
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan<kThreads>(k, s_scan, &total);
-    if (g < M) st_dev(S + g, carry + incl - k);
-    carry += total;
-  }
-  if (tid == 0) st_dev(S + M, carry);
-  __syncthreads();
-  for (int64_t l = tid; l < a.num_lists; l += kThreads)
-    a.kept_count[l] = a.prot + (int32_t)(ld_dev(S + (l + 1) * a.chunks) - ld_dev(S + l * a.chunks));
-}
-
-__global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a) {
-  __shared__ uint32_t s_tile[2 * kWaves];
-  uint32_t thr, need_eq;
-  threshold(a, &thr, &need_eq);
-  const int64_t f = blockIdx.x;
-  const int64_t M = a.num_lists * a.chunks;
-  uint32_t* eqx = a.ws + kArrays + 2 * M;
-  uint32_t* S = a.ws + kArrays + 3 * M;
-  int64_t list;
-  int32_t i0, i1;
-  item_range(a, f, &list, &i0, &i1);
-  uint32_t eq0, offset;  // keys == T before item f (flat order); kept before f in its list
-  if (M <= kDirectPrefixItems) {
-    // sums over the items before f: all of them for eq, those of f's list for gt and eq
-    uint32_t* gt_arr = a.ws + kArrays;
-    uint32_t* eq_arr = gt_arr + M;
-    const int64_t ls = list * a.chunks;
-    uint32_t e_all = 0u, gt_in = 0u, e_in = 0u;
-    for (int64_t g = threadIdx.x; g < f; g += kThreads) {
-      const uint32_t e = ld_dev(eq_arr + g);
-      e_all += e;
-      if (g >= ls) {
-        gt_in += ld_dev(gt_arr + g);
-        e_in += e;
-      }
-    }
-    eq0 = block_sum<kThreads>(e_all, s_tile);
-    gt_in = block_sum<kThreads>(gt_in, s_tile);
-    e_in = block_sum<kThreads>(e_in, s_tile);
-    // keys == T are kept in flat order, so the run [ls, f) keeps the first
-    // (need_eq - eq before ls) of its e_in, clamped to [0, e_in]
-    const uint32_t eq_ls = eq0 - e_in;
-    const uint32_t room_ls = (need_eq > eq_ls) ? need_eq - eq_ls : 0u;
-    offset = gt_in + min(e_in, room_ls);
-    if (f - ls == a.chunks - 1 && threadIdx.x == 0) {  // last item of its list
-      const uint32_t room_f = (need_eq > eq0) ? need_eq - eq0 : 0u;
-      a.kept_count[list] =
-          a.prot + (int32_t)(offset + ld_dev(gt_arr + f) + min(ld_dev(eq_arr + f), room_f));
-    }
-  } else {
-    eq0 = ld_dev(eqx + f);
-    offset = ld_dev(S + f) - ld_dev(S + list * a.chunks);
-  }
+// Emits the kept indices of an item whose keys are in registers: keys > thr,
+// and keys == thr while fewer than need_eq of them come before in flat order
+// (eq0 of them lie in earlier items).  `out` points at the item's first slot.
+__device__ __forceinline__ void emit_item(const uint32_t* keys, int32_t i0, int32_t i1,
+                                          uint32_t thr, uint32_t need_eq, uint32_t eq0,
+                                          int32_t* out, uint32_t* s_tile) {
   const uint32_t taken0 = min(eq0, need_eq);
-  int32_t* out = a.kept_idx + list * a.kept_ld + a.prot + offset;
-  uint32_t keys[kKeysPerThread];
-  load_keys(a.scores + list * a.ld, i0, i1, keys);
   const int wave = threadIdx.x / kWave;
   uint32_t carry_gt = 0u, carry_eq = 0u;
 #pragma unroll
@@ -352,6 +282,135 @@ __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a) {
   }
 }
 
+__device__ __forceinline__ void count_item(const uint32_t* keys, int32_t i0, int32_t i1,
+                                           uint32_t thr, uint32_t* gt, uint32_t* eq) {
+  uint32_t g = 0u, e = 0u;
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const bool valid = i0 + (int32_t)threadIdx.x + u * kThreads < i1;
+    g += (valid && keys[u] > thr) ? 1u : 0u;
+    e += (valid && keys[u] == thr) ? 1u : 0u;
+  }
+  *gt = g;
+  *eq = e;
+}
+
+// Per-item counts of keys > T and == T.  With more than kDirectPrefixItems
+// items, the last workgroup then scans them in flat order into per-item
+// offsets and writes the per-list counts.
+__global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a, int levels) {
+  __shared__ uint32_t s_scan[kWaves];
+  __shared__ uint32_t s_state[3][4];
+  __shared__ uint32_t s_flag;
+  const int64_t f = blockIdx.x;
+  const int64_t M = a.num_lists * a.chunks;
+  uint32_t* gt_arr = a.ws + kArrays;
+  uint32_t* eq_arr = gt_arr + M;
+  uint32_t* eqx = gt_arr + 2 * M;
+  uint32_t* S = gt_arr + 3 * M;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  HistRegs r;
+  load_hists(a.ws, levels, &r);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
+  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
+  uint32_t thr, need_eq;
+  threshold_of(a, t, &thr, &need_eq);
+  uint32_t gt, eq;
+  count_item(keys, i0, i1, thr, &gt, &eq);
+  gt = block_sum<kThreads>(gt, s_scan);
+  eq = block_sum<kThreads>(eq, s_scan);
+  if (threadIdx.x == 0) {
+    st_dev(gt_arr + f, gt);
+    st_dev(eq_arr + f, eq);
+  }
+  if (M <= kDirectPrefixItems || !last_workgroup(a.ws + kDone, &s_flag)) return;
+
+  // the last workgroup: scans in flat order and per-list counts
+  const int tid = threadIdx.x;
+  uint32_t carry = 0u;
+  for (int64_t base = 0; base < M; base += kThreads) {
+    const int64_t g = base + tid;
+    const uint32_t e = (g < M) ? ld_dev(eq_arr + g) : 0u;
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan<kThreads>(e, s_scan, &total);
+    if (g < M) st_dev(eqx + g, carry + incl - e);
+    carry += total;
+  }
+  __syncthreads();
+  carry = 0u;
+  for (int64_t base = 0; base < M; base += kThreads) {
+    const int64_t g = base + tid;
+    uint32_t k = 0u;
+    if (g < M) {
+      const uint32_t x = ld_dev(eqx + g);
+      const uint32_t room = (need_eq > x) ? need_eq - x : 0u;
+      k = ld_dev(gt_arr + g) + min(ld_dev(eq_arr + g), room);
+    }
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan<kThreads>(k, s_scan, &total);
+    if (g < M) st_dev(S + g, carry + incl - k);
+    carry += total;
+  }
+  if (tid == 0) st_dev(S + M, carry);
+  __syncthreads();
+  for (int64_t l = tid; l < a.num_lists; l += kThreads)
+    a.kept_count[l] = a.prot + (int32_t)(ld_dev(S + (l + 1) * a.chunks) - ld_dev(S + l * a.chunks));
+}
+
+__global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int levels) {
+  __shared__ uint32_t s_scan[kWaves];
+  __shared__ uint32_t s_tile[2 * kWaves];
+  __shared__ uint32_t s_state[3][4];
+  const int64_t f = blockIdx.x;
+  const int64_t M = a.num_lists * a.chunks;
+  const uint32_t* eqx = a.ws + kArrays + 2 * M;
+  const uint32_t* S = a.ws + kArrays + 3 * M;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  HistRegs r;
+  load_hists(a.ws, levels, &r);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
+  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
+  uint32_t thr, need_eq;
+  threshold_of(a, t, &thr, &need_eq);
+  // written by the count kernel's atomics: plain loads see them after the kernel boundary
+  uint32_t eq0, offset;
+  if (M <= kDirectPrefixItems) {
+    const uint32_t* gt_arr = a.ws + kArrays;
+    const uint32_t* eq_arr = gt_arr + M;
+    const int64_t ls = list * a.chunks;
+    uint32_t e_all = 0u, gt_in = 0u, e_in = 0u;
+    for (int64_t g = threadIdx.x; g < f; g += kThreads) {
+      const uint32_t e = eq_arr[g];
+      e_all += e;
+      if (g >= ls) {
+        gt_in += gt_arr[g];
+        e_in += e;
+      }
+    }
+    eq0 = block_sum<kThreads>(e_all, s_scan);
+    gt_in = block_sum<kThreads>(gt_in, s_scan);
+    e_in = block_sum<kThreads>(e_in, s_scan);
+    const uint32_t eq_ls = eq0 - e_in;
+    const uint32_t room_ls = (need_eq > eq_ls) ? need_eq - eq_ls : 0u;
+    offset = gt_in + min(e_in, room_ls);
+    if (f - ls == a.chunks - 1 && threadIdx.x == 0) {  // last item of its list
+      const uint32_t room_f = (need_eq > eq0) ? need_eq - eq0 : 0u;
+      a.kept_count[list] = a.prot + (int32_t)(offset + gt_arr[f] + min(eq_arr[f], room_f));
+    }
+  } else {
+    eq0 = eqx[f];
+    offset = S[f] - S[list * a.chunks];
+  }
+  emit_item(keys, i0, i1, thr, need_eq, eq0, a.kept_idx + list * a.kept_ld + a.prot + offset,
+            s_tile);
+}
+
 }  // namespace
 
 size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot) {
@@ -383,20 +442,20 @@ hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kep
   a.kept_ld = kept_ld;
   a.kept_count = kept_count;
 
+  const int64_t M = num_lists * chunks;
   hipLaunchKernelGGL(global_init_kernel, dim3((unsigned)num_lists), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned items = (unsigned)(num_lists * chunks);
+  const unsigned items = (unsigned)M;
   if (items == 0 || a.mode == kNone) return hipSuccess;  // the prompts are the whole result
-  if (a.mode == kNormal) {
-    for (int lvl = 0; lvl < 3; ++lvl) {
-      hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+  const int levels = (a.mode == kNormal) ? 3 : 0;
+  for (int lvl = 0; lvl < levels; ++lvl) {
+    hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(global_count_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(global_count_kernel, dim3(items), dim3(kThreads), 0, stream, a, levels);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(global_emit_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(global_emit_kernel, dim3(items), dim3(kThreads), 0, stream, a, levels);
   return hipGetLastError();
 }
 

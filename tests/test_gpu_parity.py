@@ -158,29 +158,43 @@ def test_compact_contig(D, shared):
     assert int(err.item()) == 0
 
 
-def test_compact_variable_counts():
-    say("compact contig with kept_count")
-    groups, H, n, D = 2, 4, 5000, 256
-    lists = groups * H
-    rng = np.random.default_rng(9)
-    counts = np.array([0, 1, 4999, 5000, 17, 2500, 4096, 4097], np.int32)
-    kept = np.zeros((lists, n), np.int32)
-    for l in range(lists):
+@pytest.mark.parametrize("groups,H,n,D,shared,bad", [
+    (2, 4, 5000, 256, False, False),   # teams walking several chunks, lists of 0..K rows
+    (3, 4, 3000, 64, True, False),     # shared index lists, row width known at run time
+    (1, 6, 2000, 128, False, True),    # counts outside [0, K]: clamped and counted
+    (300, 4, 200, 128, False, False),  # many short lists
+    (256, 4, 96, 256, False, True),    # many lists, bad counts
+])
+def test_compact_variable_counts(groups, H, n, D, shared, bad):
+    say(f"compact contig with kept_count groups={groups} H={H} n={n} D={D} shared={shared} bad={bad}")
+    ipg = 1 if shared else H
+    lists, idx_lists = groups * H, groups * ipg
+    rng = np.random.default_rng(groups * n + D)
+    counts = rng.integers(0, n + 1, idx_lists).astype(np.int32)
+    counts[:4] = [0, 1, n, n - 1][:min(4, idx_lists)]
+    kept = np.zeros((idx_lists, n), np.int32)
+    for l in range(idx_lists):
         kept[l, :counts[l]] = np.sort(rng.choice(n, counts[l], replace=False))
+    want_counts = counts.copy()
+    if bad:
+        counts[0], counts[-1] = -5, n + 3
+        want_counts[0], want_counts[-1] = 0, n
+        kept[-1] = np.arange(n)
     ks, vs = rand_bits((lists, n, D), 5), rand_bits((lists, n, D), 6)
     k_dst = torch.zeros((lists, n, D), dtype=torch.bfloat16, device=DEV)
     v_dst = torch.zeros_like(k_dst)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     B.kvevict_compact(B.contig_desc(D, H, n), bf16_from_bits(ks), bf16_from_bits(vs),
                       B.contig_desc(D, H, n), k_dst, v_dst, torch.from_numpy(kept).to(DEV), n,
-                      torch.from_numpy(counts).to(DEV), n, groups, H, err)
+                      torch.from_numpy(counts).to(DEV), n, groups, ipg, err)
     torch.cuda.synchronize()
     kd = np.zeros((lists, n, D), np.uint16)
     vd = np.zeros_like(kd)
     oracle.compact({"list_stride": n * D}, ks, vs, {"list_stride": n * D}, kd, vd, kept, n, D, H,
-                   0, groups, ipg=H, kept_count=counts)
+                   0, groups, ipg=ipg, kept_count=want_counts)
     assert np.array_equal(u16(k_dst), kd) and np.array_equal(u16(v_dst), vd)
-    assert int(err.item()) == 0
+    # one error per index list whose count is out of range
+    assert int(err.item()) == (2 if bad else 0)
 
 
 @pytest.mark.parametrize("shared", [False, True])
