@@ -4,8 +4,14 @@
 // the lower position).
 //
 // radix_select finds the threshold key T and how many keys equal to T are
-// kept with an 8-bit-digit radix select (at most 4 histogram passes, stopping
-// as soon as the chosen bucket is taken whole).  emit_kept then visits the kept
+// kept with a radix select that stops as soon as the chosen bucket is taken
+// whole: 8-bit digits (at most 4 passes) for NT < 1024, and 11/11/10-bit
+// digits (at most 3 passes) for the 1024-thread workgroups of long lists.  The
+// top digit of a float key is its sign and exponent, which few values share:
+// the wider digit spreads a long list's LDS atomics over more bins (64 lists
+// of 32,512 keys: 57 us against 69 us).  The short lists of 256-thread
+// workgroups lose with it (more bins to clear and scan per key), so they keep
+// 8-bit digits.  emit_kept then visits the kept
 // keys in increasing position with wave ballots and mbcnt prefix counts: a
 // kept key's output slot is the number of kept keys before it, so the keys
 // equal to T that are kept are the lowest positions.
@@ -17,10 +23,22 @@ namespace kvevict {
 
 constexpr int kSelectThreads = 256;
 
+// Digit width of radix pass p for a workgroup of NT threads.
+template <int NT>
+__host__ __device__ constexpr int select_digit_bits(int p) {
+  return NT >= 1024 ? (p < 2 ? 11 : 10) : 8;
+}
+template <int NT>
+__host__ __device__ constexpr int select_passes() {
+  return NT >= 1024 ? 3 : 4;
+}
+
 template <int NT = kSelectThreads>
 struct SelectShared {
-  static_assert(NT % kWave == 0 && NT >= 256, "one thread per histogram bin");
-  uint32_t hist[256];
+  static_assert(NT % kWave == 0 && NT >= 256, "at least one histogram bin per thread");
+  static constexpr int kBins = 1 << select_digit_bits<NT>(0);
+  static_assert(kBins % NT == 0 && kBins / NT <= 2, "one or two bins per thread");
+  uint32_t hist[kBins];
   uint32_t scan[NT / kWave];
   uint32_t pick[3];
   uint32_t tile[2 * (NT / kWave)];
@@ -34,31 +52,50 @@ __device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared<N
   const int tid = threadIdx.x;
   uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)kk;
   bool whole_bucket = false;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) sh.hist[tid] = 0u;
+  int shift = 32;
+#pragma unroll
+  for (int pass = 0; pass < select_passes<NT>(); ++pass) {
+    const int bits = select_digit_bits<NT>(pass);
+    const uint32_t bins = 1u << bits;
+    shift -= bits;
+    for (uint32_t b = tid; b < bins; b += NT) sh.hist[b] = 0u;
     __syncthreads();
     for (int32_t i = tid; i < m; i += NT) {
       const uint32_t k = key_at(i);
-      if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+      if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (bins - 1u)], 1u);
     }
     __syncthreads();
-    // thread t < 256 holds bin 255 - t (the others count 0), so the inclusive scan
-    // counts keys in bins >= 255 - t
-    const uint32_t c = tid < 256 ? sh.hist[255 - tid] : 0u;
+    // thread t holds bins [top - per, top), top = bins - per*t, highest first, so
+    // the inclusive scan counts the keys in bins >= top - per
+    const uint32_t per = bins / NT;
+    const uint32_t top = bins - per * (uint32_t)tid;
+    uint32_t h[2], c = 0u;
+#pragma unroll
+    for (uint32_t b = 0; b < 2; ++b) {
+      h[b] = (b < per) ? sh.hist[top - 1u - b] : 0u;
+      c += h[b];
+    }
     uint32_t total;
     const uint32_t incl = block_inclusive_scan<NT>(c, sh.scan, &total);
     const uint32_t excl = incl - c;
     if (excl < remaining && incl >= remaining) {
-      sh.pick[0] = 255u - (uint32_t)tid;
-      sh.pick[1] = remaining - excl;
-      sh.pick[2] = c;
+      uint32_t acc = excl;
+#pragma unroll
+      for (uint32_t b = 0; b < 2; ++b) {
+        if (b < per && acc < remaining && acc + h[b] >= remaining) {
+          sh.pick[0] = top - 1u - b;
+          sh.pick[1] = remaining - acc;
+          sh.pick[2] = h[b];
+        }
+        acc += h[b];
+      }
     }
     __syncthreads();
     const uint32_t digit = sh.pick[0];
     const uint32_t cnt = sh.pick[2];
     remaining = sh.pick[1];
     prefix |= digit << shift;
-    mask |= 0xffu << shift;
+    mask |= (bins - 1u) << shift;
     __syncthreads();
     if (remaining == cnt) {  // the whole bucket is kept: keep every key >= prefix
       whole_bucket = true;

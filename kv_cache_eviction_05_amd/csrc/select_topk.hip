@@ -19,7 +19,7 @@ namespace {
 constexpr int kThreads = kSelectThreads;
 constexpr int kBigThreads = 1024;           // workgroup for lists longer than kMaxLdsKeys
 constexpr int32_t kMaxLdsKeys = 15360;      // 60 KiB of keys (+ ~1 KiB static LDS)
-constexpr int32_t kMaxBigLdsKeys = 38912;   // 152 KiB of keys, within gfx950's 160 KiB
+constexpr int32_t kMaxBigLdsKeys = 38848;   // 151.75 KiB of keys + the 8.2 KiB select state: 160 KiB
 
 struct TopkArgs {
   int32_t* kept_idx;
