@@ -89,14 +89,36 @@ def make_scores(kind, lists, n, seed):
     raise ValueError(kind)
 
 
+def bucket_scores(lists, n, prot, hi, mid, seed):
+    """Candidates [prot, n) of every list: `hi` of them at 2 + 2^-7 and `mid` at 2.0, which
+    share the top radix digit and differ in the next one, the rest at -1; the prompt at 0.5.
+    Keeping exactly `hi` per list (or in all) takes a whole bucket: at the first digit when
+    mid = 0, at the second otherwise, so the selects stop early."""
+    rng = np.random.default_rng(seed)
+    s = np.full((lists, n), -1.0, np.float32)
+    s[:, :prot] = 0.5
+    for l in range(lists):
+        pos = prot + rng.permutation(n - prot)
+        s[l, pos[:hi]] = 2.0078125
+        s[l, pos[hi:hi + mid]] = 2.0
+    return s
+
+
 @pytest.mark.parametrize("lists,n,K,prot,kind", [
     (37, 1088, 1024, 128, "uniform"),
     (37, 1088, 1024, 128, "ties"),
     (9, 3136, 3072, 557, "uniform"),
     (7, 2112, 2048, 1024, "special"),
     (5, 2000, 700, 3, "normal"),
-    (3, 20000, 15000, 100, "uniform"),   # more candidates than LDS holds: global-memory path
+    (3, 20000, 15000, 100, "uniform"),   # a 1024-thread workgroup, keys in dynamic LDS
     (3, 20000, 9000, 0, "ties"),
+    (2, 38948, 30000, 100, "uniform"),   # 38,848 candidates: the most that LDS holds
+    (2, 38949, 30000, 100, "ties"),      # one more: keys read from global memory on every pass
+    (2, 60000, 1000, 5, "normal"),
+    (9, 1088, 1024, 128, "whole0"),      # the kept keys fill the top bucket of the first digit
+    (9, 1088, 1024, 128, "whole1"),      # ... of the second digit
+    (3, 20000, 15000, 100, "whole0"),    # the same with 11-bit digits
+    (3, 20000, 15000, 100, "whole1"),
     (4, 300, 300, 10, "uniform"),        # K = n: identity
     (4, 300, 50, 50, "uniform"),         # K = prot: prompt only
     (4, 300, 120, 0, "constant"),        # all equal: the oldest K
@@ -106,7 +128,10 @@ def make_scores(kind, lists, n, seed):
 ])
 def test_select_topk(lists, n, K, prot, kind):
     say(f"select_topk lists={lists} n={n} K={K} prot={prot} kind={kind}")
-    s = make_scores(kind, lists, n, seed=n + K)
+    if kind.startswith("whole"):
+        s = bucket_scores(lists, n, prot, K - prot, 0 if kind == "whole0" else 50, seed=n + K)
+    else:
+        s = make_scores(kind, lists, n, seed=n + K)
     ld, kept_ld = n + 3, K + 5
     s_pad = np.full((lists, ld), 123.0, np.float32)
     s_pad[:, :n] = s
@@ -275,10 +300,17 @@ def test_compact_rejects_out_of_range_rows():
     (16, 4096, 256, 0.1, "constant"),    # every candidate tied
     (1, 1, 0, 1.0, "uniform"),
     (8200, 100, 10, 0.3, "ties"),        # more items than the direct-prefix limit: scanned once
+    (6, 20100, 100, 0.3, "whole0"),      # B fills the top bucket of the first digit
+    (6, 20100, 100, 0.3, "whole1"),      # ... of the second digit
+    (8200, 100, 10, 0.3, "whole1"),      # the same, scanned once
 ])
 def test_select_global(lists, n, prot, p, kind):
     say(f"select_global lists={lists} n={n} prot={prot} p={p} kind={kind}")
-    s = make_scores(kind, lists, n, seed=lists * n)
+    if kind.startswith("whole"):
+        per = int(np.round(p * (n - prot)))
+        s = bucket_scores(lists, n, prot, per, 0 if kind == "whole0" else 50, seed=lists * n)
+    else:
+        s = make_scores(kind, lists, n, seed=lists * n)
     ld, kept_ld = n + 1, n + 2
     s_pad = np.full((lists, ld), 9.0, np.float32)
     s_pad[:, :n] = s
