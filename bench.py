@@ -12,7 +12,10 @@ Timing: W untimed rounds, then exactly K rounds between two synchronisations;
 HIP events on the launch stream bracket every kernel launch of the round, so
 each step of the round gets its own average duration.  The roofline entry
 prices the dominant kernel (the K/V gather) at its algorithmic bytes: the
-kept K and V rows, each read once and written once.
+kept K and V rows, each read once and written once.  Workloads whose round
+takes under 1 ms and leaves its inputs intact are also replayed from a HIP
+graph of ten rounds (graph_ms_per_round): the device time without the host
+launch path.
 """
 
 from __future__ import annotations
@@ -199,6 +202,27 @@ def time_workload(torch, rounds, cfg, steps, warmup):
     return out
 
 
+GRAPH_ROUNDS = 10  # rounds recorded per HIP graph
+
+
+def graph_replay_ms(torch, rounds, st, steps):
+    """Round time with the rounds replayed from a HIP graph of GRAPH_ROUNDS rounds (round
+    ids 0..GRAPH_ROUNDS-1): the same launches without the host launch path, which rounds
+    of tens of microseconds are bound by."""
+    g = rounds.capture_rounds(st, range(GRAPH_ROUNDS))
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // GRAPH_ROUNDS)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * GRAPH_ROUNDS)
+
+
 def traffic_for(kv_bytes):
     """Measured HBM bytes per launch of the gather, if the counters match this source."""
     try:
@@ -337,6 +361,11 @@ def main():
             "applied_rounds": r["applied_rounds"],
             "bad_rows": r["errors"],
         }
+        if r["ms_per_step"] < 1.0 and not (cfg.inplace or cfg.page_draw or cfg.rounds > 1):
+            # latency-bound rounds: also replayed from a HIP graph
+            g_ms = graph_replay_ms(torch, rounds, r["state"], max(steps, 10 * GRAPH_ROUNDS))
+            entry["graph_ms_per_round"] = g_ms
+            entry["graph_rounds_per_s"] = 1e3 / g_ms
         if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
         if cfg.select == "layers":

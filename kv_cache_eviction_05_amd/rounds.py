@@ -303,6 +303,32 @@ def run_round(st: RoundState, round_id: int = 0, stream=None):
     st.applied_rounds += 1
 
 
+def capture_rounds(st: RoundState, round_ids=(0,)) -> "torch.cuda.CUDAGraph":
+    """Out-of-place rounds, one per round id, recorded in order as one HIP graph.
+
+    Replaying the graph reruns the rounds' launches with the arguments they had
+    at capture (round ids, budget and buffers included) without the host launch
+    path, which dominates rounds of a few microseconds; several rounds per graph
+    spread the graph's own launch over them.  The rounds run once eagerly first,
+    so any one-time set-up of the library happens outside the capture.
+    In-place, page-draw and repeated rounds change their own inputs, so replays
+    would not repeat the same rounds; they are not captured.
+    """
+    c = st.cfg
+    if c.inplace or c.page_draw or c.rounds > 1:
+        raise ValueError(f"{c.name}: only single out-of-place rounds are captured")
+    for rid in round_ids:
+        for _, fn in phases(c):
+            fn(st, rid)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for rid in round_ids:
+            for _, fn in phases(c):
+                fn(st, rid)
+    return g
+
+
 # --- repeated rounds (persistent budget K + recent buffer r) ------------------------
 
 def append_tokens(st: RoundState, round_id: int):

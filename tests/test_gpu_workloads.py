@@ -523,3 +523,54 @@ def test_longgen_full_size_two_rounds_sampled(base):
         rounds.swap(st)
     del st
     free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "global", "paged_shared"])
+def test_graph_replay_matches_eager(name):
+    """A round captured as a HIP graph gives the eager round's outputs on every replay,
+    with eager work (clearing every output) and synchronisations between the replays."""
+    say(f"graph replay {name}")
+    cfg = configs.ALL[name]
+    st = rounds.make_state(cfg, DEV)
+
+    def outputs():
+        outs = [st.kept, st.k_dst, st.v_dst, st.errors]
+        return outs + ([st.kept_count] if st.kept_count is not None else [])
+
+    def clear():
+        st.kept.fill_(-1)
+        st.k_dst.zero_()
+        st.v_dst.zero_()
+        st.scores.fill_(-5.0)
+        if st.kept_count is not None:
+            st.kept_count.fill_(-1)
+
+    clear()
+    rounds.run_round(st, 0)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs()]
+    assert int(st.errors.item()) == 0
+    g = rounds.capture_rounds(st, [0])
+    for rep in range(3):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outputs(), want):
+            assert torch.equal(got, ref), (name, rep)
+    # several rounds in one graph: the outputs are the last round's
+    clear()
+    rounds.run_round(st, 2)
+    torch.cuda.synchronize()
+    want2 = [t.clone() for t in outputs()]
+    g2 = rounds.capture_rounds(st, [1, 2])
+    for rep in range(2):
+        clear()
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outputs(), want2):
+            assert torch.equal(got, ref), (name, "two rounds", rep)
+    del g, g2, st, want, want2
+    gc.collect()
+    torch.cuda.empty_cache()
