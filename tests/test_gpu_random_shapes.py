@@ -1,9 +1,11 @@
-"""GPU parity on seeded random shapes: the selects, the gathers and the one-launch round.
+"""GPU parity on seeded random shapes: scorers, selects, gathers and the fused rounds.
 
 Each case draws its shape from a seeded generator (list counts, lengths, prompt
 lengths, budgets, head widths, layouts, score distributions), runs the HIP
 library through the C ABI and compares with the CPU oracle on the same inputs:
-bit-exact for kept indices, counts and moved bytes.  The fixed-shape tests pin
+bit-exact for random scores, kept indices, counts, page tables and moved bytes;
+within a relative 1e-5 (weighted) or two fp32 ulps (KeyDiff) for the binary64
+scorers.  The fixed-shape tests pin
 the boundaries one by one; these sweep the combinations between them.
 """
 
@@ -13,8 +15,10 @@ import torch
 
 import oracle
 from kv_cache_eviction_05_amd import binding as B
-from test_gpu_parity import (bf16_from_bits, check_inplace, make_scores, make_store, rand_bits,
-                             say, to_np, u16)
+from kv_cache_eviction_05_amd.configs import gdn_windows
+from test_gpu_parity import (assert_keydiff_close, assert_weighted_close, bf16_from_bits,
+                             check_inplace, keep_sets, make_scores, make_store, rand_bits,
+                             rand_keys, say, to_np, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -174,3 +178,172 @@ def test_random_evict_random_inplace(case):
     assert np.array_equal(g[:, :K], kept)
     assert np.all(g[:, K:] == -9)
     check_inplace(layout, ks, vs, k, v, kept, None, groups, H, ipg, pt, ps, n, K, D, freed, fcount)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_score_random(case):
+    rng = case_rng(case, 6)
+    R, L, H = (int(x) for x in rng.integers(1, 5, 3))
+    n = int(rng.integers(1, 5000))
+    prot = int(rng.integers(0, n + 1)) if rng.random() < 0.8 else 0
+    shared, pad = bool(rng.random() < 0.3), int(rng.integers(0, 9))
+    seed, rnd = int(rng.integers(0, 2**64, dtype=np.uint64)), int(rng.integers(0, 2**32))
+    lists = R * L * (1 if shared else H)
+    say(f"random score_random case={case} R={R} L={L} H={H} n={n} prot={prot} shared={shared}")
+    s = torch.full((lists, n + pad), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_random(s, n + pad, R, L, H, n, prot, seed, rnd, shared)
+    torch.cuda.synchronize()
+    got = to_np(s)
+    assert np.array_equal(got[:, :n], oracle.score_random(L, H, n, prot, seed, rnd, shared, 0, lists))
+    assert np.all(np.isnan(got[:, n:]))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_score_weighted(case):
+    rng = case_rng(case, 7)
+    L = int(rng.integers(1, 24))
+    G = L * int(rng.integers(1, 5))
+    H, Hg = int(rng.integers(1, 7)), int(rng.integers(1, 100))
+    width = int(rng.integers(1, 8))
+    n = int(rng.integers(1, 700))
+    prot = int(rng.integers(0, n + 1)) if rng.random() < 0.7 else 0
+    say(f"random score_weighted case={case} G={G} L={L} H={H} Hg={Hg} width={width} n={n} "
+        f"prot={prot}")
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((G, n, Hg))))).astype(np.float32)
+    vnorm = np.exp(rng.standard_normal((G, n, Hg))).astype(np.float32)
+    w = rng.standard_normal((L, H, width, Hg)).astype(np.float32)
+    begins, counts = gdn_windows(L, G, width)
+    s = torch.full((L * H, n + 1), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_weighted(s, n + 1, torch.from_numpy(beta).to(DEV),
+                             torch.from_numpy(vnorm).to(DEV), n * Hg, Hg, 1,
+                             torch.from_numpy(w).to(DEV), width, begins, counts, L, H, G, Hg, n,
+                             prot)
+    torch.cuda.synchronize()
+    got = to_np(s)
+    assert np.all(np.isnan(got[:, n:]))
+    assert_weighted_close(got[:, :n], oracle.score_weighted(beta, vnorm, w, begins, counts, prot),
+                          prot)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_score_keydiff(case):
+    rng = case_rng(case, 8)
+    groups, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    D = int(rng.choice([8, 16, 32, 64, 128, 256, 512]))
+    n = int(rng.integers(1, 3000))
+    cap = n + int(rng.integers(0, 20))
+    prot = int(rng.integers(0, n + 1)) if rng.random() < 0.7 else 0
+    lists = groups * H
+    say(f"random score_keydiff case={case} groups={groups} H={H} D={D} n={n} cap={cap} prot={prot}")
+    keys = rand_keys((lists, cap, D), seed=700 + case)
+    s = torch.full((lists, n + 1), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_keydiff(s, n + 1, B.contig_desc(D, H, cap), bf16_from_bits(keys), groups, n,
+                            prot)
+    torch.cuda.synchronize()
+    got = to_np(s)
+    assert np.all(np.isnan(got[:, n:]))
+    assert_keydiff_close(got[:, :n], oracle.score_keydiff(np.ascontiguousarray(keys[:, :n]), prot))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_select_topk_layers(case):
+    rng = case_rng(case, 9)
+    R, L, H = int(rng.integers(1, 4)), int(rng.integers(1, 17)), int(rng.integers(1, 5))
+    n = int(rng.integers(1, 3000)) if case < 6 else int(rng.integers(15400, 30000))
+    prot = int(rng.integers(0, n + 1)) if rng.random() < 0.7 else 0
+    kind = str(rng.choice(KINDS))
+    lists = R * L * H
+    budget = [int(x) for x in rng.integers(0, n - prot + 1, L)]
+    say(f"random select_topk_layers case={case} R={R} L={L} H={H} n={n} prot={prot} kind={kind}")
+    s = make_scores(kind, lists, n, seed=900 + case)
+    kept = torch.full((lists, n + 1), -3, dtype=torch.int32, device=DEV)
+    counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    B.kvevict_select_topk_layers(kept, n + 1, counts, torch.from_numpy(s).to(DEV), n, R * L, L, H,
+                                 n, prot, budget)
+    torch.cuda.synchronize()
+    got, got_c = to_np(kept), to_np(counts)
+    for lst in range(lists):
+        K = prot + budget[(lst // H) % L]
+        assert got_c[lst] == K
+        assert np.array_equal(got[lst, :K], oracle.select_topk(s[lst:lst + 1], K, prot)[0]), lst
+        assert np.all(got[lst, K:] == -3)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_reduce_max_heads(case):
+    rng = case_rng(case, 10)
+    G, H, n = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.integers(1, 5000))
+    pad = int(rng.integers(0, 5))
+    say(f"random reduce_max_heads case={case} G={G} H={H} n={n}")
+    s = make_scores(str(rng.choice(KINDS)), G * H, n, seed=1100 + case)
+    s_pad = np.full((G * H, n + pad), 3.0, np.float32)
+    s_pad[:, :n] = s
+    out = torch.full((G, n + 1), 5.0, dtype=torch.float32, device=DEV)
+    B.kvevict_reduce_max_heads(out, n + 1, torch.from_numpy(s_pad).to(DEV), n + pad, G, H, n)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    assert np.array_equal(got[:, :n].view(np.uint32), oracle.shared_max_scores(s, H).view(np.uint32))
+    assert np.all(got[:, n:] == 5.0)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_compact_inplace(case):
+    rng = case_rng(case, 11)
+    ps = 16
+    layout = "paged" if rng.random() < 0.5 else "contig"
+    groups, H = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    D = int(rng.choice([8, 24, 40, 64, 128, 256]))
+    n = int(rng.integers(1, 1200))
+    prot, K = draw_prot_k(rng, n)
+    shared, variable = bool(rng.random() < 0.3), bool(rng.random() < 0.5)
+    ipg = 1 if shared else H
+    say(f"random compact_inplace case={case} {layout} groups={groups} H={H} D={D} n={n} K={K} "
+        f"prot={prot} shared={shared} variable={variable}")
+    kept, counts = keep_sets(groups * ipg, n, K, prot, seed=1200 + case, variable=variable)
+    desc, pt, ks, vs, k, v = make_store(layout, groups, H, D, n, ps, seed=60 + case)
+    freed = torch.full((groups * (n // ps + 1) + 1,), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_compact_inplace(desc, k, v, torch.from_numpy(kept).to(DEV), K,
+                              torch.from_numpy(counts).to(DEV) if variable else None, K, n,
+                              groups, ipg, freed, fcount, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_inplace(layout, ks, vs, k, v, kept, counts if variable else None, groups, H, ipg, pt, ps,
+                  n, K, D, freed, fcount)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_evict_pages_random(case):
+    rng = case_rng(case, 12)
+    ps = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    R, L = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    P = int(rng.integers(1, min(300, 4000 // ps) + 1))
+    n = P * ps
+    Kp = int(rng.integers(0, P + 1))
+    K = Kp * ps
+    prot = int(rng.integers(0, K + 1)) if rng.random() < 0.7 else 0
+    seed, rnd = int(rng.integers(0, 2**63)), int(rng.integers(0, 2**31))
+    groups = R * L
+    say(f"random evict_pages_random case={case} R={R} L={L} ps={ps} n={n} K={K} prot={prot}")
+    pt_ld = P + int(rng.integers(0, 4))
+    pool = groups * P + 5
+    pt = np.full((groups, pt_ld), 99, dtype=np.int32)
+    pt[:, :P] = rng.permutation(pool)[: groups * P].reshape(groups, P)
+    want_kept = oracle.page_keep_sets(L, n, K, prot, ps, seed, rnd, 0, groups)
+    want_pt, want_freed = oracle.page_table_edit(pt, want_kept, P)
+    dpt = torch.from_numpy(pt).to(DEV)
+    kept = torch.full((groups, Kp + 1), -9, dtype=torch.int32, device=DEV)
+    freed = torch.full((groups * (P - Kp) + 1,), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_evict_pages_random(dpt, pt_ld, ps, R, L, n, K, prot, seed, rnd, kept, Kp + 1, freed,
+                                 fcount)
+    torch.cuda.synchronize()
+    got = to_np(kept)
+    assert np.array_equal(got[:, :Kp], want_kept)
+    assert np.all(got[:, Kp:] == -9)
+    assert np.array_equal(to_np(dpt), want_pt)
+    nf = int(fcount.item())
+    assert nf == groups * (P - Kp)
+    got_freed = to_np(freed)[:nf]
+    assert sorted(got_freed.tolist()) == sorted(x for f in want_freed for x in f)
