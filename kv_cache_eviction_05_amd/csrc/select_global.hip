@@ -33,13 +33,16 @@
 namespace kvevict {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kBinsPerThread = 2048 / kThreads;
 static_assert(kBinsPerThread >= 1 && 2048 % kThreads == 0 && 1024 % kThreads == 0,
               "resolve: whole bins per thread");
 constexpr int kWaves = kThreads / kWave;
-constexpr int32_t kChunk = 8192;  // 16 keys per thread (same-process A/B: 52 us against
-                                  // 62 us for 4096-key items on 256 threads)
+// 8 keys per thread.  Same-process A/B on 64 lists of 32,512 candidates, back to
+// back / inside the round: 45.7 / 51.6 us, against 48.9 / 56.5 us with 512
+// threads and 16 keys per thread, 55.8 / 61.4 us with 4096-key items on 1024
+// threads and 49.3 / 57.6 us with 12,288-key items.
+constexpr int32_t kChunk = 8192;
 
 // workspace layout (uint32 words)
 constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
