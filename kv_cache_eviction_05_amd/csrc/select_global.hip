@@ -247,41 +247,62 @@ __global__ __launch_bounds__(kThreads) void global_hist_kernel(GlobalArgs a, int
 // Emits the kept indices of an item whose keys are in registers: keys > thr,
 // and keys == thr while fewer than need_eq of them come before in flat order
 // (eq0 of them lie in earlier items).  `out` points at the item's first slot.
+// Key u of a thread sits at item position u*kThreads + threadIdx.x, so the
+// chronological order runs over (u, wave, lane): every wave ballots all its
+// keys first, one wave scans the per-(u, wave) counts, and each key's slot is
+// its scanned prefix plus the set lanes below it (two barriers in all).
 __device__ __forceinline__ void emit_item(const uint32_t* keys, int32_t i0, int32_t i1,
                                           uint32_t thr, uint32_t need_eq, uint32_t eq0,
-                                          int32_t* out, uint32_t* s_tile) {
+                                          int32_t* out, uint32_t* s_cnt) {
+  constexpr int kSlots = kKeysPerThread * kWaves;  // (u, wave) slots per kind
+  static_assert(2 * kSlots == 4 * kWave, "the scan gives four counts to each lane of a wave");
   const uint32_t taken0 = min(eq0, need_eq);
   const int wave = threadIdx.x / kWave;
-  uint32_t carry_gt = 0u, carry_eq = 0u;
+  const uint32_t lane = lane_id();
+  uint64_t bg[kKeysPerThread], be[kKeysPerThread];
 #pragma unroll
   for (int u = 0; u < kKeysPerThread; ++u) {
-    const int32_t i = i0 + threadIdx.x + u * kThreads;
-    const bool valid = i < i1;
-    const uint32_t k = keys[u];
-    const bool gt = valid && k > thr;
-    const bool eq = valid && k == thr;
-    const uint64_t bg = __ballot(gt);
-    const uint64_t be = __ballot(eq);
-    if (lane_id() == 0) {
-      s_tile[wave] = (uint32_t)__popcll(bg);
-      s_tile[kWaves + wave] = (uint32_t)__popcll(be);
+    const bool valid = i0 + (int32_t)threadIdx.x + u * kThreads < i1;
+    bg[u] = __ballot(valid && keys[u] > thr);
+    be[u] = __ballot(valid && keys[u] == thr);
+    if (lane == 0) {
+      s_cnt[u * kWaves + wave] = (uint32_t)__popcll(bg[u]);
+      s_cnt[kSlots + u * kWaves + wave] = (uint32_t)__popcll(be[u]);
     }
-    __syncthreads();
-    uint32_t pre_gt = 0u, pre_eq = 0u, tot_gt = 0u, tot_eq = 0u;
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive prefixes, gt counts and eq counts separately
+    uint32_t c[4], run = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t g = s_tile[w], e = s_tile[kWaves + w];
-      pre_gt += (w < wave) ? g : 0u;
-      pre_eq += (w < wave) ? e : 0u;
-      tot_gt += g;
-      tot_eq += e;
+    for (int q = 0; q < 4; ++q) {
+      c[q] = s_cnt[lane * 4 + q];
+      run += c[q];
     }
-    __syncthreads();
-    const uint32_t gt_before = carry_gt + pre_gt + count_below(bg);
-    const uint32_t eq_before = eq0 + carry_eq + pre_eq + count_below(be);  // flat order
-    if (gt || (eq && eq_before < need_eq)) out[gt_before + min(eq_before, need_eq) - taken0] = i;
-    carry_gt += tot_gt;
-    carry_eq += tot_eq;
+    // lanes [0, 32) hold the gt counts, [32, 64) the eq counts
+    uint32_t incl = run;
+#pragma unroll
+    for (int d = 1; d < kWave / 2; d <<= 1) {
+      const uint32_t t = __shfl_up(incl, d, kWave / 2);
+      if ((lane & (kWave / 2 - 1)) >= (uint32_t)d) incl += t;
+    }
+    uint32_t pre = incl - run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_cnt[2 * kSlots + lane * 4 + q] = pre;
+      pre += c[q];
+    }
+  }
+  __syncthreads();
+  const uint32_t* pre_gt = s_cnt + 2 * kSlots;
+  const uint32_t* pre_eq = pre_gt + kSlots;
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const bool gt = (bg[u] >> lane) & 1u;
+    const bool eq = (be[u] >> lane) & 1u;
+    const uint32_t gt_before = pre_gt[u * kWaves + wave] + count_below(bg[u]);
+    const uint32_t eq_before = eq0 + pre_eq[u * kWaves + wave] + count_below(be[u]);  // flat order
+    if (gt || (eq && eq_before < need_eq))
+      out[gt_before + min(eq_before, need_eq) - taken0] = i0 + (int32_t)threadIdx.x + u * kThreads;
   }
 }
 
@@ -365,29 +386,26 @@ __global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a, in
 
 __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int levels) {
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_tile[2 * kWaves];
+  __shared__ uint32_t s_cnt[4 * kKeysPerThread * kWaves];
   __shared__ uint32_t s_state[3][4];
   const int64_t f = blockIdx.x;
   const int64_t M = a.num_lists * a.chunks;
-  const uint32_t* eqx = a.ws + kArrays + 2 * M;
-  const uint32_t* S = a.ws + kArrays + 3 * M;
+  const bool direct = M <= kDirectPrefixItems;
   int64_t list;
   int32_t i0, i1;
   item_range(a, f, &list, &i0, &i1);
+  // everything this workgroup reads is issued up front: the histograms, the
+  // item's keys and the per-item counts or offsets written by earlier kernels
+  // (plain loads: the kernel boundary makes them visible)
   HistRegs r;
   load_hists(a.ws, levels, &r);
   uint32_t keys[kKeysPerThread];
   load_keys(a.scores + list * a.ld, i0, i1, keys);
-  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
-  uint32_t thr, need_eq;
-  threshold_of(a, t, &thr, &need_eq);
-  // written by the count kernel's atomics: plain loads see them after the kernel boundary
-  uint32_t eq0, offset;
-  if (M <= kDirectPrefixItems) {
-    const uint32_t* gt_arr = a.ws + kArrays;
-    const uint32_t* eq_arr = gt_arr + M;
-    const int64_t ls = list * a.chunks;
-    uint32_t e_all = 0u, gt_in = 0u, e_in = 0u;
+  const uint32_t* gt_arr = a.ws + kArrays;
+  const uint32_t* eq_arr = gt_arr + M;
+  const int64_t ls = list * a.chunks;
+  uint32_t e_all = 0u, gt_in = 0u, e_in = 0u, eq0, offset;
+  if (direct) {  // sums over the items before f: all of them for eq, f's list for gt and eq
     for (int64_t g = threadIdx.x; g < f; g += kThreads) {
       const uint32_t e = eq_arr[g];
       e_all += e;
@@ -396,9 +414,19 @@ __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int
         e_in += e;
       }
     }
+  } else {
+    eq0 = gt_arr[2 * M + f];                     // eqx[f]
+    offset = gt_arr[3 * M + f] - gt_arr[3 * M + ls];  // S[f] - S[ls]
+  }
+  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
+  uint32_t thr, need_eq;
+  threshold_of(a, t, &thr, &need_eq);
+  if (direct) {
     eq0 = block_sum<kThreads>(e_all, s_scan);
     gt_in = block_sum<kThreads>(gt_in, s_scan);
     e_in = block_sum<kThreads>(e_in, s_scan);
+    // keys == T are kept in flat order, so the run [ls, f) keeps the first
+    // (need_eq - eq before ls) of its e_in, clamped to [0, e_in]
     const uint32_t eq_ls = eq0 - e_in;
     const uint32_t room_ls = (need_eq > eq_ls) ? need_eq - eq_ls : 0u;
     offset = gt_in + min(e_in, room_ls);
@@ -406,12 +434,9 @@ __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int
       const uint32_t room_f = (need_eq > eq0) ? need_eq - eq0 : 0u;
       a.kept_count[list] = a.prot + (int32_t)(offset + gt_arr[f] + min(eq_arr[f], room_f));
     }
-  } else {
-    eq0 = eqx[f];
-    offset = S[f] - S[list * a.chunks];
   }
   emit_item(keys, i0, i1, thr, need_eq, eq0, a.kept_idx + list * a.kept_ld + a.prot + offset,
-            s_tile);
+            s_cnt);
 }
 
 }  // namespace
