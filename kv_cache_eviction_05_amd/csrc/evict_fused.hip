@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void evict_random_inplace_kernel(FusedArg
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int32_t i = 4 * c + q;
-      if (i >= prot && i < n) s_keys[i - prot] = rank_key(unit_from_word(r.w[q]));
+      if (i >= prot && i < n) s_keys[i - prot] = draw_key(r.w[q]);
     }
   }
   for (int32_t j = tid; j < prot; j += kThreads) s_kept[j] = j;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void evict_random_inplace_kernel(FusedArg
   if (kk > 0) {
     auto key_at = [&](int32_t i) -> uint32_t { return s_keys[i]; };
     uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate
-    if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
+    if (kk < m) radix_select<24>(key_at, m, kk, sh, thr, need_eq);
     emit_kept(key_at, m, thr, need_eq, sh,
               [&](uint32_t slot, int32_t i) { s_kept[prot + slot] = prot + i; });
   }

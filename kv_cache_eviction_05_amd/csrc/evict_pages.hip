@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void evict_pages_kernel(PagesArgs a) {
     const Philox4x64 r =
         philox4x64_10((uint64_t)(i >> 2), 0u, layer, (request << 32) | a.round, a.seed, 0);
     const uint64_t w = (i & 2) ? ((i & 1) ? r.w[3] : r.w[2]) : ((i & 1) ? r.w[1] : r.w[0]);
-    s_keys[b - pp] = rank_key(unit_from_word(w));  // word i % 4, with constant indices
+    s_keys[b - pp] = draw_key(w);  // word i % 4, with constant indices
   }
   for (int32_t b = tid; b < P; b += kThreads) {
     s_old[b] = row[b];
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void evict_pages_kernel(PagesArgs a) {
   if (kk > 0) {
     auto key_at = [&](int32_t i) -> uint32_t { return s_keys[i]; };
     uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate page
-    if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
+    if (kk < m) radix_select<24>(key_at, m, kk, sh, thr, need_eq);
     emit_kept(key_at, m, thr, need_eq, sh, [&](uint32_t slot, int32_t i) {
       s_kept[pp + slot] = pp + i;
       s_flag[pp + i] = 1;

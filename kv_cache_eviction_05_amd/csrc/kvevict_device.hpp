@@ -62,6 +62,12 @@ __device__ __forceinline__ float unit_from_word(uint64_t word) {
   return (float)(uint32_t)(word >> 40) * (1.0f / 16777216.0f);
 }
 
+// The same 24 bits as a rank key: unit_from_word(word) is this integer times
+// 2^-24 exactly, so the two order draws alike, ties included.  The integer
+// spreads uniformly over its radix digits, where a float's top byte (sign and
+// exponent) piles most of [0, 1) into two or three bins.
+__device__ __forceinline__ uint32_t draw_key(uint64_t word) { return (uint32_t)(word >> 40); }
+
 // ---------------------------------------------------------------------------
 // Wave / block helpers (wave64).
 // ---------------------------------------------------------------------------

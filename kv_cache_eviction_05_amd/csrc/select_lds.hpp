@@ -24,13 +24,16 @@ namespace kvevict {
 constexpr int kSelectThreads = 256;
 
 // Digit width of radix pass p for a workgroup of NT threads.
-template <int NT>
+// Keys of kKeyBits = 24 (the raw draws of the random scorer) take 11/11/2 or
+// 8/8/8-bit digits: three passes.
+template <int NT, int kKeyBits = 32>
 __host__ __device__ constexpr int select_digit_bits(int p) {
-  return NT >= 1024 ? (p < 2 ? 11 : 10) : 8;
+  return kKeyBits == 24 ? (NT >= 1024 ? (p < 2 ? 11 : 2) : 8)
+                        : (NT >= 1024 ? (p < 2 ? 11 : 10) : 8);
 }
-template <int NT>
+template <int NT, int kKeyBits = 32>
 __host__ __device__ constexpr int select_passes() {
-  return NT >= 1024 ? 3 : 4;
+  return (kKeyBits == 24 || NT >= 1024) ? 3 : 4;
 }
 
 template <int NT = kSelectThreads>
@@ -46,16 +49,18 @@ struct SelectShared {
 
 // Keep kk of the m keys key_at(0..m-1), 0 < kk < m: every key > thr, and the
 // first need_eq keys == thr (need_eq = 0xffffffff: every key == thr).
-template <int NT, class KeyAt>
+// kKeyBits: the keys use only their low kKeyBits bits (32 or 24).
+template <int kKeyBits = 32, int NT, class KeyAt>
 __device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared<NT>& sh,
                              uint32_t& thr, uint32_t& need_eq) {
+  static_assert(kKeyBits == 32 || kKeyBits == 24, "32-bit rank keys or 24-bit draws");
   const int tid = threadIdx.x;
   uint32_t prefix = 0u, mask = 0u, remaining = (uint32_t)kk;
   bool whole_bucket = false;
-  int shift = 32;
+  int shift = kKeyBits;
 #pragma unroll
-  for (int pass = 0; pass < select_passes<NT>(); ++pass) {
-    const int bits = select_digit_bits<NT>(pass);
+  for (int pass = 0; pass < select_passes<NT, kKeyBits>(); ++pass) {
+    const int bits = select_digit_bits<NT, kKeyBits>(pass);
     const uint32_t bins = 1u << bits;
     shift -= bits;
     for (uint32_t b = tid; b < bins; b += NT) sh.hist[b] = 0u;
@@ -65,14 +70,16 @@ __device__ void radix_select(KeyAt key_at, int32_t m, int32_t kk, SelectShared<N
       if ((k & mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & (bins - 1u)], 1u);
     }
     __syncthreads();
-    // thread t holds bins [top - per, top), top = bins - per*t, highest first, so
-    // the inclusive scan counts the keys in bins >= top - per
-    const uint32_t per = bins / NT;
-    const uint32_t top = bins - per * (uint32_t)tid;
+    // thread t holds bins [top - per, top), top = bins - per*t, highest first (with
+    // fewer bins than threads, threads t < bins hold one each), so the inclusive
+    // scan counts the keys in bins >= top - per
+    const uint32_t per = bins >= (uint32_t)NT ? bins / NT : 1u;
+    const bool holds = (uint32_t)tid * per < bins;
+    const uint32_t top = holds ? bins - per * (uint32_t)tid : 0u;
     uint32_t h[2], c = 0u;
 #pragma unroll
     for (uint32_t b = 0; b < 2; ++b) {
-      h[b] = (b < per) ? sh.hist[top - 1u - b] : 0u;
+      h[b] = (holds && b < per) ? sh.hist[top - 1u - b] : 0u;
       c += h[b];
     }
     uint32_t total;

@@ -126,8 +126,10 @@ struct DrawArgs {
 
 // The random scorer and the per-list top-K in one launch: list `blockIdx.x`
 // draws its candidates' Philox scores (the stream of kvevict_score_random) as
-// rank keys straight into LDS, or, for lists longer than LDS holds, draws them
-// again on every pass; no score buffer is written or read.
+// their 24-bit integers (draw_key: the same order as the scores) straight into
+// LDS, or, for lists longer than LDS holds, draws them again on every pass; no
+// score buffer is written or read.  The select then takes three radix passes
+// over uniformly filled digits.
 template <bool kKeysInLds, int NT>
 __global__ __launch_bounds__(NT) void draw_select_kernel(DrawArgs a) {
   extern __shared__ uint32_t s_keys[];
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(NT) void draw_select_kernel(DrawArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int32_t i = 4 * c + q;
-        if (i >= prot && i < n) s_keys[i - prot] = rank_key(unit_from_word(r.w[q]));
+        if (i >= prot && i < n) s_keys[i - prot] = draw_key(r.w[q]);
       }
     }
     __syncthreads();
@@ -168,10 +170,10 @@ __global__ __launch_bounds__(NT) void draw_select_kernel(DrawArgs a) {
     const Philox4x64 r = philox4x64_10((uint64_t)(slot >> 2), head, layer, ctr2, a.seed, 0);
     // word slot % 4, chosen with constant indices (a variable index would place r in memory)
     const uint64_t w = (slot & 2) ? ((slot & 1) ? r.w[3] : r.w[2]) : ((slot & 1) ? r.w[1] : r.w[0]);
-    return rank_key(unit_from_word(w));
+    return draw_key(w);
   };
   uint32_t thr = 0u, need_eq = 0xffffffffu;  // kk == m: keep every candidate
-  if (kk < m) radix_select(key_at, m, kk, sh, thr, need_eq);
+  if (kk < m) radix_select<24>(key_at, m, kk, sh, thr, need_eq);
   emit_kept(key_at, m, thr, need_eq, sh,
             [&](uint32_t slot, int32_t i) { out[prot + slot] = prot + i; });
 }
