@@ -60,6 +60,8 @@ def describe(cfg) -> str:
     if cfg.select in ("global", "layers"):
         rule = ("global top-B" if cfg.select == "global"
                 else "gate-proportional per-layer top-K_l at the same total")
+        if cfg.fuse_score:
+            rule += " (score and top-B in one call, the scorer filling the first radix level)"
         return (f"{cfg.name}: {cfg.L} layers x {cfg.H} KV heads, D={cfg.D}, n={cfg.n}, "
                 f"prot={cfg.prot}, p={cfg.p}, weighted GDN score over 48 GDN layers x 48 heads, "
                 f"{rule}, {layout}")
@@ -332,7 +334,8 @@ def main():
     binding.load()
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
-        names = ["batch", "tiny", "paged", "paged_shared", "global", "longgen", "layers",
+        names = ["batch", "tiny", "paged", "paged_shared", "global", "global_fused", "longgen",
+                 "layers",
                  "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
                  "paged_fused", "longgen_fused", "paged_pages"]
     if "batch" not in names:

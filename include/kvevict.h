@@ -5,6 +5,8 @@
  *   1. score every cache entry            kvevict_score_random / kvevict_score_weighted
  *   2. pin the protected prompt prefix    (part of every scorer and selector)
  *   3. select the entries to keep         kvevict_select_topk / kvevict_select_global
+ *      (steps 1-3 fused: kvevict_select_random for the random draw and top-K,
+ *      kvevict_score_select_global for the weighted score and global top-B)
  *   4. compact the kept bf16 K/V rows     kvevict_compact
  *
  * Sources of the definitions:
@@ -252,6 +254,28 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
                                      int64_t num_lists, int32_t n, int32_t prot, double p,
                                      void* workspace, size_t* workspace_bytes,
                                      hipStream_t stream);
+
+/*
+ * Weighted score and pin + model-wide top-B in one call ([GS] Sec. 4.1 and
+ * problem statement; KVzip-style global top-B): the results of
+ * kvevict_score_weighted on its arguments followed by kvevict_select_global
+ * over its L*H lists (list = l*H + h), bit for bit.  The scorer also adds the
+ * scores it writes to the select's first radix level, so the select reads
+ * the scores one time fewer and skips one launch.
+ * Arguments are those of the two calls: scores and ld are the scores buffer
+ * the scorer writes and the select reads; workspace follows
+ * kvevict_select_global's two-phase protocol with num_lists = L*H (the same
+ * size as there); budget_out (optional, HOST) receives B.
+ * Requires what both calls require.  Nothing is written when the arguments
+ * are invalid.
+ */
+kvevict_status kvevict_score_select_global(
+    int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count, int64_t* budget_out, float* scores,
+    int64_t ld, const float* beta, const float* vnorm, int64_t sig_stride_g,
+    int64_t sig_stride_t, int64_t sig_stride_j, const float* w, int32_t w_slots,
+    const int32_t* win_begin, const int32_t* win_count, int32_t L, int32_t H, int32_t G,
+    int32_t Hg, int32_t n, int32_t prot, double p, void* workspace, size_t* workspace_bytes,
+    hipStream_t stream);
 
 /*
  * Chronological compaction ([RA] per-KV-head physical eviction, chronological

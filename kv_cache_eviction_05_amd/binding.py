@@ -30,7 +30,7 @@ LAYOUT_PAGED = 1
 EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
-           "kvevict_evict_pages_random", "kvevict_select_random",
+           "kvevict_evict_pages_random", "kvevict_select_random", "kvevict_score_select_global",
            "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
            "kvevict_abi_version")
 
@@ -74,6 +74,9 @@ def load():
     lib.kvevict_select_topk.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
     lib.kvevict_select_global.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i32, _i32, _dbl, _p,
                                           ctypes.POINTER(_sz), _p]
+    lib.kvevict_score_select_global.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _i64, _i64,
+                                                _i64, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _dbl, _p, ctypes.POINTER(_sz), _p]
     lib.kvevict_compact.argtypes = [ctypes.POINTER(KvDesc), _p, _p, ctypes.POINTER(KvDesc), _p, _p,
                                     _p, _i64, _p, _i32, _i64, _i32, _p, _p]
     lib.kvevict_select_topk_layers.argtypes = [_p, _i64, _p, _p, _i64, _i64, _i32, _i32, _i32,
@@ -95,7 +98,8 @@ def load():
                  "kvevict_select_topk_layers", "kvevict_layer_power_budget",
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
                  "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
-                 "kvevict_evict_pages_random", "kvevict_select_random"):
+                 "kvevict_evict_pages_random", "kvevict_select_random",
+                 "kvevict_score_select_global"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -193,6 +197,34 @@ def kvevict_score_weighted(scores, ld, beta, vnorm, sg, st, sj, w, w_slots, win_
                                          _ptr(w), w_slots, wb, wc, L, H, G, Hg, n, prot,
                                          _stream(stream)),
            "kvevict_score_weighted")
+
+
+def kvevict_score_select_global(kept_idx, kept_ld, kept_count, scores, ld, beta, vnorm, sg, st, sj,
+                                w, w_slots, win_begin, win_count, L, H, G, Hg, n, prot, p,
+                                workspace, workspace_bytes, stream=None) -> int:
+    """Weighted score + global top-B in one call (the budget B is returned)."""
+    lists = L * H
+    _need(scores, torch.float32, _rows(lists, ld, n), "scores")
+    sig = (G - 1) * sg + (n - 1) * st + (Hg - 1) * sj + 1 if n > 0 else 0
+    _need(beta, torch.float32, sig, "beta")
+    _need(vnorm, torch.float32, sig, "vnorm")
+    _need(w, torch.float32, L * H * w_slots * Hg, "w")
+    _need(kept_idx, torch.int32, _rows(lists, kept_ld, n), "kept_idx")
+    _need(kept_count, torch.int32, lists, "kept_count")
+    _need(workspace, None, workspace_bytes // max(workspace.element_size(), 1), "workspace")
+    if len(win_begin) != L or len(win_count) != L:
+        raise ValueError("window arrays must have L entries")
+    wb = (ctypes.c_int32 * L)(*[int(x) for x in win_begin])
+    wc = (ctypes.c_int32 * L)(*[int(x) for x in win_count])
+    budget = _i64(0)
+    size = _sz(workspace_bytes)
+    _check(load().kvevict_score_select_global(_ptr(kept_idx), kept_ld, _ptr(kept_count),
+                                              ctypes.byref(budget), _ptr(scores), ld, _ptr(beta),
+                                              _ptr(vnorm), sg, st, sj, _ptr(w), w_slots, wb, wc, L,
+                                              H, G, Hg, n, prot, p, _ptr(workspace),
+                                              ctypes.byref(size), _stream(stream)),
+           "kvevict_score_select_global")
+    return budget.value
 
 
 def kvevict_select_topk(kept_idx, kept_ld, scores, ld, num_lists, n, K, prot, stream=None):

@@ -71,6 +71,7 @@ class RoundConfig:
     fused: bool = False        # draw + select + in-place move in one launch (random, top-K)
     page_draw: bool = False    # one draw per page; compaction as page-table edits (paged)
     fuse_draw: bool = True     # random top-K out of place: draw the scores inside the select
+    fuse_score: bool = False   # weighted score and global top-B in one call
     p: float = 0.0             # kept fraction for the global budget
     rounds: int = 1
     seed: int = 0
@@ -140,6 +141,9 @@ LONGGEN = RoundConfig("longgen", R=128, L=36, H=8, D=128, K=3072, r=64, prot=557
 # next rows: GateSight's deployed per-layer allocation at the global round's shape and total,
 # and the shared list of a layer ranked by the max over its KV heads (kept count % 4 == 0)
 LAYERS = replace(GLOBAL, name="layers", select="layers")
+# the global round with the weighted score and the top-B in one call (the scorer fills the
+# select's first radix level)
+GLOBAL_FUSED = replace(GLOBAL, name="global_fused", fuse_score=True)
 PAGED_SHARED_MAX = replace(PAGED, name="paged_shared_max", shared_max=True)
 # a content scorer that reads every key once more: KeyDiff at the batch round's shape
 KEYDIFF = replace(BATCH, name="keydiff", scorer="keydiff")
@@ -150,6 +154,6 @@ PAGED_FUSED = replace(PAGED_INPLACE, name="paged_fused", fused=True)
 LONGGEN_FUSED = replace(LONGGEN_INPLACE, name="longgen_fused", fused=True)
 PAGED_PAGES = replace(PAGED_INPLACE, name="paged_pages", page_draw=True)
 
-ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, LONGGEN, LAYERS,
+ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, GLOBAL_FUSED, LONGGEN, LAYERS,
                            PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE,
                            PAGED_FUSED, LONGGEN_FUSED, PAGED_PAGES)}

@@ -82,25 +82,41 @@ kvevict_status kvevict_score_random(float* scores, int64_t ld, int64_t num_reque
                                                  shared_draw != 0, stream));
 }
 
+// Arguments of the weighted score (kvevict_score_weighted and the fused score +
+// global top-B), with the windows copied into *win.
+static kvevict_status check_weighted(const float* scores, int64_t ld, const float* beta,
+                                     const float* vnorm, int64_t sig_stride_g,
+                                     int64_t sig_stride_t, int64_t sig_stride_j, const float* w,
+                                     int32_t w_slots, const int32_t* win_begin,
+                                     const int32_t* win_count, int32_t L, int32_t H, int32_t G,
+                                     int32_t Hg, int32_t n, int32_t prot,
+                                     kvevict::WindowTable* win) {
+  if (L < 1 || L > kvevict::kMaxWeightedLayers || H < 1 || G < 1 || Hg < 1) return KVEVICT_ERR_INVALID_ARG;
+  if (n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
+  if (w_slots < 1 || w_slots > 64) return KVEVICT_ERR_INVALID_ARG;
+  if (!win_begin || !win_count) return KVEVICT_ERR_INVALID_ARG;
+  if (sig_stride_g < 0 || sig_stride_t < 0 || sig_stride_j < 0) return KVEVICT_ERR_INVALID_ARG;
+  for (int32_t l = 0; l < L; ++l) {
+    if (win_count[l] < 0 || win_count[l] > w_slots) return KVEVICT_ERR_INVALID_ARG;
+    if (win_begin[l] < 0 || win_begin[l] + (int64_t)win_count[l] > G) return KVEVICT_ERR_INVALID_ARG;
+    win->begin[l] = win_begin[l];
+    win->count[l] = win_count[l];
+  }
+  if (n > 0 && (!scores || !beta || !vnorm || !w)) return KVEVICT_ERR_INVALID_ARG;
+  return KVEVICT_OK;
+}
+
 kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* beta,
                                       const float* vnorm, int64_t sig_stride_g,
                                       int64_t sig_stride_t, int64_t sig_stride_j, const float* w,
                                       int32_t w_slots, const int32_t* win_begin,
                                       const int32_t* win_count, int32_t L, int32_t H, int32_t G,
                                       int32_t Hg, int32_t n, int32_t prot, hipStream_t stream) {
-  if (L < 1 || L > kvevict::kMaxWeightedLayers || H < 1 || G < 1 || Hg < 1) return KVEVICT_ERR_INVALID_ARG;
-  if (n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
-  if (w_slots < 1 || w_slots > 64) return KVEVICT_ERR_INVALID_ARG;
-  if (!win_begin || !win_count) return KVEVICT_ERR_INVALID_ARG;
-  if (sig_stride_g < 0 || sig_stride_t < 0 || sig_stride_j < 0) return KVEVICT_ERR_INVALID_ARG;
   kvevict::WindowTable win;
-  for (int32_t l = 0; l < L; ++l) {
-    if (win_count[l] < 0 || win_count[l] > w_slots) return KVEVICT_ERR_INVALID_ARG;
-    if (win_begin[l] < 0 || win_begin[l] + (int64_t)win_count[l] > G) return KVEVICT_ERR_INVALID_ARG;
-    win.begin[l] = win_begin[l];
-    win.count[l] = win_count[l];
-  }
-  if (n > 0 && (!scores || !beta || !vnorm || !w)) return KVEVICT_ERR_INVALID_ARG;
+  const kvevict_status st = check_weighted(scores, ld, beta, vnorm, sig_stride_g, sig_stride_t,
+                                           sig_stride_j, w, w_slots, win_begin, win_count, L, H,
+                                           G, Hg, n, prot, &win);
+  if (st != KVEVICT_OK) return st;
   return hip_status(kvevict::launch_score_weighted(scores, ld, beta, vnorm, sig_stride_g,
                                                    sig_stride_t, sig_stride_j, w, w_slots, win, L,
                                                    H, Hg, n, prot, stream));
@@ -238,11 +254,14 @@ kvevict_status kvevict_layer_power_budget(const float* gate, int32_t L, int32_t 
   return KVEVICT_OK;
 }
 
-kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
-                                     int64_t* budget_out, const float* scores, int64_t ld,
-                                     int64_t num_lists, int32_t n, int32_t prot, double p,
-                                     void* workspace, size_t* workspace_bytes,
-                                     hipStream_t stream) {
+// Arguments, workspace protocol and budget of a global top-B over num_lists
+// lists of n scores (kvevict_select_global and the fused score + global top-B).
+// *launch is false when the call only reports the workspace size.
+static kvevict_status check_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                   int64_t ld, int64_t num_lists, int32_t n, int32_t prot,
+                                   double p, void* workspace, size_t* workspace_bytes,
+                                   int64_t* budget, bool* launch) {
+  *launch = false;
   if (!workspace_bytes) return KVEVICT_ERR_INVALID_ARG;
   if (num_lists < 0 || n < 0 || prot < 0 || prot > n || ld < n || kept_ld < n) return KVEVICT_ERR_INVALID_ARG;
   if (!(p >= 0.0 && p <= 1.0)) return KVEVICT_ERR_INVALID_ARG;  // also rejects NaN
@@ -254,16 +273,65 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
   }
   if (*workspace_bytes < need) return KVEVICT_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 3u) return KVEVICT_ERR_ALIGNMENT;
-  if (num_lists > 0 && (!kept_idx || !kept_count || !scores)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_lists > 0 && (!kept_idx || !kept_count)) return KVEVICT_ERR_INVALID_ARG;
   // B = lists * round(p * (n - prot)): binary64 product, ties to even.
   const int saved = std::fegetround();
   std::fesetround(FE_TONEAREST);
   const double per_list = std::nearbyint(p * (double)(n - prot));
   std::fesetround(saved);
-  const int64_t budget = num_lists * (int64_t)per_list;
+  *budget = num_lists * (int64_t)per_list;
+  *launch = true;
+  return KVEVICT_OK;
+}
+
+kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                     int64_t* budget_out, const float* scores, int64_t ld,
+                                     int64_t num_lists, int32_t n, int32_t prot, double p,
+                                     void* workspace, size_t* workspace_bytes,
+                                     hipStream_t stream) {
+  int64_t budget = 0;
+  bool launch = false;
+  const kvevict_status st = check_global(kept_idx, kept_ld, kept_count, ld, num_lists, n, prot, p,
+                                         workspace, workspace_bytes, &budget, &launch);
+  if (st != KVEVICT_OK || !launch) return st;
+  if (num_lists > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
   if (budget_out) *budget_out = budget;
   return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
                                                   num_lists, n, prot, budget, workspace, stream));
+}
+
+kvevict_status kvevict_score_select_global(
+    int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count, int64_t* budget_out, float* scores,
+    int64_t ld, const float* beta, const float* vnorm, int64_t sig_stride_g,
+    int64_t sig_stride_t, int64_t sig_stride_j, const float* w, int32_t w_slots,
+    const int32_t* win_begin, const int32_t* win_count, int32_t L, int32_t H, int32_t G,
+    int32_t Hg, int32_t n, int32_t prot, double p, void* workspace, size_t* workspace_bytes,
+    hipStream_t stream) {
+  kvevict::WindowTable win;
+  kvevict_status st = check_weighted(scores, ld, beta, vnorm, sig_stride_g, sig_stride_t,
+                                     sig_stride_j, w, w_slots, win_begin, win_count, L, H, G, Hg,
+                                     n, prot, &win);
+  if (st != KVEVICT_OK) return st;
+  const int64_t num_lists = (int64_t)L * H;
+  int64_t budget = 0;
+  bool launch = false;
+  st = check_global(kept_idx, kept_ld, kept_count, ld, num_lists, n, prot, p, workspace,
+                    workspace_bytes, &budget, &launch);
+  if (st != KVEVICT_OK || !launch) return st;
+  if (budget_out) *budget_out = budget;
+  // prompts and cleared workspace, then the scores with the first radix level
+  // added by the scorer, then the rest of the select
+  hipError_t e = kvevict::launch_select_global_init(kept_idx, kept_ld, kept_count, num_lists, n,
+                                                    prot, budget, workspace, stream);
+  if (e != hipSuccess) return hip_status(e);
+  uint32_t* bins = kvevict::select_global_first_level_bins(num_lists, n, prot, budget, workspace);
+  e = kvevict::launch_score_weighted(scores, ld, beta, vnorm, sig_stride_g, sig_stride_t,
+                                     sig_stride_j, w, w_slots, win, L, H, Hg, n, prot, stream,
+                                     bins);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
+                                                  num_lists, n, prot, budget, workspace, stream,
+                                                  true));
 }
 
 kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,

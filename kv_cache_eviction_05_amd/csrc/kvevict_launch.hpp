@@ -18,10 +18,17 @@ struct WindowTable {
   int32_t count[kMaxWeightedLayers];
 };
 
+// First level of the global top-B: 2048 bins of rank key bits [21, 32).
+constexpr int kGlobalFirstLevelBins = 2048;
+
+// hist0 (optional): the first-level bins of a global top-B over these scores
+// (select_global_first_level_bins); every launch adds its scores of
+// candidates t >= prot to them.
 hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, const float* vnorm,
                                  int64_t sg, int64_t st, int64_t sj, const float* w,
                                  int32_t w_slots, const WindowTable& win, int32_t L, int32_t H,
-                                 int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
+                                 int32_t Hg, int32_t n, int32_t prot, hipStream_t stream,
+                                 uint32_t* hist0 = nullptr);
 
 constexpr int kMaxBudgetLayers = 64;
 
@@ -37,9 +44,21 @@ hipError_t launch_reduce_max_heads(float* out, int64_t out_ld, const float* scor
 
 size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot);
 
+// The whole global top-B (first_level_done = false), or, after
+// launch_select_global_init and a producer that filled the first-level bins,
+// the rest of it (first_level_done = true).
 hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
                                 const float* scores, int64_t ld, int64_t num_lists, int32_t n,
-                                int32_t prot, int64_t budget, void* workspace, hipStream_t stream);
+                                int32_t prot, int64_t budget, void* workspace, hipStream_t stream,
+                                bool first_level_done = false);
+// Prompt indices, prompt counts and the cleared workspace (before any producer adds bins).
+hipError_t launch_select_global_init(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                     int64_t num_lists, int32_t n, int32_t prot, int64_t budget,
+                                     void* workspace, hipStream_t stream);
+// The 2048 first-level bins (rank key bits [21, 32) of the candidates) inside
+// the workspace, or nullptr when the budget keeps nothing or everything.
+uint32_t* select_global_first_level_bins(int64_t num_lists, int32_t n, int32_t prot,
+                                         int64_t budget, void* workspace);
 
 // One K/V store as the compaction kernels see it (units: 16-byte vectors).
 struct StoreView {

@@ -67,7 +67,11 @@ struct WeightedArgs {
   int32_t slot[kLayersPerLaunch];        // its accumulator slot
   int64_t woff[kPlanLayers][kSlots];     // weight row of (g, slot) for head h0, or -1
   uint32_t end_mask[kPlanLayers];        // launch layers whose window ends at g
+  uint32_t* hist0;                       // first-level bins of a global top-B, or null
 };
+
+constexpr int kFirstLevelBins = kGlobalFirstLevelBins;  // rank key bits [21, 32)
+constexpr int kFirstLevelShift = 21;
 
 // ln(x) in binary64 for a positive normal x: x = 2^e * m, m in [1, 2);
 // c = 1 + (i + 1/2)/256 is the centre of m's slot, r = m/c - 1 (one fma with
@@ -202,6 +206,33 @@ __device__ __forceinline__ void stage_tile(const Tile<VW>& r, int32_t jn, double
   if (threadIdx.x < kWRow) w[threadIdx.x] = (double)r.w;
 }
 
+// Adds the scores this workgroup stored (every layer and head of the launch,
+// tokens [t0, t0 + kTok) from prot on) to the first-level bins of a global
+// top-B: an LDS histogram of their rank keys' top 11 bits, then one
+// device-scope add per nonzero bin.  The caller has passed a barrier after the
+// stores, so they are visible to the whole workgroup.
+__device__ void add_first_level_bins(const WeightedArgs& a, const float* scores, int32_t t0,
+                                     uint32_t* s_h) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kFirstLevelBins; b += kThreads) s_h[b] = 0u;
+  __syncthreads();
+  const int32_t total = a.nl * a.hb * kTok;
+  for (int32_t e = tid; e < total; e += kThreads) {
+    const int32_t tt = t0 + e % kTok;
+    const int32_t rest = e / kTok;
+    const int32_t hh = rest % a.hb, q = rest / a.hb;
+    if (tt >= a.prot && tt < a.n) {
+      const float v = scores[((int64_t)a.layer[q] * a.H + a.h0 + hh) * a.ld + tt];
+      atomicAdd(&s_h[rank_key(v) >> kFirstLevelShift], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < kFirstLevelBins; b += kThreads) {
+    const uint32_t h = s_h[b];
+    if (h) __hip_atomic_fetch_add(a.hist0 + b, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // The weights, signals and scores come as separate restrict-qualified
 // arguments: the kernel never writes what it reads.
 template <int VW>
@@ -232,116 +263,122 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
     for (int q = 0; q < a.nl; ++q)
       if (tile_in_prompt || ((a.empty_mask >> q) & 1u)) store(q, wave, t, 0.0);
   }
-  if (tile_in_prompt || a.g_hi <= a.g_lo) return;
-
-  if (tid < kLnTable) {
-    const double c = 1.0 + ((double)tid + 0.5) * (1.0 / kLnTable);
-    s_tab[tid] = make_double2(log(c), 1.0 / c);
-  }
-
-  const int32_t passes = (a.Hg + kJPass - 1) / kJPass;
-  const bool full = a.Hg % kJPass == 0;  // every pass is kJPass heads wide
-  const int32_t steps = (a.g_hi - a.g_lo) * passes;
-  double acc[kHB][kSlots];
-#pragma unroll
-  for (int hh = 0; hh < kHB; ++hh)
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) acc[hh][s] = 0.0;
-
-  // offsets of this thread's vectors within a full tile (-1 past the last token)
-  int64_t off[Tile<VW>::kVecs];
-#pragma unroll
-  for (int k = 0; k < Tile<VW>::kVecs; ++k) {
-    int32_t tok, j;
-    tile_pos<VW, true>(k, kJPass, &tok, &j);
-    off[k] = (t0 + tok < a.n) ? (int64_t)(t0 + tok) * a.st + (int64_t)j * a.sj : -1;
-  }
-  Tile<VW> regs;
-  if (full)
-    load_tile<VW, true>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
-  else
-    load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
-  __syncthreads();  // the ln table
-  for (int32_t step = 0; step < steps; ++step) {
-    const int32_t g = a.g_lo + step / passes;
-    const int32_t p = step - (g - a.g_lo) * passes;
-    const int32_t jn = min(kJPass, a.Hg - p * kJPass);
-    double* x = s_x[step & 1];
-    double* w = s_w[step & 1];
-    if (full)
-      stage_tile<VW, true>(regs, jn, x, w, s_tab);
-    else
-      stage_tile<VW, false>(regs, jn, x, w, s_tab);
-    if (step + 1 < steps) {  // the next tile streams in while this one is folded
-      const int32_t g2 = a.g_lo + (step + 1) / passes;
-      const int32_t p2 = step + 1 - (g2 - a.g_lo) * passes;
-      if (full)
-        load_tile<VW, true>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
-      else
-        load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
+  if (tile_in_prompt) return;
+  if (a.g_hi > a.g_lo) {  // some window of the launch is not empty
+    if (tid < kLnTable) {
+      const double c = 1.0 + ((double)tid + 0.5) * (1.0 / kLnTable);
+      s_tab[tid] = make_double2(log(c), 1.0 / c);
     }
-    __syncthreads();
 
-    const int32_t jb = wave * kJW;  // this wave's heads [jb, je) of the tile
-    const int32_t je = min(jb + kJW, jn);
-    const int32_t gi = g - a.g_lo;
-    // folds logs [jb, je) into the partial sums; kFull: je - jb == kJW
-    auto fold = [&](auto full_tag) {
-      constexpr bool kFull = decltype(full_tag)::value;
-      double xv[kJW];
+    const int32_t passes = (a.Hg + kJPass - 1) / kJPass;
+    const bool full = a.Hg % kJPass == 0;  // every pass is kJPass heads wide
+    const int32_t steps = (a.g_hi - a.g_lo) * passes;
+    double acc[kHB][kSlots];
 #pragma unroll
-      for (int k = 0; k < kJW; ++k)
-        xv[k] = (kFull || jb + k < je) ? x[(jb + k) * kXStride + lane] : 0.0;
+    for (int hh = 0; hh < kHB; ++hh)
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
-        if (a.woff[gi][s] < 0) continue;
+      for (int s = 0; s < kSlots; ++s) acc[hh][s] = 0.0;
+
+    // offsets of this thread's vectors within a full tile (-1 past the last token)
+    int64_t off[Tile<VW>::kVecs];
 #pragma unroll
-        for (int hh = 0; hh < kHB; ++hh) {
-          const double* wr = w + (s * kHB + hh) * kJPass + jb;
-          double v = acc[hh][s];
-#pragma unroll
-          for (int k = 0; k < kJW; ++k)
-            if (kFull || jb + k < je) v = fma(wr[k], xv[k], v);
-          acc[hh][s] = v;
-        }
+    for (int k = 0; k < Tile<VW>::kVecs; ++k) {
+      int32_t tok, j;
+      tile_pos<VW, true>(k, kJPass, &tok, &j);
+      off[k] = (t0 + tok < a.n) ? (int64_t)(t0 + tok) * a.st + (int64_t)j * a.sj : -1;
+    }
+    Tile<VW> regs;
+    if (full)
+      load_tile<VW, true>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
+    else
+      load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
+    __syncthreads();  // the ln table
+    for (int32_t step = 0; step < steps; ++step) {
+      const int32_t g = a.g_lo + step / passes;
+      const int32_t p = step - (g - a.g_lo) * passes;
+      const int32_t jn = min(kJPass, a.Hg - p * kJPass);
+      double* x = s_x[step & 1];
+      double* w = s_w[step & 1];
+      if (full)
+        stage_tile<VW, true>(regs, jn, x, w, s_tab);
+      else
+        stage_tile<VW, false>(regs, jn, x, w, s_tab);
+      if (step + 1 < steps) {  // the next tile streams in while this one is folded
+        const int32_t g2 = a.g_lo + (step + 1) / passes;
+        const int32_t p2 = step + 1 - (g2 - a.g_lo) * passes;
+        if (full)
+          load_tile<VW, true>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
+        else
+          load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
       }
-    };
-    if (je - jb == kJW)
-      fold(std::true_type{});
-    else if (jb < je)
-      fold(std::false_type{});
+      __syncthreads();
 
-    if (p + 1 < passes) continue;
-    // windows ending at g: add the waves' partial sums in a fixed order and store
-    uint32_t ends = a.end_mask[gi];
-    while (ends) {
-      const int32_t q = __builtin_ctz(ends);
-      ends &= ends - 1u;
-      const int32_t s_q = a.slot[q];
+      const int32_t jb = wave * kJW;  // this wave's heads [jb, je) of the tile
+      const int32_t je = min(jb + kJW, jn);
+      const int32_t gi = g - a.g_lo;
+      // folds logs [jb, je) into the partial sums; kFull: je - jb == kJW
+      auto fold = [&](auto full_tag) {
+        constexpr bool kFull = decltype(full_tag)::value;
+        double xv[kJW];
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
-        if (s == s_q) {
+        for (int k = 0; k < kJW; ++k)
+          xv[k] = (kFull || jb + k < je) ? x[(jb + k) * kXStride + lane] : 0.0;
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s) {
+          if (a.woff[gi][s] < 0) continue;
 #pragma unroll
           for (int hh = 0; hh < kHB; ++hh) {
-            s_red[wave][hh][lane] = acc[hh][s];
-            acc[hh][s] = 0.0;
+            const double* wr = w + (s * kHB + hh) * kJPass + jb;
+            double v = acc[hh][s];
+#pragma unroll
+            for (int k = 0; k < kJW; ++k)
+              if (kFull || jb + k < je) v = fma(wr[k], xv[k], v);
+            acc[hh][s] = v;
           }
         }
-      }
-      __syncthreads();
-      if (tid < kHB * kTok) {
-        const int hh = tid / kTok;
-        double v = 0.0;
+      };
+      if (je - jb == kJW)
+        fold(std::true_type{});
+      else if (jb < je)
+        fold(std::false_type{});
+
+      if (p + 1 < passes) continue;
+      // windows ending at g: add the waves' partial sums in a fixed order and store
+      uint32_t ends = a.end_mask[gi];
+      while (ends) {
+        const int32_t q = __builtin_ctz(ends);
+        ends &= ends - 1u;
+        const int32_t s_q = a.slot[q];
 #pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) v += s_red[w2][hh][lane];
-        store(q, hh, t, v);
+        for (int s = 0; s < kSlots; ++s) {
+          if (s == s_q) {
+#pragma unroll
+            for (int hh = 0; hh < kHB; ++hh) {
+              s_red[wave][hh][lane] = acc[hh][s];
+              acc[hh][s] = 0.0;
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < kHB * kTok) {
+          const int hh = tid / kTok;
+          double v = 0.0;
+#pragma unroll
+          for (int w2 = 0; w2 < kWaves; ++w2) v += s_red[w2][hh][lane];
+          store(q, hh, t, v);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
+  }
+  if (a.hist0) {
+    __syncthreads();  // the tile's scores are stored and the LDS tiles are free
+    add_first_level_bins(a, scores, t0, reinterpret_cast<uint32_t*>(&s_x[0][0]));
   }
 }
 
 static_assert(kThreads >= kHB * kTok, "one thread per (head, token) in the reduction");
+static_assert(kFirstLevelBins * 4 <= 2 * kJPass * kXStride * 8, "the bins fit the LDS tiles");
 static_assert(kWaves >= kHB, "one wave per head for the direct stores");
 
 }  // namespace
@@ -349,7 +386,8 @@ static_assert(kWaves >= kHB, "one wave per head for the direct stores");
 hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, const float* vnorm,
                                  int64_t sg, int64_t st, int64_t sj, const float* w,
                                  int32_t w_slots, const WindowTable& win, int32_t L, int32_t H,
-                                 int32_t Hg, int32_t n, int32_t prot, hipStream_t stream) {
+                                 int32_t Hg, int32_t n, int32_t prot, hipStream_t stream,
+                                 uint32_t* hist0) {
   if (n == 0 || L == 0 || H == 0) return hipSuccess;
   const unsigned tiles = (unsigned)((n + kTok - 1) / kTok);
   const bool vec = sj == 1 && sg % 2 == 0 && st % 2 == 0 && Hg % 2 == 0 &&
@@ -373,6 +411,7 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
     a.prot = prot;
     a.nl = 0;
     a.empty_mask = 0u;
+    a.hist0 = hist0;
     int32_t lo = 0x7fffffff, hi = 0;
     int32_t begin[kLayersPerLaunch], end[kLayersPerLaunch];
     for (; l < L && a.nl < kLayersPerLaunch; ++l) {

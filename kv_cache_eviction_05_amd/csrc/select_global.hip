@@ -45,6 +45,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int32_t kChunk = 8192;
 
 // workspace layout (uint32 words)
+static_assert(kGlobalFirstLevelBins == 2048, "first level: key bits [21, 32)");
 constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
 constexpr int64_t kHist1 = 2048;    // 2048 bins, key bits [10, 21)
 constexpr int64_t kHist2 = 4096;    // 1024 bins, key bits [0, 10)
@@ -449,19 +450,18 @@ size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot)
   return (size_t)((words * 4 + 255) / 256 * 256);
 }
 
-hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
-                                const float* scores, int64_t ld, int64_t num_lists, int32_t n,
-                                int32_t prot, int64_t budget, void* workspace,
-                                hipStream_t stream) {
-  if (num_lists == 0) return hipSuccess;
+namespace {
+
+GlobalArgs global_args(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                       const float* scores, int64_t ld, int64_t num_lists, int32_t n,
+                       int32_t prot, int64_t budget, void* workspace) {
   const int64_t m = n - prot;
-  const int32_t chunks = (int32_t)((m + kChunk - 1) / kChunk);
   GlobalArgs a;
   a.scores = scores;
   a.ld = ld;
   a.n = n;
   a.prot = prot;
-  a.chunks = chunks;
+  a.chunks = (int32_t)((m + kChunk - 1) / kChunk);
   a.num_lists = num_lists;
   a.budget = (uint32_t)budget;
   a.mode = (budget <= 0) ? kNone : (budget >= num_lists * m ? kAll : kNormal);
@@ -469,15 +469,44 @@ hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kep
   a.kept_idx = kept_idx;
   a.kept_ld = kept_ld;
   a.kept_count = kept_count;
+  return a;
+}
 
-  const int64_t M = num_lists * chunks;
+}  // namespace
+
+uint32_t* select_global_first_level_bins(int64_t num_lists, int32_t n, int32_t prot,
+                                         int64_t budget, void* workspace) {
+  const int64_t m = n - prot;
+  const bool levels = num_lists > 0 && m > 0 && budget > 0 && budget < num_lists * m;
+  return levels ? static_cast<uint32_t*>(workspace) + kHist0 : nullptr;
+}
+
+hipError_t launch_select_global_init(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                     int64_t num_lists, int32_t n, int32_t prot, int64_t budget,
+                                     void* workspace, hipStream_t stream) {
+  if (num_lists == 0) return hipSuccess;
+  const GlobalArgs a = global_args(kept_idx, kept_ld, kept_count, nullptr, n, num_lists, n, prot,
+                                   budget, workspace);
   hipLaunchKernelGGL(global_init_kernel, dim3((unsigned)num_lists), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned items = (unsigned)M;
+  return hipGetLastError();
+}
+
+hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
+                                const float* scores, int64_t ld, int64_t num_lists, int32_t n,
+                                int32_t prot, int64_t budget, void* workspace,
+                                hipStream_t stream, bool first_level_done) {
+  if (num_lists == 0) return hipSuccess;
+  const GlobalArgs a = global_args(kept_idx, kept_ld, kept_count, scores, ld, num_lists, n, prot,
+                                   budget, workspace);
+  hipError_t e;
+  if (!first_level_done) {
+    hipLaunchKernelGGL(global_init_kernel, dim3((unsigned)num_lists), dim3(kThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const unsigned items = (unsigned)(num_lists * a.chunks);
   if (items == 0 || a.mode == kNone) return hipSuccess;  // the prompts are the whole result
   const int levels = (a.mode == kNormal) ? 3 : 0;
-  for (int lvl = 0; lvl < levels; ++lvl) {
+  for (int lvl = (first_level_done ? 1 : 0); lvl < levels; ++lvl) {
     hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -220,6 +220,16 @@ def score(st: RoundState, round_id: int, stream=None):
                                  c.G, c.Hg, n, c.prot, stream)
 
 
+def score_select(st: RoundState, round_id: int, stream=None):
+    """Weighted score and global top-B in one call (the scorer fills the first radix level)."""
+    c, n = st.cfg, st.n
+    st.budget = B.kvevict_score_select_global(st.kept, st.kept.shape[1], st.kept_count, st.scores,
+                                              st.scores.shape[1], st.beta, st.vnorm, n * c.Hg,
+                                              c.Hg, 1, st.weights, c.win_width, st.win_begin,
+                                              st.win_count, c.L, c.H, c.G, c.Hg, n, c.prot, c.p,
+                                              st.workspace, st.workspace_bytes, stream)
+
+
 def select(st: RoundState, stream=None):
     c = st.cfg
     lists = st.scores.shape[0]
@@ -284,6 +294,8 @@ def phases(cfg: RoundConfig):
         return [("pages", pages_round)]
     if cfg.fused:
         return [("fused", fused_round)]
+    if cfg.fuse_score:
+        return [("score_select", score_select), ("compact", lambda st, rid: compact(st))]
     return [("score", score), ("select", lambda st, rid: select(st)),
             ("compact", lambda st, rid: compact(st))]
 
@@ -296,6 +308,9 @@ def run_round(st: RoundState, round_id: int = 0, stream=None):
         pages_round(st, round_id, stream)
     elif st.cfg.fused:
         fused_round(st, round_id, stream)
+    elif st.cfg.fuse_score:
+        score_select(st, round_id, stream)
+        compact(st, stream)
     else:
         score(st, round_id, stream)
         select(st, stream)

@@ -31,6 +31,7 @@ def test_exports_every_declared_symbol():
                           "kvevict_reduce_max_heads", "kvevict_score_keydiff",
                           "kvevict_compact_inplace", "kvevict_evict_random_inplace",
                           "kvevict_evict_pages_random", "kvevict_select_random",
+                          "kvevict_score_select_global",
                           "kvevict_select_global", "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
@@ -110,6 +111,39 @@ def test_select_global_workspace_protocol_and_validation():
                   0, 0.5, FAKE, ctypes.byref(size), None) == B.KVEVICT_ERR_INVALID_ARG  # > 2^31
     assert status("kvevict_select_global", FAKE, 32768, FAKE, None, FAKE, 32768, 64, 32768, 256,
                   0.25, FAKE, None, None) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_score_select_global_validation():
+    """The fused weighted score + global top-B checks both calls' arguments and follows the
+    select's workspace protocol with L*H lists."""
+    L, H, G, Hg, n, prot = 16, 4, 48, 48, 32768, 256
+    wb = (ctypes.c_int32 * L)(*[max(0, 3 * l - 3) for l in range(L)])
+    wc = (ctypes.c_int32 * L)(*[3 * l + 3 - max(0, 3 * l - 3) for l in range(L)])
+    size = ctypes.c_size_t(0)
+
+    def call(*, L=L, wb=wb, wc=wc, n=n, prot=prot, ld=n, kept_ld=n, p=0.25, ws=FAKE, sz=None):
+        return status("kvevict_score_select_global", FAKE, kept_ld, FAKE, None, FAKE, ld, FAKE,
+                      FAKE, n * Hg, Hg, 1, FAKE, 6, wb, wc, L, H, G, Hg, n, prot, p, ws,
+                      ctypes.byref(size) if sz is None else sz, None)
+
+    assert call(ws=None) == B.KVEVICT_OK  # workspace query
+    assert size.value == B.kvevict_select_global_workspace(L * H, n, prot, p=0.25)
+    need = size.value
+    size.value = need - 1
+    assert call() == B.KVEVICT_ERR_WORKSPACE
+    size.value = need
+    for p in (-0.1, 1.5, float("nan")):
+        assert call(p=p) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(kept_ld=n - 1) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(ld=n - 1) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(prot=n + 1) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(L=65) == B.KVEVICT_ERR_INVALID_ARG
+    bad = (ctypes.c_int32 * L)(*[7] * L)  # 7 > w_slots = 6
+    assert call(wc=bad) == B.KVEVICT_ERR_INVALID_ARG
+    assert call(wb=None) == B.KVEVICT_ERR_INVALID_ARG
+    assert status("kvevict_score_select_global", FAKE, n, FAKE, None, FAKE, n, FAKE, FAKE, n * Hg,
+                  Hg, 1, FAKE, 6, wb, wc, L, H, G, Hg, n, prot, 0.25, FAKE, None,
+                  None) == B.KVEVICT_ERR_INVALID_ARG  # no workspace size
 
 
 def test_compact_validation():

@@ -381,6 +381,54 @@ def test_score_weighted(G, L, H, Hg, n, prot, width):
     say(f"  bit-identical fraction {same:.6f}")
 
 
+@pytest.mark.parametrize("G,L,H,Hg,n,prot,width,p", [
+    (48, 16, 4, 48, 3000, 256, 6, 0.25),   # the GateSight shape at a short context
+    (12, 4, 6, 70, 900, 37, 6, 0.4),       # H > 4 and Hg > 48: several launches and passes
+    (60, 20, 2, 8, 500, 5, 6, 0.1),        # more than 16 attention layers
+    (9, 3, 1, 5, 64, 64, 4, 0.5),          # all protected: no candidates
+    (12, 4, 4, 48, 300, 20, 6, 0.0),       # B = 0: prompts only
+    (12, 4, 4, 48, 300, 20, 6, 1.0),       # every candidate kept
+    (12, 4, 4, 16, 20000, 100, 6, 0.3),    # several 8192-candidate items per list
+])
+def test_score_select_global(G, L, H, Hg, n, prot, width, p):
+    """The fused weighted score + global top-B equals the two calls bit for bit (scores, kept
+    indices, counts, B) and the oracle's top-B of those scores."""
+    say(f"score_select_global G={G} L={L} H={H} Hg={Hg} n={n} prot={prot} p={p}")
+    beta, vnorm, w, begins, counts = weighted_case(G, L, H, Hg, n, prot, width, seed=G + n)
+    lists, ld, kept_ld = L * H, n + 1, n + 2
+    db, dv, dw = (torch.from_numpy(x).to(DEV) for x in (beta, vnorm, w))
+    wsb = B.kvevict_select_global_workspace(lists, n, prot, ld=ld, kept_ld=kept_ld, p=p)
+
+    def outputs():
+        return (torch.full((lists, ld), float("nan"), dtype=torch.float32, device=DEV),
+                torch.full((lists, kept_ld), -3, dtype=torch.int32, device=DEV),
+                torch.full((lists,), -1, dtype=torch.int32, device=DEV),
+                torch.full((max(wsb, 256),), 0xA5, dtype=torch.uint8, device=DEV))
+
+    s2, k2, c2, ws2 = outputs()
+    B.kvevict_score_weighted(s2, ld, db, dv, n * Hg, Hg, 1, dw, width, begins, counts, L, H, G, Hg,
+                             n, prot)
+    b2 = B.kvevict_select_global(k2, kept_ld, c2, s2, ld, lists, n, prot, p, ws2, wsb)
+    s1, k1, c1, ws1 = outputs()
+    for call in range(2):  # the second call finds the first one's workspace
+        b1 = B.kvevict_score_select_global(k1, kept_ld, c1, s1, ld, db, dv, n * Hg, Hg, 1, dw,
+                                           width, begins, counts, L, H, G, Hg, n, prot, p, ws1,
+                                           wsb)
+        torch.cuda.synchronize()
+        assert b1 == b2
+        assert torch.equal(s1.view(torch.int32), s2.view(torch.int32)), call  # bit for bit
+        assert torch.equal(c1, c2) and torch.equal(k1, k2), call
+    sc = to_np(s1)[:, :n]
+    want_kept, want_counts, want_B = oracle.select_global(sc, prot, p)
+    assert b1 == want_B
+    got_c, got_k = to_np(c1), to_np(k1)
+    assert np.array_equal(got_c, want_counts)
+    for l in range(lists):
+        c = want_counts[l]
+        assert np.array_equal(got_k[l, :c], want_kept[l, :c]), l
+        assert np.all(got_k[l, c:] == -3), l
+
+
 def test_score_weighted_interleaved_signals():
     """The page's interleaved [G, n, Hg, 3] signal tensor (beta, g, |v|) through the stride arguments."""
     G, L, H, Hg, n, prot, width = 12, 4, 4, 48, 333, 20, 6

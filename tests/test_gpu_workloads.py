@@ -220,6 +220,41 @@ def test_global_round():
     free()
 
 
+def test_global_fused_round_matches_three_calls():
+    """The GateSight-shaped round with the weighted score and the top-B in one call: scores,
+    budget, counts, kept indices and compacted rows equal the three-call round's, bit for
+    bit, and the kept set is the oracle's top-B of those scores."""
+    say("global fused round: allocating")
+    st3 = rounds.make_state(configs.GLOBAL, DEV)
+    rounds.run_round(st3)
+    torch.cuda.synchronize()
+    want = {k: getattr(st3, k).clone() for k in ("scores", "kept", "kept_count")}
+    want_k, want_v, want_budget = st3.k_dst.clone(), st3.v_dst.clone(), st3.budget
+    del st3
+    free()
+    cfg = configs.GLOBAL_FUSED
+    st = rounds.make_state(cfg, DEV)
+    for rep in range(2):
+        rounds.run_round(st)
+        torch.cuda.synchronize()
+        assert st.budget == want_budget == 520192
+        for k, v in want.items():
+            got = getattr(st, k)
+            assert torch.equal(got.view(torch.int32), v.view(torch.int32)), (k, rep)
+        assert torch.equal(st.k_dst.view(torch.int16), want_k.view(torch.int16))
+        assert torch.equal(st.v_dst.view(torch.int16), want_v.view(torch.int16))
+        assert int(st.errors.item()) == 0
+    say("global fused round: the oracle's top-B of the GPU scores")
+    s = st.scores.cpu().numpy()
+    want_kept, want_counts, _ = oracle.select_global(s[:, :cfg.n], cfg.prot, cfg.p)
+    assert np.array_equal(st.kept_count.cpu().numpy(), want_counts)
+    got_kept = st.kept.cpu().numpy()
+    for l in range(cfg.L * cfg.H):
+        assert np.array_equal(got_kept[l, :want_counts[l]], want_kept[l, :want_counts[l]]), l
+    del st, want, want_k, want_v
+    free()
+
+
 def test_longgen_rounds_replayed_by_oracle():
     """30 consecutive rounds (K=3072, r=64, prot=557) on one request's 288 lists, replayed
     round by round by the oracle; survival of the first cache's entries follows q^t."""
@@ -525,7 +560,7 @@ def test_longgen_full_size_two_rounds_sampled(base):
     free()
 
 
-@pytest.mark.parametrize("name", ["tiny", "global", "paged_shared"])
+@pytest.mark.parametrize("name", ["tiny", "global", "global_fused", "paged_shared"])
 def test_graph_replay_matches_eager(name):
     """A round captured as a HIP graph gives the eager round's outputs on every replay,
     with eager work (clearing every output) and synchronisations between the replays."""
