@@ -8,14 +8,16 @@
 //             histograms and the done counter
 //   hist x3   radix histograms of the 11/11/10-bit digits of rank_key(score),
 //             restricted to the keys matching the digits chosen so far.  Each
-//             workgroup of level l derives those digits itself from the
-//             finished histograms of levels < l (the same computation in every
-//             workgroup, so no workgroup has to wait for another); it returns
-//             at once if an earlier level took its bucket whole.
-//   count     per-item counts of keys > T and == T, T the threshold key
-//             derived from the three histograms; with many items the last
+//             workgroup of level l derives the digit of level l - 1 itself
+//             from that level's finished histogram and the bucket recorded by
+//             the previous kernel (the same computation in every workgroup,
+//             so no workgroup has to wait for another), and workgroup 0
+//             records the narrowed bucket; a workgroup returns at once if an
+//             earlier level took its bucket whole.
+//   count     derives the last digit, hence the threshold key T, and writes
+//             per-item counts of keys > T and == T; with many items the last
 //             count workgroup scans them once into per-item offsets
-//   emit      the item's offset (ties at T go to the lowest list*n + i): the
+//   emit      reads T; the item's offset (ties at T go to the lowest list*n + i): the
 //             sums over the items before it, or the scanned offset; the
 //             per-list kept counts; a ballot/mbcnt chronological emit.
 // All counts are integer atomics or scans, so the result is deterministic.
@@ -50,6 +52,7 @@ constexpr int64_t kHist0 = 0;       // 2048 bins, key bits [21, 32)
 constexpr int64_t kHist1 = 2048;    // 2048 bins, key bits [10, 21)
 constexpr int64_t kHist2 = 4096;    // 1024 bins, key bits [0, 10)
 constexpr int64_t kDone = 5184;     // finished workgroups of the count kernel
+constexpr int64_t kState = 5188;    // the bucket after levels [0, k): 4 words at kState + 4 (k - 1)
 constexpr int64_t kArrays = 5248;   // gt[M], eq[M], eqx[M], S[M+1]
 
 enum Mode : int32_t { kNormal = 0, kNone = 1, kAll = 2 };
@@ -126,73 +129,81 @@ __device__ __forceinline__ void load_keys(const float* row, int32_t i0, int32_t 
   }
 }
 
-// Bins of the levels below `levels` held by this thread, top bins first:
-// thread t holds bins [top - per, top) of a level, top = bins - per * t.
-struct HistRegs {
-  uint32_t h[3][kBinsPerThread];
-};
-__device__ __forceinline__ void load_hists(const uint32_t* ws, int levels, HistRegs* r) {
+// The bins of level lvl held by this thread, top bins first: thread t holds
+// bins [top - per, top), top = bins - per * t.
+__device__ __forceinline__ void load_level_bins(const uint32_t* ws, int lvl, uint32_t* h) {
+  const Level L = level_of(lvl);
+  const uint32_t per = L.bins / kThreads;
+  const uint32_t top = L.bins - per * threadIdx.x;
 #pragma unroll
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    const Level L = level_of(lvl);
-    const uint32_t per = L.bins / kThreads;
-    const uint32_t top = L.bins - per * threadIdx.x;
-#pragma unroll
-    for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b)
-      r->h[lvl][b] = (lvl < levels && b < per) ? ws[L.off + top - 1u - b] : 0u;
-  }
+  for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b)
+    h[b] = (b < per) ? ws[L.off + top - 1u - b] : 0u;
 }
 
-// The digits chosen by levels [0, levels): prefix and mask of the bucket that
-// holds the budget-th best key, how many keys of that bucket are still to be
-// kept, and whether the bucket is kept whole (later levels are then skipped).
+// The digits chosen by levels [0, k): prefix and mask of the bucket that holds
+// the budget-th best key, how many keys of that bucket are still to be kept,
+// and whether the bucket is kept whole (later levels are then skipped).
 struct Thr {
   uint32_t prefix, mask, remaining, whole;
 };
-// s_state holds one 4-word slot per level, so no slot is rewritten while
-// another thread may still read it.
-__device__ Thr resolve_levels(const HistRegs& r, int levels, uint32_t budget, uint32_t* s_scan,
-                              uint32_t (*s_state)[4]) {
-  Thr t{0u, 0u, budget, 0u};
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    if (lvl >= levels || t.whole) break;
-    const Level L = level_of(lvl);
-    const uint32_t per = L.bins / kThreads;
-    const uint32_t top = L.bins - per * (uint32_t)tid;
-    uint32_t c = 0u;
-#pragma unroll
-    for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) c += r.h[lvl][b];
-    uint32_t* st = s_state[lvl];
-    if (tid == 0) {  // kept if no bin crosses (cannot happen: the bucket holds >= remaining)
-      st[0] = t.prefix;
-      st[1] = t.mask;
-      st[2] = t.remaining;
-      st[3] = t.whole;
-    }
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
-    const uint32_t excl = incl - c;
-    if (excl < t.remaining && incl >= t.remaining) {
-      uint32_t acc = excl;
-#pragma unroll
-      for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) {
-        const uint32_t h = r.h[lvl][b];
-        if (b < per && acc < t.remaining && acc + h >= t.remaining) {
-          const uint32_t left = t.remaining - acc;
-          st[0] = t.prefix | ((top - 1u - b) << L.shift);
-          st[1] = t.mask | ((L.bins - 1u) << L.shift);
-          st[2] = left;
-          st[3] = (left == h) ? 1u : 0u;  // the bucket is kept whole
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();  // thread 0's write came before the scan's barriers, the crossing one's after
-    t = Thr{st[0], st[1], st[2], st[3]};
+
+// The bucket after levels [0, k), k >= 1, is resolved once per kernel: every
+// workgroup of the kernel that reads the finished histogram of level k - 1
+// derives it (the same computation in each, so none waits for another) and
+// workgroup 0 records it for the later kernels of the call, which read it with
+// plain loads after the kernel boundary.
+__device__ __forceinline__ Thr load_resolved(const GlobalArgs& a, int k) {
+  if (k == 0) return Thr{0u, 0u, a.budget, 0u};
+  const uint32_t* s = a.ws + kState + 4 * (k - 1);
+  return Thr{s[0], s[1], s[2], s[3]};
+}
+__device__ __forceinline__ void store_resolved(const GlobalArgs& a, int k, const Thr& t) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    uint32_t* s = a.ws + kState + 4 * (k - 1);
+    s[0] = t.prefix;
+    s[1] = t.mask;
+    s[2] = t.remaining;
+    s[3] = t.whole;
   }
-  return t;
+}
+
+// Narrows the bucket t of levels [0, lvl) by the digit of level lvl, whose
+// bins this thread holds in h.  t is the same in every thread, so a bucket
+// already kept whole skips the level in all of them.
+__device__ Thr resolve_level(const uint32_t* h, int lvl, Thr t, uint32_t* s_scan, uint32_t* st) {
+  if (t.whole) return t;
+  const int tid = threadIdx.x;
+  const Level L = level_of(lvl);
+  const uint32_t per = L.bins / kThreads;
+  const uint32_t top = L.bins - per * (uint32_t)tid;
+  uint32_t c = 0u;
+#pragma unroll
+  for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) c += h[b];
+  if (tid == 0) {  // kept if no bin crosses (cannot happen: the bucket holds >= remaining)
+    st[0] = t.prefix;
+    st[1] = t.mask;
+    st[2] = t.remaining;
+    st[3] = t.whole;
+  }
+  uint32_t total;
+  const uint32_t incl = block_inclusive_scan<kThreads>(c, s_scan, &total);
+  const uint32_t excl = incl - c;
+  if (excl < t.remaining && incl >= t.remaining) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBinsPerThread; ++b) {
+      if (b < per && acc < t.remaining && acc + h[b] >= t.remaining) {
+        const uint32_t left = t.remaining - acc;
+        st[0] = t.prefix | ((top - 1u - b) << L.shift);
+        st[1] = t.mask | ((L.bins - 1u) << L.shift);
+        st[2] = left;
+        st[3] = (left == h[b]) ? 1u : 0u;  // the bucket is kept whole
+      }
+      acc += h[b];
+    }
+  }
+  __syncthreads();  // thread 0's write came before the scan's barriers, the crossing one's after
+  return Thr{st[0], st[1], st[2], st[3]};
 }
 
 // Threshold key T and how many keys equal to T are kept.
@@ -219,15 +230,19 @@ __global__ __launch_bounds__(kThreads) void global_init_kernel(GlobalArgs a) {
 __global__ __launch_bounds__(kThreads) void global_hist_kernel(GlobalArgs a, int lvl) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_state[3][4];
+  __shared__ uint32_t s_state[4];
   int64_t list;
   int32_t i0, i1;
   item_range(a, blockIdx.x, &list, &i0, &i1);
-  HistRegs r;
-  load_hists(a.ws, lvl, &r);
+  Thr t = load_resolved(a, lvl > 0 ? lvl - 1 : 0);
+  uint32_t h[kBinsPerThread];
+  if (lvl > 0) load_level_bins(a.ws, lvl - 1, h);
   uint32_t keys[kKeysPerThread];
-  load_keys(a.scores + list * a.ld, i0, i1, keys);  // in flight while the digits resolve
-  const Thr t = resolve_levels(r, lvl, a.budget, s_scan, s_state);
+  load_keys(a.scores + list * a.ld, i0, i1, keys);  // in flight while the digit resolves
+  if (lvl > 0) {
+    t = resolve_level(h, lvl - 1, t, s_scan, s_state);
+    store_resolved(a, lvl, t);
+  }
   if (t.whole) return;  // an earlier level took its bucket whole
   const Level L = level_of(lvl);
   for (uint32_t b = threadIdx.x; b < L.bins; b += kThreads) s_hist[b] = 0u;
@@ -325,7 +340,7 @@ __device__ __forceinline__ void count_item(const uint32_t* keys, int32_t i0, int
 // offsets and writes the per-list counts.
 __global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a, int levels) {
   __shared__ uint32_t s_scan[kWaves];
-  __shared__ uint32_t s_state[3][4];
+  __shared__ uint32_t s_state[4];
   __shared__ uint32_t s_flag;
   const int64_t f = blockIdx.x;
   const int64_t M = a.num_lists * a.chunks;
@@ -336,11 +351,15 @@ __global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a, in
   int64_t list;
   int32_t i0, i1;
   item_range(a, f, &list, &i0, &i1);
-  HistRegs r;
-  load_hists(a.ws, levels, &r);
+  Thr t = load_resolved(a, levels > 0 ? levels - 1 : 0);
+  uint32_t h[kBinsPerThread];
+  if (levels > 0) load_level_bins(a.ws, levels - 1, h);
   uint32_t keys[kKeysPerThread];
   load_keys(a.scores + list * a.ld, i0, i1, keys);
-  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
+  if (levels > 0) {
+    t = resolve_level(h, levels - 1, t, s_scan, s_state);
+    store_resolved(a, levels, t);
+  }
   uint32_t thr, need_eq;
   threshold_of(a, t, &thr, &need_eq);
   uint32_t gt, eq;
@@ -388,18 +407,16 @@ __global__ __launch_bounds__(kThreads) void global_count_kernel(GlobalArgs a, in
 __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int levels) {
   __shared__ uint32_t s_scan[kWaves];
   __shared__ uint32_t s_cnt[4 * kKeysPerThread * kWaves];
-  __shared__ uint32_t s_state[3][4];
   const int64_t f = blockIdx.x;
   const int64_t M = a.num_lists * a.chunks;
   const bool direct = M <= kDirectPrefixItems;
   int64_t list;
   int32_t i0, i1;
   item_range(a, f, &list, &i0, &i1);
-  // everything this workgroup reads is issued up front: the histograms, the
-  // item's keys and the per-item counts or offsets written by earlier kernels
-  // (plain loads: the kernel boundary makes them visible)
-  HistRegs r;
-  load_hists(a.ws, levels, &r);
+  // everything this workgroup reads is issued up front: the resolved bucket,
+  // the item's keys and the per-item counts or offsets written by earlier
+  // kernels (plain loads: the kernel boundary makes them visible)
+  const Thr t = load_resolved(a, levels);
   uint32_t keys[kKeysPerThread];
   load_keys(a.scores + list * a.ld, i0, i1, keys);
   const uint32_t* gt_arr = a.ws + kArrays;
@@ -419,7 +436,6 @@ __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int
     eq0 = gt_arr[2 * M + f];                     // eqx[f]
     offset = gt_arr[3 * M + f] - gt_arr[3 * M + ls];  // S[f] - S[ls]
   }
-  const Thr t = resolve_levels(r, levels, a.budget, s_scan, s_state);
   uint32_t thr, need_eq;
   threshold_of(a, t, &thr, &need_eq);
   if (direct) {
