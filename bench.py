@@ -15,7 +15,9 @@ prices the dominant kernel (the K/V gather) at its algorithmic bytes: the
 kept K and V rows, each read once and written once.  Workloads whose round
 takes under 1 ms and leaves its inputs intact are also replayed from a HIP
 graph of ten rounds (graph_ms_per_round): the device time without the host
-launch path.
+launch path.  Rounds with a separate select are also timed over selection +
+compaction alone as one interval (select_compact: eager, and from a HIP
+graph), with no event between the select and the gather.
 """
 
 from __future__ import annotations
@@ -225,6 +227,45 @@ def graph_replay_ms(torch, rounds, st, steps):
     return e0.elapsed_time(e1) / (reps * GRAPH_ROUNDS)
 
 
+SELECT_PHASES = ("select", "draw_select", "compact")
+
+
+def select_compact_ms(torch, rounds, st, steps):
+    """Selection + compaction (every phase of the round after a standalone scorer) timed as
+    one interval, with no event between the select and the gather: eager, `steps`
+    repetitions between two events; and replayed from a HIP graph of GRAPH_ROUNDS
+    repetitions, which also takes the host launch path out.  The scores stay those of
+    the last full round, so every repetition does the same work."""
+    fns = [fn for name, fn in rounds.phases(st.cfg) if name in SELECT_PHASES]
+    for s in range(2):
+        for fn in fns:
+            fn(st, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        for fn in fns:
+            fn(st, s)
+    e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(GRAPH_ROUNDS):
+            for fn in fns:
+                fn(st, s)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // GRAPH_ROUNDS)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return eager, e0.elapsed_time(e1) / (reps * GRAPH_ROUNDS)
+
+
 def traffic_for(kv_bytes):
     """Measured HBM bytes per launch of the gather, if the counters match this source."""
     try:
@@ -369,6 +410,15 @@ def main():
             g_ms = graph_replay_ms(torch, rounds, r["state"], max(steps, 10 * GRAPH_ROUNDS))
             entry["graph_ms_per_round"] = g_ms
             entry["graph_rounds_per_s"] = 1e3 / g_ms
+        if (cfg.rounds == 1 and not (cfg.inplace or cfg.page_draw or cfg.fused or cfg.fuse_score)
+                and any(p in ("select", "draw_select") for p, _ in rounds.phases(cfg))):
+            sc_eager, sc_graph = select_compact_ms(torch, rounds, r["state"], max(steps, 20))
+            entry["select_compact"] = {
+                "ms": round(sc_eager, 4), "graph_ms": round(sc_graph, 4),
+                "kv_gbps": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9,
+                "frac_of_peak": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "frac_of_peak_graph": r["kv_bytes"] / (sc_graph * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            }
         if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
         if cfg.select == "layers":
@@ -422,6 +472,7 @@ def main():
             "algorithmic_bytes": e["kv_bytes_per_round"],
         },
         "round_ms_p10_p50_p90": e["round_ms_p10_p50_p90"],
+        "select_compact": e.get("select_compact"),
         "algorithmic_bytes_per_round": e["algorithmic_bytes_per_round"],
         "dtod_copy": e["dtod_copy"],
         "cpu_baseline": e.get("cpu"),
