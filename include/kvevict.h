@@ -101,7 +101,7 @@ typedef struct kvevict_kv_desc {
  *         drawn from the head-0 stream, so it equals head 0's per-head draw.
  * Row entries i < prot are +inf; entries prot <= i < n get the Philox draw of
  * (seed, req, layer, head, round, i) described above; entries >= n untouched.
- * Requires 0 <= prot <= n, num_requests < 2^32, L >= 1, H >= 1.
+ * Requires 0 <= prot <= n, num_requests < 2^32, L >= 1, H >= 1, lists < 2^31.
  */
 kvevict_status kvevict_score_random(float* scores, int64_t ld, int64_t num_requests, int32_t L,
                                     int32_t H, int32_t n, int32_t prot, uint64_t seed,
@@ -145,7 +145,8 @@ kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* be
  * cos = 0; a zero score is written as +0.  A paged row whose page id falls
  * outside the pool reads as zeros.
  * Requires D = head_dim in {8, 16, 32, ..., 512}, 0 <= prot <= n <= rows of a
- * list, n * D / 8 < 2^31, ld >= n.  KVEVICT_ERR_UNSUPPORTED for other D.
+ * list, n * D / 8 < 2^31, ld >= n, num_groups*H < 2^31.  KVEVICT_ERR_UNSUPPORTED
+ * for other D.
  */
 kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv_desc* keys,
                                      const void* k_cache, int64_t num_groups, int32_t n,
@@ -172,7 +173,7 @@ kvevict_status kvevict_select_topk(int32_t* kept_idx, int64_t kept_ld, const flo
  * scores are drawn on chip and never stored.
  * kept_idx  device int32 out [lists][kept_ld], kept_ld >= K; lists and their
  *           numbering as in kvevict_score_random.
- * Requires 0 <= prot <= K <= n, num_requests < 2^32, L >= 1, H >= 1.
+ * Requires 0 <= prot <= K <= n, num_requests < 2^32, L >= 1, H >= 1, lists < 2^31.
  */
 kvevict_status kvevict_select_random(int32_t* kept_idx, int64_t kept_ld, int64_t num_requests,
                                      int32_t L, int32_t H, int32_t n, int32_t K, int32_t prot,
@@ -194,7 +195,7 @@ kvevict_status kvevict_select_random(int32_t* kept_idx, int64_t kept_ld, int64_t
  * layer_budget  HOST int32 [L] (for example from kvevict_layer_power_budget),
  *               each in [0, n - prot].
  * Requires 1 <= L <= 64, num_groups a multiple of L, 0 <= prot <= n, ld >= n,
- * kept_ld >= prot + max(layer_budget).
+ * kept_ld >= prot + max(layer_budget), num_groups*H < 2^31.
  */
 kvevict_status kvevict_select_topk_layers(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count,
                                           const float* scores, int64_t ld, int64_t num_groups,
@@ -227,7 +228,7 @@ kvevict_status kvevict_layer_power_budget(const float* gate, int32_t L, int32_t 
  * score ranks best (NaN as -inf, -0 equal to +0; the lowest such head, whose
  * bits are copied).  The shared rows then feed kvevict_select_topk as one list
  * per group and kvevict_compact with idx_lists_per_group = 1.
- * Requires H >= 1, ld >= n, shared_ld >= n.
+ * Requires H >= 1, ld >= n, shared_ld >= n, num_groups*H < 2^31.
  */
 kvevict_status kvevict_reduce_max_heads(float* shared, int64_t shared_ld, const float* scores,
                                         int64_t ld, int64_t num_groups, int32_t H, int32_t n,
@@ -294,7 +295,7 @@ kvevict_status kvevict_score_select_global(
  *              id falls outside its store is skipped and adds 1, and each
  *              index list whose count is outside [0, K] adds 1 and is clamped
  *              to that range.  May be NULL.
- * Requires K <= dst rows per list, kept_ld >= K.
+ * Requires K <= dst rows per list, kept_ld >= K, num_groups*H < 2^31.
  */
 kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,
                                const kvevict_kv_desc* dst, void* k_dst, void* v_dst,

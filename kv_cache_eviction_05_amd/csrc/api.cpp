@@ -20,6 +20,10 @@ constexpr int64_t kUint32Max = 4294967295LL;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// a * b <= limit for a, b >= 0 and limit >= 0, decided without forming a
+// product that could overflow.
+bool prod_le(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
+
 kvevict_status hip_status(hipError_t e) { return e == hipSuccess ? KVEVICT_OK : KVEVICT_ERR_HIP; }
 
 int log2_exact(int32_t v) {
@@ -45,6 +49,7 @@ kvevict_status check_store(const kvevict_kv_desc* d, const void* k, const void* 
   if (d->capacity < 0) return KVEVICT_ERR_INVALID_ARG;
   if (d->layout == KVEVICT_LAYOUT_CONTIG) {
     out->paged = 0;
+    if (!prod_le(d->capacity, d->head_dim, INT64_MAX)) return KVEVICT_ERR_INVALID_ARG;
     if (d->list_stride < d->capacity * d->head_dim) return KVEVICT_ERR_INVALID_ARG;
     if (d->list_stride % 8 != 0) return KVEVICT_ERR_ALIGNMENT;
     out->list_stride_v = d->list_stride / 8;
@@ -75,9 +80,10 @@ kvevict_status kvevict_score_random(float* scores, int64_t ld, int64_t num_reque
                                     uint32_t round, int32_t shared_draw, hipStream_t stream) {
   if (num_requests < 0 || num_requests > 0xffffffffll || L < 1 || H < 1) return KVEVICT_ERR_INVALID_ARG;
   if (n < 0 || prot < 0 || prot > n || ld < n) return KVEVICT_ERR_INVALID_ARG;
-  const int64_t lists = num_requests * L * (shared_draw ? 1 : H);
+  const int64_t per_request = (int64_t)L * (shared_draw ? 1 : H);
+  if (!prod_le(num_requests, per_request, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_requests * per_request;
   if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
-  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_score_random(scores, ld, lists, L, H, n, prot, seed, round,
                                                  shared_draw != 0, stream));
 }
@@ -144,8 +150,8 @@ kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv
   if (vpr > 64 || (vpr & (vpr - 1)) != 0) return KVEVICT_ERR_UNSUPPORTED;  // D in {8, 16, ..., 512}
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
   if ((int64_t)n * vpr > kInt32Max) return KVEVICT_ERR_INVALID_ARG;  // 32-bit row offsets
+  if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   const int64_t lists = num_groups * H;
-  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
   if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_score_keydiff(scores, ld, sv, k_cache, D, H, lists, n, prot,
                                                   stream));
@@ -165,8 +171,8 @@ kvevict_status kvevict_select_topk_layers(int32_t* kept_idx, int64_t kept_ld,
     most = layer_budget[l] > most ? layer_budget[l] : most;
   }
   if (kept_ld < prot + most) return KVEVICT_ERR_INVALID_ARG;
+  if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   const int64_t lists = num_groups * H;
-  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
   if (lists > 0 && (!kept_idx || !kept_count || !scores)) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_select_topk(kept_idx, kept_ld, kept_count, scores, ld, lists,
                                                 n, prot, prot, L, H, layer_budget, stream));
@@ -176,6 +182,7 @@ kvevict_status kvevict_reduce_max_heads(float* shared, int64_t shared_ld, const 
                                         int64_t ld, int64_t num_groups, int32_t H, int32_t n,
                                         hipStream_t stream) {
   if (num_groups < 0 || H < 1 || n < 0 || ld < n || shared_ld < n) return KVEVICT_ERR_INVALID_ARG;
+  if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups > 0 && n > 0 && (!shared || !scores)) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(
       kvevict::launch_reduce_max_heads(shared, shared_ld, scores, ld, num_groups, H, n, stream));
@@ -265,7 +272,7 @@ static kvevict_status check_global(int32_t* kept_idx, int64_t kept_ld, int32_t* 
   if (!workspace_bytes) return KVEVICT_ERR_INVALID_ARG;
   if (num_lists < 0 || n < 0 || prot < 0 || prot > n || ld < n || kept_ld < n) return KVEVICT_ERR_INVALID_ARG;
   if (!(p >= 0.0 && p <= 1.0)) return KVEVICT_ERR_INVALID_ARG;  // also rejects NaN
-  if (num_lists * (int64_t)n > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  if (!prod_le(num_lists, n, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   const size_t need = kvevict::select_global_workspace_bytes(num_lists, n, prot);
   if (!workspace) {
     *workspace_bytes = need;
@@ -351,6 +358,7 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
   st = check_store(dst, k_dst, v_dst, num_groups, &dv);
   if (st != KVEVICT_OK) return st;
   if (K > dv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   const int32_t D = src->head_dim;
   if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;  // one token row of all heads
@@ -383,8 +391,8 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
   if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;  // K and V are distinct stores
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
-  if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
-  if (sv.paged && num_groups * ((n + store->page_size - 1) / store->page_size) > kUint32Max)
+  if (!prod_le(num_groups, H, kInt32Max) || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if (sv.paged && !prod_le(num_groups, (n + store->page_size - 1) / store->page_size, kUint32Max))
     return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit
   return hip_status(kvevict::launch_compact_inplace(sv, k, v, D, H, kept_idx, kept_ld, kept_count,
                                                     K, n, num_groups, idx_lists_per_group,
@@ -412,9 +420,9 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
   if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
-  if (num_groups * H > kInt32Max || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if (!prod_le(num_groups, H, kInt32Max) || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
   if ((int64_t)(n - prot) + K > kvevict::kMaxFusedEntries) return KVEVICT_ERR_UNSUPPORTED;
-  if (sv.paged && num_groups * ((n + store->page_size - 1) / store->page_size) > kUint32Max)
+  if (sv.paged && !prod_le(num_groups, (n + store->page_size - 1) / store->page_size, kUint32Max))
     return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit
   return hip_status(kvevict::launch_evict_random_inplace(
       sv, k, v, D, H, num_groups, L, n, K, prot, seed, round, shared_draw != 0, kept_idx, kept_ld,
@@ -427,8 +435,9 @@ kvevict_status kvevict_select_random(int32_t* kept_idx, int64_t kept_ld, int64_t
                                      hipStream_t stream) {
   if (num_requests < 0 || num_requests > 0xffffffffll || L < 1 || H < 1) return KVEVICT_ERR_INVALID_ARG;
   if (prot < 0 || K < prot || n < K || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
-  const int64_t lists = num_requests * L * (shared_draw ? 1 : H);
-  if (lists > kInt32Max) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t per_request = (int64_t)L * (shared_draw ? 1 : H);
+  if (!prod_le(num_requests, per_request, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
+  const int64_t lists = num_requests * per_request;
   if (lists > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_draw_select(kept_idx, kept_ld, lists, L, H, n, K, prot, seed,
                                                 round, shared_draw != 0, stream));

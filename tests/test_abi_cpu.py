@@ -330,3 +330,40 @@ def test_select_random_validation():
     assert call(H=0) == B.KVEVICT_ERR_INVALID_ARG
     assert call(R=1 << 32) == B.KVEVICT_ERR_INVALID_ARG
     assert call(R=1 << 20, L=64, H=64) == B.KVEVICT_ERR_INVALID_ARG  # 2^32 lists
+
+
+def test_sizes_whose_products_overflow_are_rejected():
+    """List and page counts are products of caller sizes; each product is bounded without
+    being formed, so sizes whose product wraps a 64-bit integer are rejected, not launched."""
+    INV = B.KVEVICT_ERR_INVALID_ARG
+    big_req, big_l, big_h = (1 << 32) - 1, (1 << 31) - 1, (1 << 31) - 1
+    huge = 1 << 62
+    D, H = 128, 8
+    assert status("kvevict_score_random", FAKE, 16, big_req, big_l, big_h, 16, 0, 0, 0, 0,
+                  None) == INV
+    assert status("kvevict_score_random", FAKE, 16, big_req, big_l, big_h, 16, 0, 0, 0, 1,
+                  None) == INV
+    assert status("kvevict_select_random", FAKE, 16, big_req, big_l, big_h, 16, 16, 0, 0, 0, 0,
+                  None) == INV
+    keys = B.contig_desc(D, H, 1088)
+    assert status("kvevict_score_keydiff", FAKE, 1088, ctypes.byref(keys), FAKE, huge, 1088, 0,
+                  None) == INV
+    budget = (ctypes.c_int32 * 1)(8)
+    assert status("kvevict_select_topk_layers", FAKE, 16, FAKE, FAKE, 16, huge, 1, H, 16, 0,
+                  budget, None) == INV
+    assert status("kvevict_reduce_max_heads", FAKE, 16, FAKE, 16, huge, H, 16, None) == INV
+    ws = B._sz(0)
+    assert status("kvevict_select_global", FAKE, 16, FAKE, None, FAKE, 16, huge, 16, 0, 0.5,
+                  None, ctypes.byref(ws), None) == INV
+    src, dst = B.contig_desc(D, H, 1088), B.contig_desc(D, H, 1024)
+    assert status("kvevict_compact", ctypes.byref(src), FAKE, FAKE * 2, ctypes.byref(dst),
+                  FAKE * 3, FAKE * 4, FAKE, 1024, None, 1024, huge, H, None, None) == INV
+    store = B.contig_desc(D, H, 1088)
+    assert status("kvevict_compact_inplace", ctypes.byref(store), FAKE, FAKE * 2, FAKE, 1024,
+                  None, 1024, 1088, huge, H, None, None, None, None) == INV
+    assert status("kvevict_evict_random_inplace", ctypes.byref(store), FAKE, FAKE * 2, big_req,
+                  big_l, 1088, 1024, 0, 0, 0, 0, None, 0, None, None, None, None) == INV
+    # a contiguous store whose capacity * head_dim wraps
+    wrap = B.KvDesc(B.LAYOUT_CONTIG, D, H, 0, 1 << 60, 1 << 20, None, 0)
+    assert status("kvevict_compact", ctypes.byref(wrap), FAKE, FAKE * 2, ctypes.byref(dst),
+                  FAKE * 3, FAKE * 4, FAKE, 1024, None, 1024, 1, H, None, None) == INV
