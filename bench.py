@@ -319,7 +319,66 @@ def cpu_baseline(torch, cfg, st, seconds):
     frac = lists / cfg.lists
     return {"value": reps * frac / el, "unit": "rounds/s", "cores": threads, "kind": "oracle",
             "sample": f"{req} of {cfg.R} requests ({lists} of {cfg.lists} lists: score, select, "
-                      f"compact) x {reps} repetitions in {el:.1f} s on {threads} threads"}
+                      f"compact) x {reps} repetitions in {el:.1f} s on {threads} threads",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_single_thread(torch, cfg, st, min_seconds=2.0):
+    """The oracle on one host thread over the whole round of a small workload (the tiny
+    round, or the global round: weighted score, global top-B and compaction), on the same
+    inputs, downloaded first (download untimed)."""
+    import numpy as np
+
+    import oracle
+
+    def bits(t):
+        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    ks, vs = bits(st.k_src), bits(st.v_src)
+    kd = np.zeros(tuple(st.k_dst.shape), np.uint16)
+    vd = np.zeros_like(kd)
+    if cfg.select == "global":
+        beta, vnorm = st.beta.cpu().numpy(), st.vnorm.cpu().numpy()
+        w = st.weights.cpu().numpy()
+
+        def one_round():
+            s = oracle.score_weighted(beta, vnorm, w, st.win_begin, st.win_count, cfg.prot)
+            kept, counts, _ = oracle.select_global(s, cfg.prot, cfg.p)
+            oracle.compact({"list_stride": cfg.n * cfg.D}, ks, vs, {"list_stride": cfg.n * cfg.D},
+                           kd, vd, kept, cfg.n, cfg.D, cfg.H, 0, cfg.groups, ipg=cfg.H,
+                           kept_count=counts)
+        what = "weighted score, global top-B and compaction"
+    else:
+        def one_round():
+            s = oracle.score_random(cfg.L, cfg.H, cfg.n, cfg.prot, cfg.seed, 0, False, 0,
+                                    cfg.lists)
+            kept = oracle.select_topk(s, cfg.K, cfg.prot)
+            oracle.compact({"list_stride": cfg.n * cfg.D}, ks, vs, {"list_stride": cfg.K * cfg.D},
+                           kd, vd, kept, cfg.K, cfg.D, cfg.H, 0, cfg.groups, ipg=cfg.H)
+        what = "random score, top-K and compaction"
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_round()
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": reps / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole round ({what}) x {reps} in {el:.1f} s on 1 thread",
+            "cpu_model": cpu_model()}
 
 
 def dtod_copy(torch, kv_bytes, gather_gbps, reps=5):
@@ -419,6 +478,9 @@ def main():
                 "frac_of_peak": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                 "frac_of_peak_graph": r["kv_bytes"] / (sc_graph * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             }
+        if name in ("tiny", "global") and not args.no_cpu_baseline:
+            print(f"# cpu baseline on one thread (oracle): {name}", file=sys.stderr, flush=True)
+            entry["cpu_baseline_1_thread"] = cpu_single_thread(torch, cfg, r["state"])
         if cfg.select in ("global", "layers"):
             entry["budget"] = r["budget"]
         if cfg.select == "layers":
