@@ -20,6 +20,13 @@
 //   emit      reads T; the item's offset (ties at T go to the lowest list*n + i): the
 //             sums over the items before it, or the scanned offset; the
 //             per-list kept counts; a ballot/mbcnt chronological emit.
+// With at most kCollectItems items the third histogram gets no kernel of its
+// own: after two levels the count kernel resolves the second digit, counts per
+// item the keys above the 22-bit bucket and in it, adds the bucket's keys to
+// the last level's histogram and lists them (item, low 10 bits) while the
+// list has room; the emit resolves the last digit and takes the per-item
+// counts at T from the list, or, when too many keys share the bucket to list
+// them, recounts the items before its own that hold some.
 // All counts are integer atomics or scans, so the result is deterministic.
 //
 // Words passed between workgroups of one kernel (the per-item counts and the
@@ -53,7 +60,16 @@ constexpr int64_t kHist1 = 2048;    // 2048 bins, key bits [10, 21)
 constexpr int64_t kHist2 = 4096;    // 1024 bins, key bits [0, 10)
 constexpr int64_t kDone = 5184;     // finished workgroups of the count kernel
 constexpr int64_t kState = 5188;    // the bucket after levels [0, k): 4 words at kState + 4 (k - 1)
-constexpr int64_t kArrays = 5248;   // gt[M], eq[M], eqx[M], S[M+1]
+constexpr int64_t kCollected = 5200;  // keys of the 22-bit bucket the count kernel met
+constexpr int64_t kArrays = 5248;   // gt[M], eq[M], eqx[M], S[M+1], then the collect list
+static_assert(kState + 12 <= kCollected && kCollected < kArrays, "workspace words overlap");
+// The collect list: (item << 10) | low 10 key bits of each key in the bucket.
+constexpr uint32_t kCollectCap = 4096;
+// Items up to which the two-level flow runs.  Its fallback (too many keys in
+// the bucket to list) recounts up to all earlier items in every emit
+// workgroup, so its cost grows with the square of the items.
+constexpr int64_t kCollectItems = 256;
+static_assert(kCollectItems << 10 < (1LL << 32), "collect entries fit 32 bits");
 
 enum Mode : int32_t { kNormal = 0, kNone = 1, kAll = 2 };
 
@@ -456,13 +472,184 @@ __global__ __launch_bounds__(kThreads) void global_emit_kernel(GlobalArgs a, int
             s_cnt);
 }
 
+// Two-level flow, count: resolves the second digit (the bucket of the top 22
+// key bits).  A bucket kept whole fixes T exactly, and the item's counts of
+// keys > T and == T are stored as in the three-level flow.  Otherwise gt[f]
+// is the count of keys above the bucket and eq[f] of keys in it; the bucket's
+// keys add to the third level's bins and are listed while the list has room
+// (the counter keeps counting past it).
+__global__ __launch_bounds__(kThreads) void global_count_collect_kernel(GlobalArgs a) {
+  __shared__ uint32_t s_hist[1024];
+  __shared__ uint32_t s_scan[kWaves];
+  __shared__ uint32_t s_state[4];
+  __shared__ uint32_t s_base;
+  const int tid = threadIdx.x;
+  const int64_t f = blockIdx.x;
+  const int64_t M = a.num_lists * a.chunks;
+  uint32_t* gt_arr = a.ws + kArrays;
+  uint32_t* eq_arr = gt_arr + M;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  Thr t = load_resolved(a, 1);
+  uint32_t h[kBinsPerThread];
+  load_level_bins(a.ws, 1, h);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
+  t = resolve_level(h, 1, t, s_scan, s_state);
+  store_resolved(a, 2, t);
+  uint32_t gt = 0u, eq = 0u;
+  if (t.whole) {
+    uint32_t thr, need_eq;
+    threshold_of(a, t, &thr, &need_eq);
+    count_item(keys, i0, i1, thr, &gt, &eq);
+    gt = block_sum<kThreads>(gt, s_scan);
+    eq = block_sum<kThreads>(eq, s_scan);
+    if (tid == 0) {
+      st_dev(gt_arr + f, gt);
+      st_dev(eq_arr + f, eq);
+    }
+    return;
+  }
+  for (int b = tid; b < 1024; b += kThreads) s_hist[b] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    if (i0 + tid + u * kThreads >= i1) continue;
+    const uint32_t top = keys[u] & t.mask;
+    if (top > t.prefix) {
+      ++gt;
+    } else if (top == t.prefix) {
+      ++eq;
+      atomicAdd(&s_hist[keys[u] & 1023u], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < 1024; b += kThreads) {
+    const uint32_t c = s_hist[b];
+    if (c) add_dev(a.ws + kHist2 + b, c);
+  }
+  uint32_t total_eq;
+  const uint32_t eq_before = block_inclusive_scan<kThreads>(eq, s_scan, &total_eq) - eq;
+  gt = block_sum<kThreads>(gt, s_scan);
+  if (tid == 0) {
+    st_dev(gt_arr + f, gt);
+    st_dev(eq_arr + f, total_eq);
+    s_base = total_eq ? add_dev(a.ws + kCollected, total_eq) : 0u;
+  }
+  __syncthreads();
+  uint32_t slot = s_base + eq_before;
+  uint32_t* lst = a.ws + kArrays + 4 * M + 1;
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    if (i0 + tid + u * kThreads >= i1 || (keys[u] & t.mask) != t.prefix) continue;
+    if (slot < kCollectCap) lst[slot] = ((uint32_t)f << 10) | (keys[u] & 1023u);
+    ++slot;
+  }
+}
+
+// Two-level flow, emit: resolves the last digit from the third level's bins
+// (unless the bucket was kept whole), then the item's offset as in the direct
+// three-level emit, with the per-item counts at T taken from the list (or by
+// recounting the earlier items that hold bucket keys when it overflowed).
+__global__ __launch_bounds__(kThreads) void global_emit_collect_kernel(GlobalArgs a) {
+  __shared__ uint32_t s_scan[kWaves];
+  __shared__ uint32_t s_cnt[4 * kKeysPerThread * kWaves];
+  __shared__ uint32_t s_state[4];
+  const int tid = threadIdx.x;
+  const int64_t f = blockIdx.x;
+  const int64_t M = a.num_lists * a.chunks;
+  int64_t list;
+  int32_t i0, i1;
+  item_range(a, f, &list, &i0, &i1);
+  Thr t = load_resolved(a, 2);
+  uint32_t h[kBinsPerThread];
+  load_level_bins(a.ws, 2, h);
+  uint32_t keys[kKeysPerThread];
+  load_keys(a.scores + list * a.ld, i0, i1, keys);
+  const uint32_t* gt_arr = a.ws + kArrays;
+  const uint32_t* eq_arr = gt_arr + M;
+  const uint32_t collected = a.ws[kCollected];
+  const bool whole = t.whole != 0u;
+  const int64_t ls = list * a.chunks;
+  // over the items before f: gt of [ls, f) (exact if whole, else above the
+  // bucket), and, if whole, eq of all of them and of [ls, f)
+  uint32_t g_in = 0u, e_all = 0u, e_in = 0u;
+  for (int64_t g = tid; g < f; g += kThreads) {
+    const uint32_t e = whole ? eq_arr[g] : 0u;
+    e_all += e;
+    if (g >= ls) {
+      g_in += gt_arr[g];
+      e_in += e;
+    }
+  }
+  t = resolve_level(h, 2, t, s_scan, s_state);  // unchanged when whole
+  uint32_t thr, need_eq;
+  threshold_of(a, t, &thr, &need_eq);
+  if (!whole) {
+    const uint32_t d = thr & 1023u;
+    if (collected <= kCollectCap) {
+      const uint32_t* lst = a.ws + kArrays + 4 * M + 1;
+      for (uint32_t e = tid; e < collected; e += kThreads) {
+        const uint32_t x = lst[e];
+        const int64_t g = x >> 10;
+        const uint32_t low = x & 1023u;
+        if (g >= f) continue;
+        if (low == d) {
+          ++e_all;
+          if (g >= ls) ++e_in;
+        } else if (low > d && g >= ls) {
+          ++g_in;
+        }
+      }
+    } else {
+      for (int64_t g = 0; g < f; ++g) {
+        if (eq_arr[g] == 0u) continue;  // no key of item g is in the bucket
+        int64_t gl;
+        int32_t j0, j1;
+        item_range(a, g, &gl, &j0, &j1);
+        uint32_t k2[kKeysPerThread];
+        load_keys(a.scores + gl * a.ld, j0, j1, k2);
+        uint32_t cg, ce;
+        count_item(k2, j0, j1, thr, &cg, &ce);
+        e_all += ce;
+        if (g >= ls) {
+          e_in += ce;
+          g_in += cg;  // the exact count replaces the keys above the bucket, added once
+          if (tid == 0) g_in -= gt_arr[g];
+        }
+      }
+    }
+  }
+  const uint32_t eq0 = block_sum<kThreads>(e_all, s_scan);
+  g_in = block_sum<kThreads>(g_in, s_scan);
+  e_in = block_sum<kThreads>(e_in, s_scan);
+  // keys == T are kept in flat order, so the run [ls, f) keeps the first
+  // (need_eq - eq before ls) of its e_in, clamped to [0, e_in]
+  const uint32_t eq_ls = eq0 - e_in;
+  const uint32_t room_ls = (need_eq > eq_ls) ? need_eq - eq_ls : 0u;
+  const uint32_t offset = g_in + min(e_in, room_ls);
+  if (f - ls == a.chunks - 1) {  // last item of its list: the list's kept count
+    uint32_t cg, ce;
+    count_item(keys, i0, i1, thr, &cg, &ce);
+    cg = block_sum<kThreads>(cg, s_scan);
+    ce = block_sum<kThreads>(ce, s_scan);
+    if (tid == 0) {
+      const uint32_t room_f = (need_eq > eq0) ? need_eq - eq0 : 0u;
+      a.kept_count[list] = a.prot + (int32_t)(offset + cg + min(ce, room_f));
+    }
+  }
+  emit_item(keys, i0, i1, thr, need_eq, eq0, a.kept_idx + list * a.kept_ld + a.prot + offset,
+            s_cnt);
+}
+
 }  // namespace
 
 size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot) {
   const int64_t m = n - prot;
   const int64_t chunks = (m + kChunk - 1) / kChunk;
   const int64_t M = num_lists * chunks;
-  const int64_t words = kArrays + 4 * M + 1;
+  const int64_t words = kArrays + 4 * M + 1 + kCollectCap;
   return (size_t)((words * 4 + 255) / 256 * 256);
 }
 
@@ -521,6 +708,16 @@ hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kep
   }
   const unsigned items = (unsigned)(num_lists * a.chunks);
   if (items == 0 || a.mode == kNone) return hipSuccess;  // the prompts are the whole result
+  if (a.mode == kNormal && (int64_t)items <= kCollectItems) {  // two histogram levels
+    for (int lvl = (first_level_done ? 1 : 0); lvl < 2; ++lvl) {
+      hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(global_count_collect_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(global_emit_collect_kernel, dim3(items), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const int levels = (a.mode == kNormal) ? 3 : 0;
   for (int lvl = (first_level_done ? 1 : 0); lvl < levels; ++lvl) {
     hipLaunchKernelGGL(global_hist_kernel, dim3(items), dim3(kThreads), 0, stream, a, lvl);
