@@ -381,6 +381,40 @@ def test_score_weighted(G, L, H, Hg, n, prot, width):
     say(f"  bit-identical fraction {same:.6f}")
 
 
+@pytest.mark.parametrize("tied", [4096, 4097])
+def test_select_global_tied_bucket_list_capacity(tied):
+    """`tied` candidates share the threshold value exactly, spread over all lists, and the
+    budget ends inside them.  With few items the count lists the keys of the threshold's
+    22-bit bucket in 4096 entries: 4096 fit and the emit reads the list, 4097 do not and
+    the emit recounts the earlier items.  Both must give the oracle's keep sets."""
+    lists, n, prot = 4, 8192, 0
+    p = 2500 / 8192  # round(p * n) = 2500 per list, B = 10000
+    rng = np.random.default_rng(tied)
+    flat = rng.random(lists * n, dtype=np.float32) * 0.25           # below the tie
+    pos = rng.permutation(lists * n)
+    flat[pos[:8000]] = 0.5 + rng.random(8000, dtype=np.float32) * 0.5  # above it
+    flat[pos[8000:8000 + tied]] = 0.375                             # the tie
+    s = flat.reshape(lists, n)
+    say(f"select_global tied bucket: {tied} keys at the threshold")
+    kept = torch.full((lists, n), -3, dtype=torch.int32, device=DEV)
+    counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    wsb = B.kvevict_select_global_workspace(lists, n, prot, p=p)
+    ws = torch.full((wsb,), 0x3C, dtype=torch.uint8, device=DEV)
+    want_kept, want_counts, want_B = oracle.select_global(s, prot, p)
+    assert want_B == 10000
+    for call in range(2):
+        budget = B.kvevict_select_global(kept, n, counts, torch.from_numpy(s).to(DEV), n, lists, n,
+                                         prot, p, ws, wsb)
+        torch.cuda.synchronize()
+        assert budget == want_B
+        got_counts, got = to_np(counts), to_np(kept)
+        assert np.array_equal(got_counts, want_counts), call
+        for l in range(lists):
+            c = want_counts[l]
+            assert np.array_equal(got[l, :c], want_kept[l, :c]), (call, l)
+            assert np.all(got[l, c:] == -3)
+
+
 @pytest.mark.parametrize("G,L,H,Hg,n,prot,width,p", [
     (48, 16, 4, 48, 3000, 256, 6, 0.25),   # the GateSight shape at a short context
     (12, 4, 6, 70, 900, 37, 6, 0.4),       # H > 4 and Hg > 48: several launches and passes
