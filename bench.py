@@ -323,6 +323,15 @@ def cpu_baseline(torch, cfg, st, seconds):
             "cpu_model": cpu_model()}
 
 
+def device_info(torch) -> dict:
+    """What the runtime reports for the GPU the bench ran on."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None),
+            "compute_units": pr.multi_processor_count,
+            "hbm_bytes": pr.total_memory,
+            "l2_bytes": getattr(pr, "L2_cache_size", None)}
+
+
 def cpu_model() -> str:
     """The host CPU's model name, from /proc/cpuinfo."""
     try:
@@ -539,6 +548,7 @@ def main():
         "dtod_copy": e["dtod_copy"],
         "cpu_baseline": e.get("cpu"),
         "bad_rows": e["bad_rows"],
+        "device": device_info(torch),
     }
     if extra:
         line["workloads"] = extra
