@@ -60,7 +60,7 @@ typedef enum kvevict_status {
   KVEVICT_ERR_INVALID_ARG = 1, /* a size, count or pointer is out of its documented range */
   KVEVICT_ERR_ALIGNMENT = 2,   /* a K/V base or stride is not 16-byte aligned */
   KVEVICT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  KVEVICT_ERR_UNSUPPORTED = 4, /* a valid request this build does not implement */
+  KVEVICT_ERR_UNSUPPORTED = 4, /* a valid request the library does not implement */
   KVEVICT_ERR_HIP = 5          /* the HIP runtime reported an error */
 } kvevict_status;
 
