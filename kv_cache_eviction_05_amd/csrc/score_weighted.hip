@@ -17,9 +17,11 @@
 // holds the attention layer whose window contains g; the host assigns slots
 // so that layers with overlapping windows never share one (at most kSlots at
 // a time, else more launches) and passes, per GDN layer, each slot's weight
-// row and the windows that end there.  When a layer's window ends, the waves'
-// partial sums are added through LDS in a fixed order and the fp32 score is
-// stored.  The LDS tiles are double-buffered, so each step needs one barrier.
+// row and the windows that end there.  When a layer's window ends, each wave
+// leaves its partial sums in LDS; right after the next step's barrier the
+// first four waves add them in wave order and store the fp32 score while the
+// other waves fold (no barriers of its own).  The LDS tiles are double-
+// buffered, so each step needs one barrier.
 //
 // Each thread's offsets within a full tile are computed once; a step adds only
 // the GDN layer and pass offsets.  The log table holds {ln c, 1/c} pairs, so a
@@ -293,6 +295,22 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
     else
       load_tile<VW, false>(a, beta, vnorm, wts, a.g_lo, 0, t0, regs, off);
     __syncthreads();  // the ln table
+    // A window that ends leaves each wave's partial sums in s_red; they are
+    // added (in wave order) and stored right after the next step's barrier, by
+    // the first kHB waves, while the others go on folding.  s_red is written
+    // again only at the next window end; when that comes at the very next
+    // step, a barrier first lets the pending sums be read.
+    int32_t pending = -1;       // launch layer whose sums wait in s_red
+    int32_t pending_step = -2;  // the step whose barrier they are added after
+    auto reduce_store = [&](int32_t q) {
+      if (tid < kHB * kTok) {
+        const int hh = tid / kTok;
+        double v = 0.0;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) v += s_red[w2][hh][lane];
+        store(q, hh, t, v);
+      }
+    };
     for (int32_t step = 0; step < steps; ++step) {
       const int32_t g = a.g_lo + step / passes;
       const int32_t p = step - (g - a.g_lo) * passes;
@@ -312,6 +330,11 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
           load_tile<VW, false>(a, beta, vnorm, wts, g2, p2, t0, regs, off);
       }
       __syncthreads();
+      if (pending >= 0) {
+        reduce_store(pending);
+        pending = -1;
+        pending_step = step;
+      }
 
       const int32_t jb = wave * kJW;  // this wave's heads [jb, je) of the tile
       const int32_t je = min(jb + kJW, jn);
@@ -349,6 +372,13 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
         const int32_t q = __builtin_ctz(ends);
         ends &= ends - 1u;
         const int32_t s_q = a.slot[q];
+        if (pending >= 0) {  // a second window ends at this step: add the first one now
+          __syncthreads();
+          reduce_store(pending);
+          pending = -1;
+          pending_step = step;
+        }
+        if (pending_step == step) __syncthreads();  // s_red was read after this step's barrier
 #pragma unroll
         for (int s = 0; s < kSlots; ++s) {
           if (s == s_q) {
@@ -359,16 +389,12 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
             }
           }
         }
-        __syncthreads();
-        if (tid < kHB * kTok) {
-          const int hh = tid / kTok;
-          double v = 0.0;
-#pragma unroll
-          for (int w2 = 0; w2 < kWaves; ++w2) v += s_red[w2][hh][lane];
-          store(q, hh, t, v);
-        }
-        __syncthreads();
+        pending = q;
       }
+    }
+    if (pending >= 0) {
+      __syncthreads();
+      reduce_store(pending);
     }
   }
   if (a.hist0) {
