@@ -10,12 +10,13 @@
 // Cache, so a second pass over the keys goes back to HBM.  One workgroup of
 // 512 threads per list keeps the list's first rows on chip between the two
 // passes: a row of D bf16 is VPR = D/8 16-byte vectors, thread t owns vector
-// column t % VPR of rows t / VPR + k * (512 / VPR); its first 8 such rows stay
-// in registers and the next 7 or 8 in LDS (64 KB), which at D = 128 holds 512
-// of 1088 rows; the rest are read twice.  Two such workgroups fit a CU, so one
-// list's loads overlap the other's binary64 work: measured against one
+// column t % VPR of rows t / VPR + k * (512 / VPR); its first 10 such rows
+// stay in registers and the next 7 or 8 in LDS (64 KB), which at D = 128 holds
+// 576 of 1088 rows; the rest are read twice.  Two such workgroups fit a CU, so
+// one list's loads overlap the other's binary64 work: measured against one
 // 1024-thread workgroup per CU holding 1024 rows (1.04x traffic, no overlap),
-// 14% faster at ~1.5x traffic.
+// 14% faster at ~1.5x traffic.  Ten register rows (118 VGPRs) beat eight by 2%;
+// a ninth LDS row, or twelve register rows (132 VGPRs, 3 waves per SIMD), do not.
 // Pass 1 accumulates the column sums in binary64 in a fixed order (lanes of a
 // column with shuffles, then the waves in a tree through LDS) into the mean
 // and its squared norm.  Pass 2 forms each row's dot product with the mean and
@@ -31,7 +32,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kReg = 8;     // rows per thread held in registers
+constexpr int kReg = 10;    // rows per thread held in registers
 constexpr int kUnroll = 2;  // rows per thread in flight for the streamed tail
 
 // rows per thread held in LDS: 16 KB each, next to 8*D + D doubles of sums
