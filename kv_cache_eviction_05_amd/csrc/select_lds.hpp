@@ -1,5 +1,5 @@
 // Top-k of a list of 32-bit rank keys held by one workgroup of NT threads
-// (NT a multiple of 64, at least 256)
+// (NT a multiple of 64, at least 128: one or two histogram bins per thread)
 // ("Random Attention" blog summary, Algorithm 1: top-K per KV head; ties go to
 // the lower position).
 //
@@ -38,7 +38,7 @@ __host__ __device__ constexpr int select_passes() {
 
 template <int NT = kSelectThreads>
 struct SelectShared {
-  static_assert(NT % kWave == 0 && NT >= 256, "at least one histogram bin per thread");
+  static_assert(NT % kWave == 0 && NT >= 128, "at most two histogram bins per thread");
   static constexpr int kBins = 1 << select_digit_bits<NT>(0);
   static_assert(kBins % NT == 0 && kBins / NT <= 2, "one or two bins per thread");
   uint32_t hist[kBins];
@@ -161,15 +161,14 @@ __device__ void emit_kept_rounds(KeyAt key_at, int32_t m, uint32_t thr, uint32_t
 // below it, two barriers per group.  The scan reuses the histogram and pick
 // words of `sh`, which the select no longer needs.  Long lists only (NT >=
 // 1024: layers select, 64 lists of 32,512 keys, 33 us against 58 us); the
-// 256-thread workgroups of short lists keep one round at a time, which was
-// 5-6% faster for them.
+// 128- and 256-thread workgroups of short lists keep one round at a time,
+// which was 5-6% faster for them.
 template <int NT, class KeyAt, class Out>
 __device__ void emit_kept(KeyAt key_at, int32_t m, uint32_t thr, uint32_t need_eq,
                           SelectShared<NT>& sh, Out out) {
   if constexpr (NT < 1024) {
     emit_kept_rounds<NT>(key_at, m, thr, need_eq, sh, out);
-    return;
-  }
+  } else {
   constexpr int kW = NT / kWave;
   constexpr int kRounds = 8;                  // rounds of NT keys per group
   constexpr int kS = kRounds * kW;            // (round, wave) slots per kind
@@ -230,6 +229,7 @@ __device__ void emit_kept(KeyAt key_at, int32_t m, uint32_t thr, uint32_t need_e
     }
     carry_gt += sh.pick[0];
     carry_eq += sh.pick[1];
+  }
   }
 }
 
