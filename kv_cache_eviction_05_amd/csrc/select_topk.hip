@@ -17,10 +17,12 @@ namespace kvevict {
 namespace {
 
 constexpr int kThreads = kSelectThreads;
-// The random draw + top-K of lists that fit LDS: 128 threads, so twice as many
-// lists are in flight per CU as with 256 (same-process A/B: batch 154 -> 125 us,
-// paged 93 -> 78 us, the 30-round shape 322 -> 288 us, keep sets identical).
-constexpr int kDrawThreads = 128;
+// The top-K of lists that fit LDS, drawn or stored: 128 threads, so twice as
+// many lists are in flight per CU as with 256 (same-process A/B, keep sets
+// identical: random draw batch 154 -> 125 us, paged 93 -> 78 us, the 30-round
+// shape 322 -> 288 us; stored scores KeyDiff 154 -> 129 us, shared max over
+// heads 25 -> 21 us, paged in place 93 -> 90 us).
+constexpr int kShortThreads = 128;
 constexpr int kBigThreads = 1024;           // workgroup for lists longer than kMaxLdsKeys
 constexpr int32_t kMaxLdsKeys = 15360;      // 60 KiB of keys (+ ~1 KiB static LDS)
 constexpr int32_t kMaxBigLdsKeys = 38848;   // 151.75 KiB of keys + the 8.2 KiB select state: 160 KiB
@@ -107,7 +109,8 @@ hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_
   const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((select_topk_kernel<true, kThreads>), grid, dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((select_topk_kernel<true, kShortThreads>), grid, dim3(kShortThreads), lds,
+                       stream, a);
   } else if (big_lds_ok(m, reinterpret_cast<const void*>(&select_topk_kernel<true, kBigThreads>))) {
     hipLaunchKernelGGL((select_topk_kernel<true, kBigThreads>), grid, dim3(kBigThreads),
                        (size_t)m * sizeof(uint32_t), stream, a);
@@ -225,7 +228,7 @@ hipError_t launch_draw_select(int32_t* kept_idx, int64_t kept_ld, int64_t num_li
   const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((draw_select_kernel<true, kDrawThreads>), grid, dim3(kDrawThreads), lds,
+    hipLaunchKernelGGL((draw_select_kernel<true, kShortThreads>), grid, dim3(kShortThreads), lds,
                        stream, a);
   } else if (big_lds_ok(m, reinterpret_cast<const void*>(&draw_select_kernel<true, kBigThreads>))) {
     hipLaunchKernelGGL((draw_select_kernel<true, kBigThreads>), grid, dim3(kBigThreads),
