@@ -5,7 +5,7 @@
 // The candidates of each list ([prot, n)) are cut into items of kChunk
 // positions, item f = list * chunks + chunk in flat order.
 //   init      prompt indices and kept_count = prot for every list; zeroes the
-//             histograms and the done counter
+//             histograms, the done counter and the collect counter
 //   hist x3   radix histograms of the 11/11/10-bit digits of rank_key(score),
 //             restricted to the keys matching the digits chosen so far.  Each
 //             workgroup of level l derives the digit of level l - 1 itself
@@ -27,7 +27,8 @@
 // list has room; the emit resolves the last digit and takes the per-item
 // counts at T from the list, or, when too many keys share the bucket to list
 // them, recounts the items before its own that hold some.
-// All counts are integer atomics or scans, so the result is deterministic.
+// All counts are integer atomics or scans, so the result is deterministic (the
+// collect list's order varies from run to run; only counts over it are used).
 //
 // Words passed between workgroups of one kernel (the per-item counts and the
 // done counter read by the last count workgroup) are written and read only
