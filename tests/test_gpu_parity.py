@@ -115,6 +115,8 @@ def bucket_scores(lists, n, prot, hi, mid, seed):
     (2, 38948, 30000, 100, "uniform"),   # 38,848 candidates: the most that LDS holds
     (2, 38949, 30000, 100, "ties"),      # one more: keys read from global memory on every pass
     (2, 60000, 1000, 5, "normal"),
+    (3, 15460, 9000, 100, "uniform"),    # 15,360 candidates: the most a 128-thread workgroup holds
+    (3, 15461, 9000, 100, "ties"),       # one more: the 1024-thread workgroup
     (9, 1088, 1024, 128, "whole0"),      # the kept keys fill the top bucket of the first digit
     (9, 1088, 1024, 128, "whole1"),      # ... of the second digit
     (3, 20000, 15000, 100, "whole0"),    # the same with 11-bit digits
@@ -845,6 +847,8 @@ def test_evict_pages_random(R, L, n, K, prot, ps):
     (1, 2, 3, 301, 301, 5, False),       # K == n
     (1, 2, 3, 300, 40, 40, False),       # prot == K
     (3, 1, 2, 777, 300, 0, False),       # no prompt, ragged
+    (1, 1, 3, 15460, 9000, 100, False),  # 15,360 candidates: the most a 128-thread workgroup holds
+    (1, 1, 3, 15461, 9000, 100, True),   # one more: the 1024-thread workgroup
 ])
 def test_select_random(R, L, H, n, K, prot, shared):
     seed, rnd = 17, 9
