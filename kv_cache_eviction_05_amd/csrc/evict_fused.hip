@@ -45,7 +45,7 @@ struct FusedArgs {
 template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void evict_random_inplace_kernel(FusedArgs a) {
   extern __shared__ uint32_t s_dyn[];  // candidate keys [n - prot], then kept indices [K]
-  __shared__ SelectShared<> sh;
+  __shared__ SelectShared<kThreads> sh;
   __shared__ int32_t s_min[kWaves];
   const int32_t H = a.H, n = a.n, K = a.K, prot = a.prot;
   const int64_t g = blockIdx.x / H;

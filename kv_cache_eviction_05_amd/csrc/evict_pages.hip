@@ -38,7 +38,7 @@ struct PagesArgs {
 
 __global__ __launch_bounds__(kThreads) void evict_pages_kernel(PagesArgs a) {
   extern __shared__ int32_t s_dyn[];  // keys [P - pp], old row [P], kept [Kp], kept flag [P]
-  __shared__ SelectShared<> sh;
+  __shared__ SelectShared<kThreads> sh;
   __shared__ uint32_t s_scan[kThreads / kWave];
   __shared__ uint32_t s_base;
   const int32_t P = a.P, pp = a.pp, Kp = a.Kp, ps = a.ps;

@@ -36,7 +36,9 @@ __host__ __device__ constexpr int select_passes() {
   return (kKeyBits == 24 || NT >= 1024) ? 3 : 4;
 }
 
-template <int NT = kSelectThreads>
+// NT must be the workgroup size: the select's loops stride by it and its scans
+// take one word per wave.
+template <int NT>
 struct SelectShared {
   static_assert(NT % kWave == 0 && NT >= 128, "at most two histogram bins per thread");
   static constexpr int kBins = 1 << select_digit_bits<NT>(0);
