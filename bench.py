@@ -446,7 +446,7 @@ def main():
         names = ["batch", "tiny", "paged", "paged_shared", "global", "global_fused", "longgen",
                  "layers",
                  "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
-                 "paged_fused", "longgen_fused", "paged_pages"]
+                 "paged_fused", "longgen_fused", "paged_pages", "paged_single"]
     if "batch" not in names:
         names = ["batch"] + names
     head = None

@@ -153,7 +153,9 @@ LONGGEN_INPLACE = replace(LONGGEN, name="longgen_inplace", inplace=True)
 PAGED_FUSED = replace(PAGED_INPLACE, name="paged_fused", fused=True)
 LONGGEN_FUSED = replace(LONGGEN_INPLACE, name="longgen_fused", fused=True)
 PAGED_PAGES = replace(PAGED_INPLACE, name="paged_pages", page_draw=True)
+# one request of the paged shape: a single stream's whole-model round (36 layers x 8 KV heads)
+PAGED_SINGLE = replace(PAGED, name="paged_single", R=1)
 
 ALL = {c.name: c for c in (TINY, BATCH, PAGED, PAGED_SHARED, GLOBAL, GLOBAL_FUSED, LONGGEN, LAYERS,
                            PAGED_SHARED_MAX, KEYDIFF, PAGED_INPLACE, LONGGEN_INPLACE,
-                           PAGED_FUSED, LONGGEN_FUSED, PAGED_PAGES)}
+                           PAGED_FUSED, LONGGEN_FUSED, PAGED_PAGES, PAGED_SINGLE)}

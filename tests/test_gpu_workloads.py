@@ -138,9 +138,10 @@ def test_batch_round_sampled_and_deterministic():
     free()
 
 
-@pytest.mark.parametrize("cfg", [configs.PAGED, configs.PAGED_SHARED], ids=["per_head", "shared"])
+@pytest.mark.parametrize("cfg", [configs.PAGED, configs.PAGED_SHARED, configs.PAGED_SINGLE],
+                         ids=["per_head", "shared", "single_request"])
 def test_paged_round_sampled(cfg):
-    """Paged round (64 x 36 x 8, 16-token pages): sampled groups against the oracle."""
+    """Paged round (64 or 1 request(s) x 36 x 8, 16-token pages): sampled groups against the oracle."""
     say(f"paged round {cfg.name}: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st, round_id=3)
@@ -560,7 +561,7 @@ def test_longgen_full_size_two_rounds_sampled(base):
     free()
 
 
-@pytest.mark.parametrize("name", ["tiny", "global", "global_fused", "paged_shared"])
+@pytest.mark.parametrize("name", ["tiny", "global", "global_fused", "paged_shared", "paged_single"])
 def test_graph_replay_matches_eager(name):
     """A round captured as a HIP graph gives the eager round's outputs on every replay,
     with eager work (clearing every output) and synchronisations between the replays."""
