@@ -5,10 +5,12 @@
 // prompt plus K_l entries), and the shared list of a layer (Appendix H: one
 // list per layer ranked by the larger of its per-head scores).
 //
-// One workgroup (256 threads, 4 waves) per list.  The n - prot candidate keys
-// (rank_key of the score) are staged in LDS, then the radix select and the
-// chronological emit of select_lds.hpp write the kept indices in increasing
-// order, ties at the threshold to the lowest positions.
+// One workgroup per list: 128 threads (2 waves) when the n - prot candidate
+// keys fit LDS next to the select state, else 1024 threads with the keys in
+// dynamic LDS or, past that, read again on every pass.  The keys (rank_key of
+// the score, or the draw's 24-bit integer) are staged in LDS, then the radix
+// select and the chronological emit of select_lds.hpp write the kept indices
+// in increasing order, ties at the threshold to the lowest positions.
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 #include "select_lds.hpp"
