@@ -48,7 +48,7 @@ problem statement (B = L*H*round(p*(n-prot)), prot <= 256).
 
 from __future__ import annotations
 
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 
 
 @dataclass(frozen=True)
