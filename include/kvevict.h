@@ -287,8 +287,12 @@ kvevict_status kvevict_score_select_global(
  * with idx = kept_idx + (g*idx_lists_per_group + (idx_lists_per_group == 1 ? 0 : h))*kept_ld
  * and count = kept_count ? kept_count[that index list] : K.
  * idx_lists_per_group is H (one index list per KV head) or 1 (shared draw:
- * one list applied to every head of the group).  Out of place: source and
- * destination must not overlap.  Destination rows >= count are untouched.
+ * one list applied to every head of the group).  Out of place: no byte of
+ * k_dst or v_dst may lie in k_src's or v_src's extent, nor k_dst's in v_dst's,
+ * else KVEVICT_ERR_INVALID_ARG (the two sources are only read and may overlap).
+ * A store's extent follows its descriptor: CONTIG ((num_groups*H - 1)*list_stride
+ * + capacity*D)*2 bytes from its base, PAGED the pool, capacity*page_size*H*D*2
+ * bytes.  Destination rows >= count are untouched.
  * src, dst     host descriptors (see kvevict_kv_desc), same D and H.
  * k_src ...    device bf16 stores, 16-byte aligned.
  * errors       optional device uint32 counter; each row whose index or page
@@ -330,7 +334,9 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
  *         Counts outside [0, K] are clamped.
  * Limits: num_groups * H < 2^31, n * head_dim / 8 <= 2^30 and, paged,
  * num_groups * ceil(n / page_size) < 2^32 (free-list offsets), else
- * KVEVICT_ERR_INVALID_ARG.  Calls on the same store must not overlap.
+ * KVEVICT_ERR_INVALID_ARG.  The K and V extents (as in kvevict_compact) must
+ * be disjoint, else KVEVICT_ERR_INVALID_ARG.  Calls on the same store must not
+ * overlap in time.
  */
 kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
                                        const int32_t* kept_idx, int64_t kept_ld,
@@ -357,7 +363,8 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
  *             keeps K, so pages ceil(K / page_size) .. ceil(n / page_size) - 1 are freed).
  * Requires 0 <= prot <= K <= n <= rows of a list, num_requests < 2^32, L >= 1;
  * KVEVICT_ERR_UNSUPPORTED when (n - prot) + K > 15360 (keys and indices are held on chip).
- * Limits of kvevict_compact_inplace apply.  Calls on the same store must not overlap.
+ * Limits of kvevict_compact_inplace apply, disjoint K and V extents included.
+ * Calls on the same store must not overlap in time.
  */
 kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* k, void* v,
                                            int64_t num_requests, int32_t L, int32_t n, int32_t K,

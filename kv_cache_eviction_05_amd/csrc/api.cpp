@@ -71,6 +71,28 @@ kvevict_status check_store(const kvevict_kv_desc* d, const void* k, const void* 
   return KVEVICT_OK;
 }
 
+// Byte extent of a store as its descriptor lays it out for `lists` lists:
+// contiguous ((lists - 1)*list_stride + capacity*D) elements, paged
+// capacity*page_size*H*D elements (the whole pool), 2 bytes each.  Taken in
+// 128-bit arithmetic on a validated descriptor, so it cannot wrap.
+typedef unsigned __int128 u128;
+u128 store_extent_bytes(const kvevict_kv_desc* d, int64_t lists) {
+  if (lists <= 0) return 0;
+  u128 elems;
+  if (d->layout == KVEVICT_LAYOUT_CONTIG)
+    elems = (u128)(lists - 1) * (u128)d->list_stride + (u128)d->capacity * (u128)d->head_dim;
+  else
+    elems = (u128)d->capacity * (u128)d->page_size * (u128)d->heads * (u128)d->head_dim;
+  return elems * 2u;
+}
+
+// True if the byte ranges [a, a + alen) and [b, b + blen) share a byte.
+bool ranges_overlap(const void* a, u128 alen, const void* b, u128 blen) {
+  if (alen == 0 || blen == 0) return false;
+  const u128 x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + blen && y < x + alen;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,10 +385,14 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
   const int32_t D = src->head_dim;
   if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;  // one token row of all heads
   if (num_groups > 0 && K > 0) {
-    // out of place: K/V destinations must not overlap the sources
-    const uintptr_t ks = (uintptr_t)k_src, vs = (uintptr_t)v_src;
-    const uintptr_t kd = (uintptr_t)k_dst, vd = (uintptr_t)v_dst;
-    if (ks == kd || vs == vd || ks == vd || vs == kd) return KVEVICT_ERR_INVALID_ARG;
+    // out of place: no destination byte may lie in a source store or in the
+    // other destination store (the sources are only read and may overlap)
+    const int64_t lists = num_groups * H;
+    const u128 se = store_extent_bytes(src, lists), de = store_extent_bytes(dst, lists);
+    if (ranges_overlap(k_dst, de, k_src, se) || ranges_overlap(k_dst, de, v_src, se) ||
+        ranges_overlap(v_dst, de, k_src, se) || ranges_overlap(v_dst, de, v_src, se) ||
+        ranges_overlap(k_dst, de, v_dst, de))
+      return KVEVICT_ERR_INVALID_ARG;
   }
   return hip_status(kvevict::launch_compact(sv, k_src, v_src, dv, k_dst, v_dst, D, H, kept_idx,
                                             kept_ld, kept_count, K, num_groups,
@@ -388,10 +414,12 @@ kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, vo
   if (st != KVEVICT_OK) return st;
   if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
-  if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;  // K and V are distinct stores
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
   if (!prod_le(num_groups, H, kInt32Max) || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > 0 && ranges_overlap(k, store_extent_bytes(store, num_groups * H), v,
+                                       store_extent_bytes(store, num_groups * H)))
+    return KVEVICT_ERR_INVALID_ARG;  // K and V are disjoint stores
   if (sv.paged && !prod_le(num_groups, (n + store->page_size - 1) / store->page_size, kUint32Max))
     return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit
   return hip_status(kvevict::launch_compact_inplace(sv, k, v, D, H, kept_idx, kept_ld, kept_count,
@@ -418,9 +446,11 @@ kvevict_status kvevict_evict_random_inplace(const kvevict_kv_desc* store, void* 
   if (st != KVEVICT_OK) return st;
   if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
-  if (k == v && num_groups > 0) return KVEVICT_ERR_INVALID_ARG;
   if (sv.paged && num_groups > 0 && (!freed_pages || !freed_count)) return KVEVICT_ERR_INVALID_ARG;
   if (!prod_le(num_groups, H, kInt32Max) || (int64_t)n * (D / 8) > (1LL << 30)) return KVEVICT_ERR_INVALID_ARG;
+  if (num_groups > 0 && ranges_overlap(k, store_extent_bytes(store, num_groups * H), v,
+                                       store_extent_bytes(store, num_groups * H)))
+    return KVEVICT_ERR_INVALID_ARG;  // K and V are disjoint stores
   if ((int64_t)(n - prot) + K > kvevict::kMaxFusedEntries) return KVEVICT_ERR_UNSUPPORTED;
   if (sv.paged && !prod_le(num_groups, (n + store->page_size - 1) / store->page_size, kUint32Max))
     return KVEVICT_ERR_INVALID_ARG;  // free-list offsets are 32-bit

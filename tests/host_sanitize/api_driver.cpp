@@ -36,8 +36,8 @@ void expect(kvevict_status got, kvevict_status want, int launches_before, bool l
 
 // Non-null, 16-byte aligned addresses that the host code never dereferences.
 template <typename T>
-T* fake(uintptr_t k) {
-  return reinterpret_cast<T*>(k << 20);
+T* fake(uintptr_t k) {  // stand-in device addresses 1 TiB apart: the stores never overlap
+  return reinterpret_cast<T*>(k << 40);
 }
 
 kvevict_kv_desc contig(int32_t D, int32_t H, int64_t cap) {
@@ -180,6 +180,26 @@ int main() {
                         nullptr), INV, false);  // K > dst rows
   CHECK(kvevict_compact(&src, ks, vs, &dst, vs, vd, idx, 1024, nullptr, 1024, 16, 8, nullptr,
                         nullptr), INV, false);  // K dst aliases V src
+  {  // partial overlaps, by the descriptors' extents (16 groups x 8 heads)
+    const int64_t src_bytes = 128LL * 1088 * 128 * 2, dst_bytes = 128LL * 1024 * 128 * 2;
+    uint8_t* k8 = fake<uint8_t>(6);
+    uint8_t* v8 = fake<uint8_t>(7);
+    uint8_t* d8 = fake<uint8_t>(8);
+    CHECK(kvevict_compact(&src, ks, vs, &dst, k8 + 4096, vd, idx, 1024, nullptr, 1024, 16, 8,
+                          nullptr, nullptr), INV, false);  // K dst starts inside K src
+    CHECK(kvevict_compact(&src, ks, vs, &dst, k8 - dst_bytes + 16, vd, idx, 1024, nullptr, 1024,
+                          16, 8, nullptr, nullptr), INV, false);  // K dst runs into K src
+    CHECK(kvevict_compact(&src, ks, vs, &dst, k8 + src_bytes, vd, idx, 1024, nullptr, 1024, 16, 8,
+                          nullptr, nullptr), OK, true);  // touching, not overlapping
+    CHECK(kvevict_compact(&src, ks, vs, &dst, kd, v8 + src_bytes - 16, idx, 1024, nullptr, 1024,
+                          16, 8, nullptr, nullptr), INV, false);  // V dst in V src's last row
+    CHECK(kvevict_compact(&src, ks, vs, &dst, kd, kd, idx, 1024, nullptr, 1024, 16, 8, nullptr,
+                          nullptr), INV, false);  // K dst and V dst alias
+    CHECK(kvevict_compact(&src, ks, vs, &dst, kd, d8 + dst_bytes - 16, idx, 1024, nullptr, 1024,
+                          16, 8, nullptr, nullptr), INV, false);  // V dst in K dst's last row
+    CHECK(kvevict_compact(&src, ks, k8 + 4096, &dst, kd, vd, idx, 1024, nullptr, 1024, 16, 8,
+                          nullptr, nullptr), OK, true);  // overlapping sources are only read
+  }
   CHECK(kvevict_compact(&src, fake<uint8_t>(6) + 8, vs, &dst, kd, vd, idx, 1024, nullptr, 1024, 16,
                         8, nullptr, nullptr), ALIGN, false);
   CHECK(kvevict_compact(&src, ks, vs, &dst, kd, vd, idx, 1024, nullptr, 1024, huge, 8, nullptr,
@@ -213,6 +233,12 @@ int main() {
                                 nullptr, nullptr, nullptr), OK, true);
   CHECK(kvevict_compact_inplace(&store, ks, ks, idx, 3072, nullptr, 3072, 3136, 16, 8, nullptr,
                                 nullptr, nullptr, nullptr), INV, false);  // K and V the same
+  CHECK(kvevict_compact_inplace(&store, ks, fake<uint8_t>(6) + 128LL * 3136 * 128 * 2 - 16, idx,
+                                3072, nullptr, 3072, 3136, 16, 8, nullptr, nullptr, nullptr,
+                                nullptr), INV, false);  // V starts in K's last row
+  CHECK(kvevict_compact_inplace(&store, ks, fake<uint8_t>(6) + 128LL * 3136 * 128 * 2, idx, 3072,
+                                nullptr, 3072, 3136, 16, 8, nullptr, nullptr, nullptr, nullptr),
+        OK, true);  // V begins where K ends
   CHECK(kvevict_compact_inplace(&store, ks, vs, idx, 3072, nullptr, 3072, 3136, huge, 8, nullptr,
                                 nullptr, nullptr, nullptr), INV, false);
   kvevict_kv_desc pstore = paged(128, 8, 16, 304128, pt, 132);

@@ -47,7 +47,8 @@ def test_abi_version_and_strings():
     assert B.status_string(99) == "unknown status"
 
 
-FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
+FAKE = 1 << 40  # a non-null, 16-byte aligned address that is never dereferenced; multiples
+#                are 1 TiB apart, so the stores the tests describe at them never overlap
 
 
 def status(fn, *args):
@@ -175,6 +176,44 @@ def test_compact_validation():
     assert call(weird, dst) == B.KVEVICT_ERR_INVALID_ARG
 
 
+def test_compact_rejects_overlapping_stores():
+    """Out of place: no destination byte may lie in a source store or in the other destination.
+
+    Extents follow the descriptors: contiguous ((lists - 1)*list_stride + capacity*D)*2 bytes,
+    paged capacity*page_size*H*D*2 bytes.  Only rejections are checked here (a call that passes
+    would launch); the host sanitizer driver, whose launchers are stand-ins, checks that stores
+    which merely touch, and sources that overlap each other, are accepted.
+    """
+    D, H, groups = 128, 8, 4
+    src = B.contig_desc(D, H, 1088)
+    dst = B.contig_desc(D, H, 1024)
+    src_bytes = (groups * H - 1) * 1088 * D * 2 + 1088 * D * 2
+    dst_bytes = groups * H * 1024 * D * 2
+    INV = B.KVEVICT_ERR_INVALID_ARG
+
+    def call(s=src, d=dst, ks=FAKE, vs=FAKE * 2, kd=FAKE * 3, vd=FAKE * 4):
+        return status("kvevict_compact", ctypes.byref(s), ks, vs, ctypes.byref(d), kd, vd, FAKE,
+                      1024, None, 1024, groups, H, None, None)
+
+    assert call(kd=FAKE + 4096) == INV                       # K dst starts inside K src
+    assert call(kd=FAKE * 2 + src_bytes - 16) == INV         # K dst's first row in V src's last
+    assert call(kd=FAKE - dst_bytes + 16) == INV             # K dst runs into K src's first row
+    assert call(vd=FAKE * 2 + (1 << 20)) == INV              # V dst inside V src
+    assert call(vd=FAKE + 512) == INV                        # V dst inside K src
+    assert call(vd=FAKE * 3) == INV                          # K dst and V dst alias
+    assert call(vd=FAKE * 3 + dst_bytes - 16) == INV         # V dst starts in K dst's last row
+    # a padded list stride widens the contiguous extent
+    padded = B.contig_desc(D, H, 1088, list_stride=4096 * D)
+    padded_bytes = ((groups * H - 1) * 4096 + 1088) * D * 2
+    assert call(s=padded, kd=FAKE + src_bytes) == INV          # past the dense extent, not the padded
+    assert call(s=padded, kd=FAKE + padded_bytes - 16) == INV
+    # paged: the whole pool, capacity pages of page_size * H * D elements
+    pool = B.KvDesc(B.LAYOUT_PAGED, D, H, 16, 1000, 0, FAKE * 9, 68)
+    pool_bytes = 1000 * 16 * H * D * 2
+    assert call(s=pool, kd=FAKE + pool_bytes - 16) == INV
+    assert call(d=pool, vd=FAKE * 3 + pool_bytes - 16) == INV  # the two destination pools
+
+
 def test_layer_power_budget_matches_the_oracle():
     """The library's exact largest-remainder budgets equal the oracle's rational ones (host only)."""
     import numpy as np
@@ -258,6 +297,9 @@ def test_compact_inplace_validation():
     assert call(kept_ld=1000) == B.KVEVICT_ERR_INVALID_ARG      # kept_ld < K
     assert call(ipg=3) == B.KVEVICT_ERR_INVALID_ARG
     assert call(v=FAKE) == B.KVEVICT_ERR_INVALID_ARG            # K and V alias
+    assert call(v=FAKE + 4 * H * 1088 * D * 2 - 16) == B.KVEVICT_ERR_INVALID_ARG  # V starts in K
+    assert call(k=FAKE * 2 - 16) == B.KVEVICT_ERR_INVALID_ARG   # K ends inside V
+    assert call(d=pg, v=FAKE + 1000 * 16 * H * D * 2 - 16) == B.KVEVICT_ERR_INVALID_ARG
     assert call(n=1089) == B.KVEVICT_ERR_INVALID_ARG            # n beyond the store
     assert call(k=FAKE + 8) == B.KVEVICT_ERR_ALIGNMENT
     assert call(d=pg, freed=None) == B.KVEVICT_ERR_INVALID_ARG  # paged needs the free list
@@ -286,6 +328,7 @@ def test_evict_random_inplace_validation():
     assert call(R=1 << 32) == B.KVEVICT_ERR_INVALID_ARG
     assert call(kept_ld=1000) == B.KVEVICT_ERR_INVALID_ARG      # kept_ld < K with an output
     assert call(v=FAKE) == B.KVEVICT_ERR_INVALID_ARG            # K and V alias
+    assert call(v=FAKE + 4 * 36 * H * 4096 * D * 2 - 16) == B.KVEVICT_ERR_INVALID_ARG  # V in K
     assert call(n=4097) == B.KVEVICT_ERR_INVALID_ARG            # n beyond the store
     assert call(k=FAKE + 8) == B.KVEVICT_ERR_ALIGNMENT
     assert call(d=pg, freed=None) == B.KVEVICT_ERR_INVALID_ARG
