@@ -363,7 +363,8 @@ def cpu_single_thread(torch, cfg, st, min_seconds=2.0):
         w = st.weights.cpu().numpy()
 
         def one_round():
-            s = oracle.score_weighted(beta, vnorm, w, st.win_begin, st.win_count, cfg.prot)
+            s = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(cfg.L, cfg.G, cfg.win_width),
+                                      cfg.prot)
             kept, counts, _ = oracle.select_global(s, cfg.prot, cfg.p)
             oracle.compact({"list_stride": cfg.n * cfg.D}, ks, vs, {"list_stride": cfg.n * cfg.D},
                            kd, vd, kept, cfg.n, cfg.D, cfg.H, 0, cfg.groups, ipg=cfg.H,

@@ -111,6 +111,32 @@ def score_random(L, H, n, prot, seed, round_id, shared_draw, list_begin, list_en
 # GateSight-style weighted score (Sec. 4.1 window; log effective write)
 # ---------------------------------------------------------------------------
 
+def gdn_windows(L: int, G: int, width: int = 6):
+    """GDN layers read by each attention layer: (begins, counts), in GDN numbering.
+
+    GateSight, model paragraph: a hybrid stack in which every fourth layer is full
+    attention and the other three are Gated DeltaNet; Sec. 4.1: an attention
+    layer's estimator reads the signals of the up-to-six GDN layers before it
+    (three for the first attention layer).  Written as a walk over the stack:
+    each attention layer is preceded by G // L GDN layers of its own block, the
+    GDN layers are numbered in stack order, and attention layer a reads the
+    last ``width`` GDN layers met before it.  GDN layers past the last attention
+    layer are read by none.
+    """
+    per_block = G // L
+    seen = []                     # GDN numbers met so far, in stack order
+    begins, counts = [], []
+    gdn_number = 0
+    for _block in range(L):
+        for _ in range(per_block):
+            seen.append(gdn_number)
+            gdn_number += 1
+        window = seen[-width:] if width > 0 else []
+        begins.append(window[0] if window else len(seen))
+        counts.append(len(window))
+    return begins, counts
+
+
 def score_weighted(beta: np.ndarray, vnorm: np.ndarray, w: np.ndarray, win_begin, win_count,
                    prot: int, t_begin: int = 0, t_end: int | None = None) -> np.ndarray:
     """Weighted scores float32 [L*H][n] from planar signals [G][n][Hg] and weights [L][H][S][Hg]."""

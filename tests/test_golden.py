@@ -33,7 +33,8 @@ def test_page_facts():
     assert g.prot <= f["max_protected_prefix"]["value"]
 
     e = f["estimator_inputs"]
-    begins, counts = configs.gdn_windows(g.L, g.G, g.win_width)
+    begins, counts = oracle.gdn_windows(g.L, g.G, g.win_width)
+    assert (begins, counts) == configs.gdn_windows(g.L, g.G, g.win_width)
     assert max(counts) == e["window_layers"] and counts[0] == e["first_window_layers"]
     per_head = e["gdn_heads"] * e["signals_per_head"]
     assert counts[1] * per_head + e["age_features"] == e["value"]

@@ -342,6 +342,8 @@ def test_select_global(lists, n, prot, p, kind):
 # ---------------------------------------------------------------------------
 
 def weighted_case(G, L, H, Hg, n, prot, width, seed):
+    """Seeded signals and weights, and the library's window table for the GPU calls (the
+    oracle takes its own reading, oracle.gdn_windows)."""
     rng = np.random.default_rng(seed)
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((G, n, Hg))))).astype(np.float32)
     vnorm = np.exp(rng.standard_normal((G, n, Hg))).astype(np.float32)
@@ -378,7 +380,7 @@ def test_score_weighted(G, L, H, Hg, n, prot, width):
     torch.cuda.synchronize()
     got = to_np(s)
     assert np.all(np.isnan(got[:, n:]))
-    want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot)
+    want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(L, G, width), prot)
     same = assert_weighted_close(got[:, :n], want, prot)
     say(f"  bit-identical fraction {same:.6f}")
 
@@ -479,7 +481,7 @@ def test_score_weighted_interleaved_signals():
     B.kvevict_score_weighted(s, n, flat[0:], flat[2:], n * Hg * 3, Hg * 3, 3,
                              torch.from_numpy(w).to(DEV), width, begins, counts, L, H, G, Hg, n, prot)
     torch.cuda.synchronize()
-    want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot)
+    want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(L, G, width), prot)
     same = assert_weighted_close(to_np(s), want, prot)
     say(f"  bit-identical fraction {same:.6f}")
 
@@ -501,7 +503,7 @@ def test_score_weighted_special_signals():
                              H, G, Hg, n, prot)
     torch.cuda.synchronize()
     got = to_np(s).astype(np.float64)
-    want = oracle.score_weighted(beta, vnorm, w, begins, counts, prot).astype(np.float64)
+    want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(L, G, width), prot).astype(np.float64)
     assert np.array_equal(np.isnan(got), np.isnan(want))
     assert np.array_equal(np.isposinf(got), np.isposinf(want))
     assert np.array_equal(np.isneginf(got), np.isneginf(want))

@@ -221,8 +221,8 @@ def test_random_score_weighted(case):
     torch.cuda.synchronize()
     got = to_np(s)
     assert np.all(np.isnan(got[:, n:]))
-    assert_weighted_close(got[:, :n], oracle.score_weighted(beta, vnorm, w, begins, counts, prot),
-                          prot)
+    want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(L, G, width), prot)
+    assert_weighted_close(got[:, :n], want, prot)
 
 
 @pytest.mark.parametrize("case", range(8))

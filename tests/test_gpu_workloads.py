@@ -199,7 +199,7 @@ def test_global_round():
     beta, vnorm, w = st.beta.cpu().numpy(), st.vnorm.cpu().numpy(), st.weights.cpu().numpy()
     got = st.scores.cpu().numpy()
     for t0 in (0, 240, 7777, cfg.n - 300):
-        want = oracle.score_weighted(beta, vnorm, w, st.win_begin, st.win_count, cfg.prot,
+        want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(cfg.L, cfg.G, cfg.win_width), cfg.prot,
                                      t_begin=t0, t_end=t0 + 300)
         g, o = got[:, t0:t0 + 300], want[:, t0:t0 + 300]
         fin = np.isfinite(o)

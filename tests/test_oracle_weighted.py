@@ -18,7 +18,9 @@ import numpy as np
 import pytest
 
 import oracle
-from kv_cache_eviction_05_amd.configs import gdn_windows
+from kv_cache_eviction_05_amd import configs
+
+gdn_windows = oracle.gdn_windows
 
 
 def make_signals(G, n, Hg, seed):
@@ -26,6 +28,15 @@ def make_signals(G, n, Hg, seed):
     beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((G, n, Hg))))).astype(np.float32)
     vnorm = np.exp(rng.standard_normal((G, n, Hg))).astype(np.float32)
     return beta, vnorm
+
+
+def test_product_windows_equal_the_oracle_reading():
+    """The library's window table (configs.gdn_windows, used by the workloads) equals the
+    oracle's walk over the hybrid stack for every small shape and width."""
+    for L in range(1, 20):
+        for G in range(0, 80):
+            for width in range(0, 9):
+                assert configs.gdn_windows(L, G, width) == oracle.gdn_windows(L, G, width)
 
 
 def test_window_counts_match_page_numbers():
