@@ -132,18 +132,24 @@ kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* be
                                       int32_t Hg, int32_t n, int32_t prot, hipStream_t stream);
 
 /*
- * KeyDiff scores (GateSight Sec. 5.1 baselines paragraph: the cosine
- * similarity of each cached key to the unnormalised mean key of its head; the
- * least similar keys are kept, under flat per-head budgets with
- * kvevict_select_topk).
+ * KeyDiff scores (GateSight Sec. 5.1, baselines paragraph).  A key scores
+ * minus its cosine to its head's mean key (keys not normalised first), so a
+ * flat per-head budget in kvevict_select_topk keeps the keys that differ most
+ * from the mean.
  *
  * For every list (group g, head h), list = g*H + h, with its n keys in the
  * store `keys` (contiguous or paged, see kvevict_kv_desc; values are not read):
  *     scores[list*ld + i] = -cos(k_i, mean of k_0 .. k_{n-1})   for i >= prot,
  *                           +inf                                for i <  prot,
- * in binary64 with one rounding to fp32.  A key or a mean of norm zero gives
- * cos = 0; a zero score is written as +0.  A paged row whose page id falls
- * outside the pool reads as zeros.
+ * computed as -dot / (sqrt(|k_i|^2) * sqrt(|mean|^2)) in binary64 (IEEE square
+ * roots and division) and rounded once to fp32.  Precision: the sums run in
+ * another order than a plain loop's, so before that rounding the cosine may
+ * differ from a plain loop's binary64 value x by at most about
+ * 2^-53 * (D + n * |sum_i |k_i|| / |sum_i k_i|) (a few 1e-13 for N(0,1) keys
+ * at n = 1088, D = 128); the score is fp32(-x), or its neighbour one fp32 ulp
+ * away when -x lies within that bound of a midpoint between two fp32 values.
+ * A key or a mean of norm zero gives cos = 0; a zero score is written as +0.
+ * A paged row whose page id falls outside the pool reads as zeros.
  * Requires D = head_dim in {8, 16, 32, ..., 512}, 0 <= prot <= n <= rows of a
  * list, n * D / 8 < 2^31, ld >= n, num_groups*H < 2^31.  KVEVICT_ERR_UNSUPPORTED
  * for other D.

@@ -1,6 +1,7 @@
-// KeyDiff key scores (GateSight Sec. 5.1 baselines paragraph: the cosine
-// similarity of each key, as stored in the cache, to the unnormalised mean key
-// of its head; the least similar keys are kept under flat per-head budgets).
+// KeyDiff key scores (GateSight Sec. 5.1, baselines paragraph): each cached
+// key is scored by minus its cosine to the mean of its head's keys, taken
+// without normalising the keys first, so that a per-head top-K keeps the keys
+// that point away from the mean.
 //
 //   score[list][i] = -cos(k_i, mean_j k_j)   (mean over all n keys of the list),
 //   +inf for i < prot; a zero norm gives cos = 0; zero is written as +0.
@@ -21,7 +22,13 @@
 // column with shuffles, then the waves in a tree through LDS) into the mean
 // and its squared norm.  Pass 2 forms each row's dot product with the mean and
 // its squared norm in binary64, adds the VPR partials of a row with DPP lane
-// moves, and rounds -dot * rsqrt(|k|^2) / |mean| once to fp32.
+// moves, and rounds -dot / (sqrt(|k|^2) * sqrt(|mean|^2)) once to fp32, with
+// IEEE binary64 square roots and division.  The sums run in another order than
+// a plain loop's, so the binary64 cosine may differ from it by a few units of
+// 2^-53 times (D + n * |sum of |k_i|| / |sum of k_i|); the fp32 score then
+// equals the plain loop's rounding except where that cosine lies within this
+// bound of a midpoint between two fp32 values, where it may be the other
+// neighbour (one fp32 ulp away).
 #include <cmath>
 
 #include "kvevict_device.hpp"
@@ -120,13 +127,6 @@ __device__ __forceinline__ double group_sum(double v) {
   if (W >= 32) v += __shfl_xor(v, 16, kWave);
   if (W >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
-}
-
-// 1 / sqrt(x) for x > 0: the hardware estimate and one Newton step (relative
-// error far below the fp32 rounding of the score).
-__device__ __forceinline__ double rsqrt_nr(double x) {
-  const double y = __builtin_amdgcn_rsq(x);
-  return y * fma(-0.5 * x * y, y, 1.5);
 }
 
 // Partial dot with the mean and squared norm of one 16-byte vector.
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
   }
   __syncthreads();
   const double mm = s_mm;
-  const double inv_mnorm = mm > 0.0 ? 1.0 / sqrt(mm) : 0.0;
+  const double mnorm = sqrt(mm);  // correctly rounded, as every sqrt and divide below
   // Hide the held rows' values from the compiler between the passes, so it
   // converts them again rather than keeping 64 binary64 values of pass 1 live
   // (which would spill).
@@ -264,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
     if (col == 0 && t < n) {
       float sc = INFINITY;
       if (t >= a.prot) {
-        sc = (kk > 0.0 && mm > 0.0) ? (float)(-(dot * rsqrt_nr(kk)) * inv_mnorm) : 0.0f;
+        const double den = sqrt(kk) * mnorm;
+        sc = (den > 0.0) ? (float)(-(dot / den)) : 0.0f;
         if (sc == 0.0f) sc = 0.0f;  // -0 written as +0
       }
       out[t] = sc;

@@ -288,9 +288,9 @@ def shared_kept_count(K: int, prot: int) -> int:
 
 
 # ---------------------------------------------------------------------------
-# KeyDiff key scores (GateSight Sec. 5.1 baselines paragraph: cosine similarity
-# of each cached key to the unnormalised mean key of its head; the least
-# similar keys are kept under flat per-head budgets)
+# KeyDiff key scores (GateSight Sec. 5.1, baselines paragraph): minus each
+# key's cosine to its head's mean key, keys taken as stored; a per-head top-K
+# then keeps the keys farthest from the mean
 # ---------------------------------------------------------------------------
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -298,17 +298,18 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def score_keydiff(keys: np.ndarray, prot: int) -> np.ndarray:
+def score_keydiff(keys: np.ndarray, prot: int, binary64: bool = False) -> np.ndarray:
     """Scores float32 [lists][n] from keys (uint16 bf16 bits) [lists][n][D].
 
     score_i = -cos(k_i, mean_j k_j), the mean over all n keys of the list, in binary64,
     rounded once to float32; higher is kept first, so the least similar keys survive.
     Readings: the mean runs over every entry of the list, prompt included; a key or a mean
     of norm zero gives cos = 0; a zero score is written as +0; slots < prot score +inf.
+    With ``binary64`` the scores are returned as float64, before that rounding.
     """
     k = bf16_to_f64(keys)
     lists, n, D = k.shape
-    out = np.empty((lists, n), dtype=np.float32)
+    out = np.empty((lists, n), dtype=np.float64 if binary64 else np.float32)
     for l in range(lists):
         mean = k[l].sum(axis=0) / n if n else np.zeros(D)
         mm = float(np.dot(mean, mean))
@@ -319,8 +320,8 @@ def score_keydiff(keys: np.ndarray, prot: int) -> np.ndarray:
             kk = float(np.dot(k[l, i], k[l, i]))
             den = math.sqrt(kk) * math.sqrt(mm)
             cos = float(np.dot(k[l, i], mean)) / den if den > 0 else 0.0
-            v = np.float32(-cos)
-            out[l, i] = v if v != 0 else np.float32(0.0)  # -0 written as +0
+            v = -cos if binary64 else np.float32(-cos)
+            out[l, i] = v if v != 0 else 0.0  # -0 written as +0
     return out
 
 

@@ -19,6 +19,7 @@ import torch
 import oracle
 from kv_cache_eviction_05_amd import binding as B
 from kv_cache_eviction_05_amd import configs, rounds, synth
+from test_gpu_parity import assert_keydiff_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -385,8 +386,9 @@ def test_layers_round():
 
 
 def test_keydiff_round_sampled():
-    """The batch round scored by KeyDiff: sampled lists against the oracle's scores (two fp32
-    ulps), selection given the GPU's scores, and the whole gather."""
+    """The batch round scored by KeyDiff: sampled lists against the oracle's scores (the stated
+    precision: the oracle's fp32 rounding, or its neighbour next to a midpoint), selection given
+    the GPU's scores, and the whole gather."""
     cfg = configs.KEYDIFF
     say("keydiff round: allocating")
     st = rounds.make_state(cfg, DEV)
@@ -397,9 +399,7 @@ def test_keydiff_round_sampled():
     check_contig_gather(st, cfg.K)
     got_s = st.scores.cpu().numpy()
     for l in sample_lists(cfg.lists, 12, seed=8):
-        want = oracle.score_keydiff(u16(st.k_src[l:l + 1]), cfg.prot)
-        fin = np.isfinite(want)
-        assert np.all(np.abs(got_s[l:l + 1][fin] - want[fin]) <= 2 * np.spacing(np.abs(want[fin]))), l
+        assert_keydiff_close(got_s[l:l + 1], u16(st.k_src[l:l + 1]), cfg.prot)
         assert np.array_equal(st.kept[l].cpu().numpy(),
                               oracle.select_topk(got_s[l:l + 1], cfg.K, cfg.prot)[0]), l
     del st
