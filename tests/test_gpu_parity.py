@@ -89,19 +89,24 @@ def make_scores(kind, lists, n, seed):
     raise ValueError(kind)
 
 
-def bucket_scores(lists, n, prot, hi, mid, seed):
-    """Candidates [prot, n) of every list: `hi` of them at 2 + 2^-7 and `mid` at 2.0, which
-    share the top radix digit and differ in the next one, the rest at -1; the prompt at 0.5.
-    Keeping exactly `hi` per list (or in all) takes a whole bucket: at the first digit when
-    mid = 0, at the second otherwise, so the selects stop early."""
+def bucket_scores(lists, n, prot, hi, mid, seed, hi_value=2.0078125):
+    """Candidates [prot, n) of every list: `hi` of them at hi_value and `mid` at 2.0, the rest
+    at -1; the prompt at 0.5.  2 + 2^-7 shares the top radix digit (key bits 21-31) with 2.0
+    and differs in the second (bits 10-20); 2 + 2^-22, the next float after 2.0, shares the
+    top 22 bits and differs in the last digit (bits 0-9).  Keeping exactly `hi` per list (or
+    in all) takes a whole bucket: at the first digit when mid = 0, else at the digit where
+    the two values part, so the selects stop early."""
     rng = np.random.default_rng(seed)
     s = np.full((lists, n), -1.0, np.float32)
     s[:, :prot] = 0.5
     for l in range(lists):
         pos = prot + rng.permutation(n - prot)
-        s[l, pos[:hi]] = 2.0078125
+        s[l, pos[:hi]] = hi_value
         s[l, pos[hi:hi + mid]] = 2.0
     return s
+
+
+NEXT_AFTER_TWO = float(np.nextafter(np.float32(2.0), np.float32(3.0)))  # 2 + 2^-22
 
 
 @pytest.mark.parametrize("lists,n,K,prot,kind", [
@@ -305,12 +310,24 @@ def test_compact_rejects_out_of_range_rows():
     (6, 20100, 100, 0.3, "whole0"),      # B fills the top bucket of the first digit
     (6, 20100, 100, 0.3, "whole1"),      # ... of the second digit
     (8200, 100, 10, 0.3, "whole1"),      # the same, scanned once
+    # 257-8192 items of 8192 candidates: three histogram levels, and every emit workgroup sums
+    # the per-item counts before its own item itself (the direct-prefix flow)
+    (64, 65536, 256, 0.25, "uniform"),   # the GateSight model shape at a 64K context: 512 items
+    (128, 32768, 256, 0.25, "normal"),   # 512 items
+    (257, 8192, 0, 0.3, "uniform"),      # 257 items: one past the two-level flow
+    (64, 65536, 256, 0.25, "ties"),      # the threshold value split between items and lists
+    (8192, 100, 10, 0.3, "ties"),        # 8192 items: the direct-prefix flow's largest grid
+    (40, 56944, 100, 0.3, "whole0"),     # 280 items; B fills the top bucket of the first digit
+    (40, 56944, 100, 0.3, "whole1"),     # ... of the second digit
+    (40, 56944, 100, 0.3, "whole2"),     # ... of the last digit
+    (6, 20100, 100, 0.3, "whole2"),      # the last digit in the two-level flow
 ])
 def test_select_global(lists, n, prot, p, kind):
     say(f"select_global lists={lists} n={n} prot={prot} p={p} kind={kind}")
     if kind.startswith("whole"):
         per = int(np.round(p * (n - prot)))
-        s = bucket_scores(lists, n, prot, per, 0 if kind == "whole0" else 50, seed=lists * n)
+        s = bucket_scores(lists, n, prot, per, 0 if kind == "whole0" else 50, seed=lists * n,
+                          hi_value=NEXT_AFTER_TWO if kind == "whole2" else 2.0078125)
     else:
         s = make_scores(kind, lists, n, seed=lists * n)
     ld, kept_ld = n + 1, n + 2
@@ -427,6 +444,8 @@ def test_select_global_tied_bucket_list_capacity(tied):
     (12, 4, 4, 48, 300, 20, 6, 0.0),       # B = 0: prompts only
     (12, 4, 4, 48, 300, 20, 6, 1.0),       # every candidate kept
     (12, 4, 4, 16, 20000, 100, 6, 0.3),    # several 8192-candidate items per list
+    (48, 16, 4, 8, 65536, 256, 6, 0.25),   # the GateSight model shape at 64K: 512 items, three levels
+    (24, 8, 4, 4, 73000, 0, 6, 0.4),       # 288 items, ragged last item
 ])
 def test_score_select_global(G, L, H, Hg, n, prot, width, p):
     """The fused weighted score + global top-B equals the two calls bit for bit (scores, kept

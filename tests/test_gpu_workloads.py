@@ -1,16 +1,19 @@
 """The five workloads at their real sizes, in the launch configuration the
 benchmark times, checked against the oracle.
 
-Where the oracle cannot redo a whole workload in seconds, sampled lists are
-recomputed one by one by the oracle and compared bit for bit, and properties
-that hold at any size are checked on every list with plain torch ops:
-indices strictly increasing, prompt kept, |S| = K or sum |S| = lists*prot + B,
-and every destination row equal to the source row its index names.
+Keep sets are compared with the oracle's on every list: the oracle draws the
+scores and sorts each list itself, spread over the host's cores (its C calls
+release the interpreter lock).  Compacted K/V are compared on every list with
+a torch gather (contiguous) or page walk (paged) of the source through the
+oracle's kept indices, and on sampled lists with the oracle's own row copies.
+Weighted scores are compared with the oracle's at every position.
 """
 
 import gc
 import math
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -51,12 +54,79 @@ def check_kept_properties(kept, K, prot, n):
     assert int(k.min()) >= 0 and int(k.max()) < n
 
 
-def check_contig_gather(st, K, counts=None, chunk=1024):
-    """dst[list][j] == src[list][kept[list][j]] for every list (torch gather in chunks)."""
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_keep_sets(cfg, round_id, K=None, n=None):
+    """The oracle's kept indices int32 [lists][K] of a random top-K round on every list: its
+    Philox draw and its stable sort, list ranges spread over the host threads."""
+    K = cfg.K if K is None else K
+    n = cfg.n if n is None else n
+    lists = cfg.lists
+    out = np.empty((lists, K), np.int32)
+    step = max(64, -(-lists // (4 * THREADS)))
+
+    def part(l0):
+        l1 = min(lists, l0 + step)
+        sc = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, cfg.seed, round_id, cfg.shared, l0, l1)
+        out[l0:l1] = oracle.select_topk(sc, K, cfg.prot)
+
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        list(ex.map(part, range(0, lists, step)))
+    return out
+
+
+def assert_keep_sets(got, want, what):
+    """Every list's kept indices equal the oracle's; the first differing list is named."""
+    g = got.cpu().numpy() if torch.is_tensor(got) else got
+    g = g[:, :want.shape[1]]
+    if not np.array_equal(g, want):
+        bad = np.nonzero(np.any(g != want, axis=1))[0]
+        raise AssertionError(f"{what}: {len(bad)} of {len(want)} lists differ, first {bad[0]}")
+
+
+def check_paged_gather(st, cfg, kept, K, chunk=128):
+    """Every group's destination pages against a page walk of the source through `kept`: for
+    list (g, h) and j < K, the row of head h at token j of g's destination table equals the
+    row of head h at token kept[j] of its source table (one index list per group when the draw
+    is shared).  Runs on the GPU over groups in chunks."""
+    ps, H, D, groups = cfg.page_size, cfg.H, cfg.D, cfg.groups
+    per_head = kept.shape[0] == groups * H
+    j = torch.arange(K, device=DEV)
+    heads = torch.arange(H, device=DEV)
+    for src, dst in ((st.k_src, st.k_dst), (st.v_src, st.v_dst)):
+        pool_s = src.view(torch.int16).reshape(-1, H, D)  # token-major rows [pages*ps][H][D]
+        pool_d = dst.view(torch.int16).reshape(-1, H, D)
+        for g0 in range(0, groups, chunk):
+            g1 = min(groups, g0 + chunk)
+            gc_ = g1 - g0
+            rows = kept[g0 * H:g1 * H] if per_head else kept[g0:g1]
+            idx = torch.from_numpy(np.ascontiguousarray(rows[:, :K])).to(DEV).long()
+            idx = idx.view(gc_, H if per_head else 1, K)
+            spt = st.src_pt[g0:g1].long()
+            dpt = st.dst_pt[g0:g1].long()
+            src_tok = torch.gather(spt, 1, (idx // ps).reshape(gc_, -1)).view_as(idx) * ps + idx % ps
+            dst_tok = dpt[:, j // ps] * ps + j % ps                        # [gc, K]
+            if per_head:
+                want = pool_s[src_tok, heads[None, :, None]]               # [gc, H, K, D]
+                got = pool_d[dst_tok[:, None, :], heads[None, :, None]]
+            else:
+                want = pool_s[src_tok[:, 0, :]]                            # [gc, K, H, D]
+                got = pool_d[dst_tok]
+            assert torch.equal(got, want), (g0, g1)
+            del want, got
+
+
+def check_contig_gather(st, K, counts=None, chunk=1024, kept=None):
+    """dst[list][j] == src[list][idx[list][j]] for every list (torch gather in chunks), with
+    idx the oracle's kept indices `kept` (host) when given, else the round's own."""
     lists = st.k_src.shape[0]
     for l0 in range(0, lists, chunk):
         l1 = min(lists, l0 + chunk)
-        idx = st.kept[l0:l1, :K].long()
+        if kept is not None:
+            idx = torch.from_numpy(np.ascontiguousarray(kept[l0:l1, :K])).to(DEV).long()
+        else:
+            idx = st.kept[l0:l1, :K].long()
         if counts is not None:
             valid = torch.arange(K, device=DEV)[None, :] < counts[l0:l1, None]
             idx = torch.where(valid, idx, torch.zeros_like(idx))
@@ -101,18 +171,22 @@ def test_tiny_round_full():
     assert st.kv_bytes_moved() == 2 * 1024 * 2 * 256 * 2
 
 
-def test_batch_round_sampled_and_deterministic():
-    """Decode-time batch round (128 x 36 x 8 lists): sampled oracle parity, full properties."""
+def test_batch_round_full_and_deterministic():
+    """Decode-time batch round (128 x 36 x 8 lists): every list's keep set and compacted rows
+    against the oracle's, sampled lists through the oracle's own row copies, determinism."""
     cfg = configs.BATCH
     say("batch round: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st, round_id=0)
     torch.cuda.synchronize()
-    say("batch round: properties")
-    check_kept_properties(st.kept, cfg.K, cfg.prot, cfg.n)
-    check_contig_gather(st, cfg.K)
     assert int(st.errors.item()) == 0
-    say("batch round: sampled oracle parity")
+    say("batch round: the oracle's keep sets of all 36,864 lists")
+    want_all = oracle_keep_sets(cfg, 0)
+    assert_keep_sets(st.kept, want_all, "batch round")
+    say("batch round: every list's rows against a gather through the oracle's indices")
+    check_contig_gather(st, cfg.K, kept=want_all)
+    del want_all
+    say("batch round: sampled lists through the oracle's scorer and row copies")
     rounds.score(st, 0)  # the standalone scorer (the round drew its scores on chip)
     torch.cuda.synchronize()
     for l in sample_lists(cfg.lists, 24, seed=2):
@@ -141,14 +215,21 @@ def test_batch_round_sampled_and_deterministic():
 
 @pytest.mark.parametrize("cfg", [configs.PAGED, configs.PAGED_SHARED, configs.PAGED_SINGLE],
                          ids=["per_head", "shared", "single_request"])
-def test_paged_round_sampled(cfg):
-    """Paged round (64 or 1 request(s) x 36 x 8, 16-token pages): sampled groups against the oracle."""
+def test_paged_round_full(cfg):
+    """Paged round (64 or 1 request(s) x 36 x 8, 16-token pages): every keep set against the
+    oracle's, every group's destination pages against a page walk of the source through the
+    oracle's indices, sampled groups through the oracle's own page-table copies."""
     say(f"paged round {cfg.name}: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st, round_id=3)
     torch.cuda.synchronize()
     assert int(st.errors.item()) == 0
-    check_kept_properties(st.kept, cfg.K, cfg.prot, cfg.n)
+    say(f"paged round {cfg.name}: the oracle's keep sets of all {cfg.lists} lists")
+    want_all = oracle_keep_sets(cfg, 3)
+    assert_keep_sets(st.kept, want_all, cfg.name)
+    say(f"paged round {cfg.name}: every group's pages against a walk through the oracle's indices")
+    check_paged_gather(st, cfg, want_all, cfg.K)
+    del want_all
     ps, H, D = cfg.page_size, cfg.H, cfg.D
     src_pt, dst_pt = st.src_pt.cpu().numpy(), st.dst_pt.cpu().numpy()
     say(f"paged round {cfg.name}: sampled oracle parity")
@@ -194,19 +275,36 @@ def test_global_round():
     counts = st.kept_count
     assert int(counts.sum()) == lists * cfg.prot + B_want
     assert int(st.errors.item()) == 0
-    say("global round: compaction of every list")
-    check_contig_gather(st, cfg.n, counts=counts, chunk=8)
-    say("global round: weighted scores on sampled token ranges")
+    say("global round: weighted scores at all 64 x 32,768 positions against the oracle's")
     beta, vnorm, w = st.beta.cpu().numpy(), st.vnorm.cpu().numpy(), st.weights.cpu().numpy()
-    got = st.scores.cpu().numpy()
-    for t0 in (0, 240, 7777, cfg.n - 300):
-        want = oracle.score_weighted(beta, vnorm, w, *oracle.gdn_windows(cfg.L, cfg.G, cfg.win_width), cfg.prot,
-                                     t_begin=t0, t_end=t0 + 300)
-        g, o = got[:, t0:t0 + 300], want[:, t0:t0 + 300]
-        fin = np.isfinite(o)
-        assert np.array_equal(np.isposinf(g), np.isposinf(o))
-        rel = np.abs(g[fin].astype(np.float64) - o[fin]) / np.maximum(np.abs(o[fin]), 1e-30)
-        assert rel.max() <= 1e-5, float(rel.max())
+    got = st.scores.cpu().numpy()[:, :cfg.n]
+    want = np.empty((lists, cfg.n), np.float32)
+    wins = oracle.gdn_windows(cfg.L, cfg.G, cfg.win_width)
+    step = -(-cfg.n // (4 * THREADS))
+
+    def part(t0):
+        t1 = min(cfg.n, t0 + step)
+        want[:, t0:t1] = oracle.score_weighted(beta, vnorm, w, *wins, cfg.prot, t_begin=t0,
+                                               t_end=t1)[:, t0:t1]
+
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        list(ex.map(part, range(0, cfg.n, step)))
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isposinf(got), np.isposinf(want))
+    rel = np.abs(got[fin].astype(np.float64) - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30)
+    assert rel.max() <= 1e-5, float(rel.max())
+    say(f"  bit-identical fraction {float(np.mean(got[fin] == want[fin])):.6f}, "
+        f"largest relative difference {float(rel.max()):.3g}")
+    say("global round: the oracle's top-B of the round's own scores, every list")
+    want_kept, want_counts, _ = oracle.select_global(got, cfg.prot, cfg.p)
+    assert np.array_equal(st.kept_count.cpu().numpy(), want_counts)
+    got_kept = st.kept.cpu().numpy()
+    for l in range(lists):
+        assert np.array_equal(got_kept[l, :want_counts[l]], want_kept[l, :want_counts[l]]), l
+    say("global round: every list's rows against a gather through the oracle's indices")
+    check_contig_gather(st, cfg.n, counts=torch.from_numpy(want_counts).to(DEV), chunk=8,
+                        kept=want_kept)
+    del beta, vnorm, got, want
     say("global round: selection on identical (oracle-side) scores")
     s = synth.uniform_scores(lists, cfg.n, seed=17, device="cpu").numpy()
     s[:, :cfg.prot] = np.inf
@@ -528,32 +626,63 @@ def test_fused_and_three_launch_rounds_agree():
     free()
 
 
+def check_inplace_gather(st, before_k, before_v, kept, K, chunk=2048):
+    """In place: each list's first K rows are the rows of the cache before the round at the
+    oracle's kept indices, and its rows past K are unchanged (torch, in chunks of lists)."""
+    lists = st.k_src.shape[0]
+    for l0 in range(0, lists, chunk):
+        l1 = min(lists, l0 + chunk)
+        idx = torch.from_numpy(np.ascontiguousarray(kept[l0:l1, :K])).to(DEV).long()
+        for now, before in ((st.k_src, before_k), (st.v_src, before_v)):
+            b = before[l0:l1].view(torch.int16)
+            g = torch.gather(b, 1, idx[:, :, None].expand(-1, -1, b.shape[2]))
+            assert torch.equal(now[l0:l1, :K].view(torch.int16), g), (l0, l1)
+            assert torch.equal(now[l0:l1, K:].view(torch.int16), b[:, K:]), (l0, l1)
+
+
 @pytest.mark.parametrize("base", [configs.LONGGEN, configs.LONGGEN_INPLACE, configs.LONGGEN_FUSED],
                          ids=lambda c: c.name)
-def test_longgen_full_size_two_rounds_sampled(base):
+def test_longgen_full_size_two_rounds(base):
     """The 30-round workload at its full size (36,864 lists of 3136 rows): two rounds of the
-    driver exactly as the benchmark runs them; sampled lists against the oracle (kept indices
-    from its scores, rows from its gather of the cache before the round), properties on every
-    list."""
+    driver exactly as the benchmark runs them.  Every list's keep set against the oracle's
+    (its draw and sort of each round), every list's rows against a gather of the cache before
+    the round through the oracle's indices, sampled lists through the oracle's row copies."""
     cfg = base
     say(f"{cfg.name} full size: allocating")
     st = rounds.make_state(cfg, DEV)
     n, K, D = cfg.n, cfg.K, cfg.D
+    inplace = cfg.inplace
     samples = sample_lists(cfg.lists, 10, seed=11)
     idx = torch.tensor(samples, device=DEV)
     for rnd in range(2):
         before_k, before_v = u16(st.k_src[idx]), u16(st.v_src[idx])
+        if inplace:  # the round overwrites its source: keep a copy of the whole cache
+            whole_k, whole_v = st.k_src.clone(), st.v_src.clone()
         rounds.run_round(st, round_id=rnd)
         torch.cuda.synchronize()
         assert int(st.errors.item()) == 0
-        check_kept_properties(st.kept, K, cfg.prot, n)
-        out_k, out_v = u16(st.k_dst[idx][:, :K]), u16(st.v_dst[idx][:, :K])
+        say(f"{cfg.name} full size: round {rnd}, the oracle's keep sets of all lists")
+        want_all = oracle_keep_sets(cfg, rnd)
+        assert_keep_sets(st.kept, want_all, f"{cfg.name} round {rnd}")
+        say(f"{cfg.name} full size: round {rnd}, every list's rows")
+        if inplace:
+            check_inplace_gather(st, whole_k, whole_v, want_all, K)
+            del whole_k, whole_v
+        else:
+            check_contig_gather(st, K, kept=want_all)
+        out = (st.k_src if inplace else st.k_dst, st.v_src if inplace else st.v_dst)
+        out_k, out_v = u16(out[0][idx][:, :K]), u16(out[1][idx][:, :K])
         for a, l in enumerate(samples):
             want_s = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, cfg.seed, rnd, False, l, l + 1)
-            want_k = oracle.select_topk(want_s, K, cfg.prot)[0]
-            assert np.array_equal(st.kept[l].cpu().numpy(), want_k), (rnd, l)
-            assert np.array_equal(out_k[a], before_k[a][want_k]), (rnd, l)
-            assert np.array_equal(out_v[a], before_v[a][want_k]), (rnd, l)
+            want_k = oracle.select_topk(want_s, K, cfg.prot)
+            assert np.array_equal(want_k[0], want_all[l]), (rnd, l)
+            kd = np.zeros((1, K, D), np.uint16)
+            vd = np.zeros_like(kd)
+            oracle.compact({"list_stride": n * D}, before_k[a:a + 1], before_v[a:a + 1],
+                           {"list_stride": K * D}, kd, vd, want_k, K, D, 1, 0, 1, ipg=1)
+            assert np.array_equal(out_k[a], kd[0]), (rnd, l)
+            assert np.array_equal(out_v[a], vd[0]), (rnd, l)
+        del want_all
         say(f"{cfg.name} full size: round {rnd} ok")
         rounds.append_tokens(st, rnd)
         rounds.swap(st)
