@@ -263,6 +263,33 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
                                      hipStream_t stream);
 
 /*
+ * kvevict_select_global without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: its workspace is a
+ * static device array inside the library, KVEVICT_SELECT_GLOBAL_NOALLOC_BYTES
+ * bytes, one copy per GPU, held until the process ends; its address is looked
+ * up on the first call on each device (hipGetSymbolAddress, with that device
+ * current), so the stream must belong to the current device.
+ *
+ * Arguments, result and validation as kvevict_select_global.  A call whose
+ * workspace (the size kvevict_select_global's query reports) would exceed
+ * KVEVICT_SELECT_GLOBAL_NOALLOC_BYTES returns KVEVICT_ERR_WORKSPACE, nothing
+ * enqueued.  65,536 items fit, an item being a run of up to 8,192 of a list's
+ * candidates [prot, n) (e.g. 1,024 lists of 524,288 candidates).
+ * KVEVICT_ERR_HIP if the array's address cannot be found.  Every call on one
+ * GPU shares that GPU's array and leaves its contents behind (the next call
+ * clears what it needs), so calls that overlap in time on one GPU -- on
+ * different streams, or from different threads -- race and must be ordered by
+ * the caller.
+ */
+#define KVEVICT_SELECT_GLOBAL_NOALLOC_BYTES 1086208
+kvevict_status kvevict_select_global_noalloc(int32_t* kept_idx, int64_t kept_ld,
+                                             int32_t* kept_count, int64_t* budget_out,
+                                             const float* scores, int64_t ld, int64_t num_lists,
+                                             int32_t n, int32_t prot, double p,
+                                             hipStream_t stream);
+
+/*
  * Weighted score and pin + model-wide top-B in one call ([GS] Sec. 4.1 and
  * problem statement; KVzip-style global top-B): the results of
  * kvevict_score_weighted on its arguments followed by kvevict_select_global

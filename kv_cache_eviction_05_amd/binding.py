@@ -31,8 +31,11 @@ EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_top
            "kvevict_select_topk_layers", "kvevict_layer_power_budget", "kvevict_reduce_max_heads",
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
            "kvevict_evict_pages_random", "kvevict_select_random", "kvevict_score_select_global",
-           "kvevict_select_global", "kvevict_compact", "kvevict_status_string",
-           "kvevict_abi_version")
+           "kvevict_select_global", "kvevict_select_global_noalloc", "kvevict_compact",
+           "kvevict_status_string", "kvevict_abi_version")
+
+# size of the static workspace array behind kvevict_select_global_noalloc (kvevict.h)
+SELECT_GLOBAL_NOALLOC_BYTES = 1086208
 
 
 class KvevictError(RuntimeError):
@@ -74,6 +77,8 @@ def load():
     lib.kvevict_select_topk.argtypes = [_p, _i64, _p, _i64, _i64, _i32, _i32, _i32, _p]
     lib.kvevict_select_global.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i32, _i32, _dbl, _p,
                                           ctypes.POINTER(_sz), _p]
+    lib.kvevict_select_global_noalloc.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i32, _i32,
+                                                  _dbl, _p]
     lib.kvevict_score_select_global.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _i64, _i64,
                                                 _i64, _p, _i32, _p, _p, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _dbl, _p, ctypes.POINTER(_sz), _p]
@@ -99,7 +104,7 @@ def load():
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
                  "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
                  "kvevict_evict_pages_random", "kvevict_select_random",
-                 "kvevict_score_select_global"):
+                 "kvevict_score_select_global", "kvevict_select_global_noalloc"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -301,6 +306,20 @@ def kvevict_select_global(kept_idx, kept_ld, kept_count, scores, ld, num_lists, 
                                         ctypes.byref(budget), _ptr(scores), ld, num_lists, n, prot,
                                         p, _ptr(workspace), ctypes.byref(size), _stream(stream)),
            "kvevict_select_global")
+    return budget.value
+
+
+def kvevict_select_global_noalloc(kept_idx, kept_ld, kept_count, scores, ld, num_lists, n, prot,
+                                  p, stream=None) -> int:
+    """kvevict_select_global on the library's static workspace (no allocation)."""
+    _need(scores, torch.float32, _rows(num_lists, ld, n), "scores")
+    _need(kept_idx, torch.int32, _rows(num_lists, kept_ld, n), "kept_idx")
+    _need(kept_count, torch.int32, num_lists, "kept_count")
+    budget = _i64(0)
+    _check(load().kvevict_select_global_noalloc(_ptr(kept_idx), kept_ld, _ptr(kept_count),
+                                                ctypes.byref(budget), _ptr(scores), ld, num_lists,
+                                                n, prot, p, _stream(stream)),
+           "kvevict_select_global_noalloc")
     return budget.value
 
 

@@ -329,6 +329,31 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
                                                   num_lists, n, prot, budget, workspace, stream));
 }
 
+kvevict_status kvevict_select_global_noalloc(int32_t* kept_idx, int64_t kept_ld,
+                                             int32_t* kept_count, int64_t* budget_out,
+                                             const float* scores, int64_t ld, int64_t num_lists,
+                                             int32_t n, int32_t prot, double p,
+                                             hipStream_t stream) {
+  // the arguments, and the workspace the call needs against the static array's size
+  size_t need = 0;
+  int64_t budget = 0;
+  bool launch = false;
+  kvevict_status st = check_global(kept_idx, kept_ld, kept_count, ld, num_lists, n, prot, p,
+                                   nullptr, &need, &budget, &launch);
+  if (st != KVEVICT_OK) return st;
+  if (need > (size_t)KVEVICT_SELECT_GLOBAL_NOALLOC_BYTES) return KVEVICT_ERR_WORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (kvevict::select_global_scratch(&ws, &ws_bytes) != hipSuccess) return KVEVICT_ERR_HIP;
+  st = check_global(kept_idx, kept_ld, kept_count, ld, num_lists, n, prot, p, ws, &ws_bytes,
+                    &budget, &launch);
+  if (st != KVEVICT_OK || !launch) return st;
+  if (num_lists > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
+  if (budget_out) *budget_out = budget;
+  return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
+                                                  num_lists, n, prot, budget, ws, stream));
+}
+
 kvevict_status kvevict_score_select_global(
     int32_t* kept_idx, int64_t kept_ld, int32_t* kept_count, int64_t* budget_out, float* scores,
     int64_t ld, const float* beta, const float* vnorm, int64_t sig_stride_g,

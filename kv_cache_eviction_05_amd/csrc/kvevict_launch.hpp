@@ -44,6 +44,10 @@ hipError_t launch_reduce_max_heads(float* out, int64_t out_ld, const float* scor
 
 size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot);
 
+// The current device's copy of the select's static scratch array (looked up on
+// the first call on each device) and its size in bytes.  No allocation.
+hipError_t select_global_scratch(void** ptr, size_t* bytes);
+
 // The whole global top-B (first_level_done = false), or, after
 // launch_select_global_init and a producer that filled the first-level bins,
 // the rest of it (first_level_done = true).

@@ -37,6 +37,9 @@
 // invalidate every XCD's L2).  Words read only by later kernels of the call
 // (histograms, per-item counts, offsets) are read with plain loads: the kernel
 // boundary makes them visible.
+#include <mutex>
+
+#include "kvevict.h"
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 
@@ -652,6 +655,44 @@ size_t select_global_workspace_bytes(int64_t num_lists, int32_t n, int32_t prot)
   const int64_t M = num_lists * chunks;
   const int64_t words = kArrays + 4 * M + 1 + kCollectCap;
   return (size_t)((words * 4 + 255) / 256 * 256);
+}
+
+// --- the workspace of the allocation-free entry point ------------------------------
+// One static device array per GPU, sized for kScratchItems items of kChunk
+// candidates (the workspace select_global_workspace_bytes asks for at that many
+// items).  Every call on a GPU uses that GPU's copy; the select clears what it
+// needs at the start of each call (init kernel), so nothing carries over.
+constexpr int64_t kScratchItems = 65536;
+constexpr size_t kScratchBytes =
+    (size_t)(((kArrays + 4 * kScratchItems + 1 + kCollectCap) * 4 + 255) / 256 * 256);
+static_assert(kScratchBytes == KVEVICT_SELECT_GLOBAL_NOALLOC_BYTES,
+              "the header states the scratch size");
+
+namespace {
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+}  // namespace
+
+hipError_t select_global_scratch(void** ptr, size_t* bytes) {
+  *ptr = nullptr;
+  *bytes = kScratchBytes;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {  // first call on this device, which is current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 namespace {

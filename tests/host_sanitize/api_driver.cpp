@@ -158,6 +158,15 @@ int main() {
                               nullptr, nullptr), INV, false);
   CHECK(kvevict_select_global(idx, 32768, cnt, &budget, sc, 32768, 64, 32768, 256, 0.25,
                               fake<uint8_t>(5) + 2, &wsb, nullptr), ALIGN, false);
+  // allocation-free variant: the static array's size bounds the call
+  CHECK(kvevict_select_global_noalloc(idx, 32768, cnt, &budget, sc, 32768, 64, 32768, 256, 0.25,
+                                      nullptr), OK, true);
+  CHECK(kvevict_select_global_noalloc(idx, 100, cnt, &budget, sc, 100, 65600, 100, 10, 0.3,
+                                      nullptr), WS, false);  // more than the array holds
+  CHECK(kvevict_select_global_noalloc(idx, 32768, cnt, &budget, sc, 32768, 64, 32768, 256, NAN,
+                                      nullptr), INV, false);
+  CHECK(kvevict_select_global_noalloc(idx, 32768, cnt, &budget, nullptr, 32768, 64, 32768, 256,
+                                      0.25, nullptr), INV, false);  // no scores
   size_t wsb2 = 0;
   CHECK(kvevict_score_select_global(idx, 32768, cnt, &budget, sc, 32768, sig, sig, 32768 * 48, 48,
                                     1, sig, 6, wb, wc, 2, 4, 6, 48, 32768, 256, 0.25, nullptr,

@@ -72,6 +72,13 @@ hipError_t launch_select_global(int32_t*, int64_t kept_ld, int32_t*, const float
   return launched();
 }
 
+hipError_t select_global_scratch(void** ptr, size_t* bytes) {
+  alignas(256) static unsigned char stand_in[256];  // a stand-in address, never dereferenced
+  *ptr = &stand_in;
+  *bytes = 1086208;
+  return hipSuccess;
+}
+
 hipError_t launch_select_global_init(int32_t*, int64_t, int32_t*, int64_t num_lists, int32_t n,
                                      int32_t prot, int64_t budget, void* workspace, hipStream_t) {
   need(num_lists >= 0 && prot >= 0 && prot <= n && budget >= 0 && workspace, "init sizes");

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                           "kvevict_compact_inplace", "kvevict_evict_random_inplace",
                           "kvevict_evict_pages_random", "kvevict_select_random",
                           "kvevict_score_select_global",
-                          "kvevict_select_global", "kvevict_compact",
+                          "kvevict_select_global", "kvevict_select_global_noalloc",
+                          "kvevict_compact",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
@@ -112,6 +113,25 @@ def test_select_global_workspace_protocol_and_validation():
                   0, 0.5, FAKE, ctypes.byref(size), None) == B.KVEVICT_ERR_INVALID_ARG  # > 2^31
     assert status("kvevict_select_global", FAKE, 32768, FAKE, None, FAKE, 32768, 64, 32768, 256,
                   0.25, FAKE, None, None) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_select_global_noalloc_validation():
+    """The allocation-free global top-B validates like kvevict_select_global, and a call whose
+    workspace would exceed the static array is rejected with KVEVICT_ERR_WORKSPACE before any
+    HIP call (65,600 items of one 90-candidate run each)."""
+    st = lambda *a: status("kvevict_select_global_noalloc", *a)
+    assert st(FAKE, 100, FAKE, None, FAKE, 100, 65600, 100, 10, 0.3, None) == B.KVEVICT_ERR_WORKSPACE
+    assert B.kvevict_select_global_workspace(65600, 100, 10) > B.SELECT_GLOBAL_NOALLOC_BYTES
+    assert B.kvevict_select_global_workspace(65536, 100, 10) == B.SELECT_GLOBAL_NOALLOC_BYTES
+    assert B.kvevict_select_global_workspace(1024, 524288 + 256, 256) == B.SELECT_GLOBAL_NOALLOC_BYTES
+    INV = B.KVEVICT_ERR_INVALID_ARG
+    assert st(FAKE, 100, FAKE, None, FAKE, 99, 4, 100, 10, 0.3, None) == INV        # ld < n
+    assert st(FAKE, 99, FAKE, None, FAKE, 100, 4, 100, 10, 0.3, None) == INV        # kept_ld < n
+    assert st(FAKE, 100, FAKE, None, FAKE, 100, 4, 100, 101, 0.3, None) == INV      # prot > n
+    for p in (-0.5, 1.01, float("nan")):
+        assert st(FAKE, 100, FAKE, None, FAKE, 100, 4, 100, 10, p, None) == INV
+    assert st(FAKE, 1 << 20, FAKE, None, FAKE, 1 << 20, 4096, 1 << 20, 0, 0.5, None) == INV  # > 2^31
+    assert st(FAKE, 100, FAKE, None, FAKE, 100, -1, 100, 10, 0.3, None) == INV
 
 
 def test_score_select_global_validation():
