@@ -5,19 +5,33 @@
 A step is one whole eviction round (score -> pin + select -> compact) over one
 batch of synthetic inputs resident in HBM.  The headline workload is the
 decode-time batch round (128 requests x 36 layers x 8 KV heads, D=128,
-n=1088, K=1024, prot=128, contiguous storage, per-head random draw).  Other
-workloads, if requested, are reported under "workloads".  Prints ONE JSON line.
+n=1088, K=1024, prot=128, contiguous storage, per-head random draw).  By
+default the other configurations are timed too and reported under
+"workloads": the tiny round, the paged round in per-head and shared-draw
+modes, the GateSight-shaped global round and the 30-round long generation
+(exactly its 30 rounds after the warmup, with the survival curve).  Prints
+ONE JSON line.
 
 Timing: W untimed rounds, then exactly K rounds between two synchronisations;
 HIP events on the launch stream bracket every kernel launch of the round, so
-each step of the round gets its own average duration.  The roofline entry
-prices the dominant kernel (the K/V gather) at its algorithmic bytes: the
-kept K and V rows, each read once and written once.  Workloads whose round
-takes under 1 ms and leaves its inputs intact are also replayed from a HIP
-graph of ten rounds (graph_ms_per_round): the device time without the host
-launch path.  Rounds with a separate select are also timed over selection +
-compaction alone as one interval (select_compact: eager, and from a HIP
-graph), with no event between the select and the gather.
+each step of the round gets its own average duration.  Every workload carries
+a roofline entry for its dominant kernel, the K/V gather, priced at its
+algorithmic bytes (the kept K and V rows, each read once and written once),
+with the HBM bytes its FETCH_SIZE/WRITE_SIZE counters measured
+(profiles/gather_traffic.json, null once the gather's source has changed).
+Workloads whose round takes under 1 ms and leaves its inputs intact are also
+replayed from a HIP graph of ten rounds (graph_ms_per_round).  Out-of-place
+rounds are also timed over selection + compaction alone as one interval
+(select_compact: eager, and from a HIP graph), with no event between the
+select and the gather.  The paged rounds carry a ceiling: a plain copy of the
+same bytes, whole pages through the same random page tables.
+
+    python bench.py --summarize-traffic WORKLOAD FETCH.csv WRITE.csv
+
+folds the per-dispatch counters of two rocprofv3 --pmc runs (FETCH_SIZE, then
+WRITE_SIZE) of `bench.py --profile-workload WORKLOAD` into
+profiles/gather_traffic.json, scaled by a plain copy's counters
+(`--summarize-traffic copy` over two runs of `bench.py --copy-calibration`).
 """
 
 from __future__ import annotations
@@ -34,8 +48,12 @@ sys.path.insert(0, HERE)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "eviction rounds/sec and achieved HBM GB/s (fraction of peak) per MI355X"
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "compact_batch_traffic.json")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gather_traffic.json")
 COMPACT_SRC = os.path.join(HERE, "kv_cache_eviction_05_amd", "csrc", "compact.hip")
+DEFAULT_WORKLOADS = "batch,tiny,paged,paged_shared,global,longgen"
+ALL_WORKLOADS = ["batch", "tiny", "paged", "paged_shared", "global", "global_fused", "longgen",
+                 "layers", "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
+                 "paged_fused", "longgen_fused", "paged_pages", "paged_single"]
 
 
 def parse():
@@ -43,12 +61,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="batch",
-                    help="comma list of workload names from configs.ALL (or 'all')")
+    ap.add_argument("--workloads", default=DEFAULT_WORKLOADS,
+                    help="comma list of workload names from configs.ALL (or 'all'); the "
+                         "headline batch round is always timed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for PMC scaling)")
+    ap.add_argument("--profile-workload", default=None,
+                    help="time this one workload only (no headline, no baselines): the "
+                         "process that rocprofv3 counter runs wrap")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV"),
+                    help="fold two rocprofv3 --pmc counter files into " + TRAFFIC_FILE)
     return ap.parse_args()
 
 
@@ -130,17 +154,19 @@ def time_workload(torch, rounds, cfg, steps, warmup):
     round_id = 0
     survival = None
     if cfg.rounds > 1:
-        # repeated rounds: each step is one round of the persistent-budget loop; the
-        # append of r fresh tokens between rounds is input synthesis and stays untimed,
-        # and so does the survival bookkeeping on sampled lists
-        survival = rounds.SurvivalTracker(st)
+        # repeated rounds: after the warmup rounds, exactly cfg.rounds rounds of the
+        # persistent-budget loop are timed, one step each, and the survival curve follows
+        # the entries present when they start; the append of r fresh tokens between rounds
+        # is input synthesis and stays untimed, and so does the survival bookkeeping on
+        # sampled lists
+        steps = cfg.rounds
         for _ in range(warmup):
             rounds.run_round(st, round_id)
-            survival.after_round(st)
             rounds.append_tokens(st, round_id)
             rounds.swap(st)
             round_id += 1
         torch.cuda.synchronize()
+        survival = rounds.SurvivalTracker(st)
         timer = Timer(torch, [name for name, _ in phases])
         total_ms = 0.0
         for _ in range(steps):
@@ -200,7 +226,7 @@ def time_workload(torch, rounds, cfg, steps, warmup):
     kv_bytes = st.kv_bytes_moved()
     errors = int(st.errors.item())
     out = {"state": st, "ms_per_step": ms_per, "kernels_ms": kern, "kv_bytes": kv_bytes,
-           "round_ms_dist": dist, "algorithmic_bytes": st.algorithmic_bytes(),
+           "round_ms_dist": dist, "algorithmic_bytes": st.algorithmic_bytes(), "steps": steps,
            "errors": errors, "applied_rounds": st.applied_rounds - warmup,
            "budget": st.budget, "survival": survival.report(st) if survival else None}
     return out
@@ -266,16 +292,119 @@ def select_compact_ms(torch, rounds, st, steps):
     return eager, e0.elapsed_time(e1) / (reps * GRAPH_ROUNDS)
 
 
-def traffic_for(kv_bytes):
-    """Measured HBM bytes per launch of the gather, if the counters match this source."""
+GATHER_KERNELS = ("compact_list_kernel", "compact_group_kernel")
+
+
+def load_traffic() -> dict:
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            return json.load(f)
     except (OSError, ValueError):
+        return {}
+
+
+def traffic_for(name):
+    """Measured HBM bytes per launch of a workload's gather, if its counters were taken on
+    the gather's current source (else None: the kernel changed since)."""
+    t = load_traffic().get("workloads", {}).get(name)
+    if not t or t.get("source_sha256_16") != source_hash(COMPACT_SRC):
         return None
-    if t.get("source_sha256_16") != source_hash(COMPACT_SRC):
-        return None  # the kernel changed since the counters were taken
     return t.get("bytes_per_launch")
+
+
+def read_counter_csv(path, counter, match):
+    """Per-dispatch sums of `counter` (KiB) over the dispatches whose kernel name contains
+    one of `match`, from a rocprofv3 counter_collection.csv."""
+    import csv
+
+    per = {}
+    names = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter or not any(m in row["Kernel_Name"] for m in match):
+                continue
+            d = row["Dispatch_Id"]
+            per[d] = per.get(d, 0.0) + float(row["Counter_Value"])
+            names[d] = row["Kernel_Name"]
+    return per, names
+
+
+def summarize_traffic(name, fetch_csv, write_csv):
+    """Fold two counter runs into TRAFFIC_FILE: the plain copy's scale factors (name
+    'copy', over runs of --copy-calibration: 3 copies of 4 GiB), or a workload's gather
+    bytes per launch (over runs of --profile-workload), scaled by those factors."""
+    t = load_traffic()
+    if name == "copy":
+        f, _ = read_counter_csv(fetch_csv, "FETCH_SIZE", ("copyBuffer",))
+        w, _ = read_counter_csv(write_csv, "WRITE_SIZE", ("copyBuffer",))
+        big = lambda d: [v for v in d.values() if v > 1e6]  # the 4 GiB copies, not set-up fills
+        fk, wk = big(f), big(w)
+        copied = 4 << 30
+        t["copy_calibration"] = {
+            "bytes": copied, "dispatches": [len(fk), len(wk)],
+            "fetch_kib": sum(fk) / len(fk), "write_kib": sum(wk) / len(wk),
+            "fetch_scale": copied / (1024 * sum(fk) / len(fk)),
+            "write_scale": copied / (1024 * sum(wk) / len(wk)),
+            "commands": {c: f"rocprofv3 --pmc {c} --output-format csv -d <dir> -- "
+                            f"python3 bench.py --copy-calibration" for c in ("FETCH_SIZE",
+                                                                                "WRITE_SIZE")}}
+    else:
+        cal = t["copy_calibration"]
+        f, names = read_counter_csv(fetch_csv, "FETCH_SIZE", GATHER_KERNELS)
+        w, _ = read_counter_csv(write_csv, "WRITE_SIZE", GATHER_KERNELS)
+        fb = 1024 * cal["fetch_scale"] * sum(f.values()) / len(f)
+        wb = 1024 * cal["write_scale"] * sum(w.values()) / len(w)
+        t.setdefault("workloads", {})[name] = {
+            "kernel": sorted(set(names.values()))[0],
+            "source": os.path.relpath(COMPACT_SRC, HERE),
+            "source_sha256_16": source_hash(COMPACT_SRC),
+            "dispatches": [len(f), len(w)],
+            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "bytes_per_launch": fb + wb,
+            "commands": {c: f"rocprofv3 --pmc {c} --output-format csv -d <dir> -- "
+                            f"python3 bench.py --profile-workload {name} --steps 2 --warmup 0"
+                         for c in ("FETCH_SIZE", "WRITE_SIZE")}}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(t.get("workloads", {}).get(name, t.get("copy_calibration"))))
+
+
+def roofline(name, cfg, kv_bytes, comp_ms):
+    """The workload's dominant kernel, the K/V gather, against the HBM peak."""
+    achieved = kv_bytes / (comp_ms * 1e-3) / 1e9
+    kernel = ("compact_group_kernel (paged K/V gather)" if cfg.layout == "paged" else
+              "compact_list_kernel (contiguous K/V gather)")
+    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_for(name),
+            "algorithmic_bytes": kv_bytes, "ms": round(comp_ms, 4)}
+
+
+def paged_copy_ceiling(torch, binding, st, cfg, gather_gbps, reps=5):
+    """A plain copy of the paged gather's bytes through the same random page tables: every
+    destination page of the round filled whole, K and V, from the source page its group's
+    table holds at the same position (kvevict_copy_pages).  Overwrites the destination."""
+    kp = cfg.K // cfg.page_size
+    src_ids = st.src_pt[:, :kp].reshape(-1).contiguous()
+    dst_ids = st.dst_pt[:, :kp].reshape(-1).contiguous()
+    page_bytes = cfg.page_size * cfg.H * cfg.D * 2
+    moved = 2 * 2 * src_ids.numel() * page_bytes  # K and V, read and written
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    run = lambda: binding.kvevict_copy_pages(st.k_src, st.v_src, src_ids, st.k_dst, st.v_dst,
+                                             dst_ids, page_bytes, err)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = moved / (ms * 1e-3) / 1e9
+    return {"bytes_moved": moved, "ms": round(ms, 4), "gbps": gbps,
+            "frac_of_peak": gbps / PEAK_HBM_GBPS, "gather_vs_copy": gather_gbps / gbps,
+            "bad_pages": int(err.item())}
 
 
 def cpu_baseline(torch, cfg, st, seconds):
@@ -427,8 +556,90 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
+def measure(torch, binding, configs, rounds, name, args, headline):
+    """Times one workload and returns its entry (and the state, for the baselines)."""
+    cfg = configs.ALL[name]
+    print(f"# timing {name}", file=sys.stderr, flush=True)
+    r = time_workload(torch, rounds, cfg, args.steps, args.warmup)
+    steps = r["steps"]
+    main_phase = "pages" if cfg.page_draw else "fused" if cfg.fused else "compact"
+    comp_ms = r["kernels_ms"][main_phase]
+    achieved = r["kv_bytes"] / (comp_ms * 1e-3) / 1e9
+    entry = {
+        "workload": describe(cfg),
+        "rounds_per_s": 1e3 / r["ms_per_step"],
+        "ms_per_round": r["ms_per_step"],
+        "steps": steps,
+        "kernel_ms": {k: round(v, 4) for k, v in r["kernels_ms"].items()},
+        "kv_bytes_per_round": r["kv_bytes"],
+        "kv_gbps_round": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+        "compact_gbps": achieved if not cfg.page_draw else None,
+        "compact_frac_of_peak": achieved / PEAK_HBM_GBPS if not cfg.page_draw else None,
+        "round_ms_p10_p50_p90": [round(r["round_ms_dist"][q], 4) for q in ("p10", "p50", "p90")],
+        "algorithmic_bytes_per_round": r["algorithmic_bytes"],
+        "applied_rounds": r["applied_rounds"],
+        "bad_rows": r["errors"],
+    }
+    if not cfg.page_draw:
+        entry["roofline"] = roofline(name, cfg, r["kv_bytes"], comp_ms)
+    if cfg.scorer == "weighted" and "score" in r["kernels_ms"]:
+        # the weighted scorer: GDN signals read once, scores written once
+        lists = cfg.L * cfg.H * cfg.R
+        sb = r["algorithmic_bytes"]["inputs"] + lists * r["state"].n * 4
+        sg = sb / (r["kernels_ms"]["score"] * 1e-3) / 1e9
+        entry["roofline_score"] = {"bound": "hbm", "kernel": "score_weighted_kernel",
+                                   "achieved": sg, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                   "frac": sg / PEAK_HBM_GBPS, "algorithmic_bytes": sb,
+                                   "ms": round(r["kernels_ms"]["score"], 4)}
+    st = r["state"]
+    if r["ms_per_step"] < 1.0 and not (cfg.inplace or cfg.page_draw or cfg.rounds > 1):
+        # latency-bound rounds: also replayed from a HIP graph
+        g_ms = graph_replay_ms(torch, rounds, st, max(steps, 10 * GRAPH_ROUNDS))
+        entry["graph_ms_per_round"] = g_ms
+        entry["graph_rounds_per_s"] = 1e3 / g_ms
+    if (not (cfg.inplace or cfg.page_draw or cfg.fused or cfg.fuse_score)
+            and any(p in ("select", "draw_select") for p, _ in rounds.phases(cfg))):
+        sc_eager, sc_graph = select_compact_ms(torch, rounds, st, max(steps, 20))
+        entry["select_compact"] = {
+            "ms": round(sc_eager, 4), "graph_ms": round(sc_graph, 4),
+            "kv_gbps": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9,
+            "frac_of_peak": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "frac_of_peak_graph": r["kv_bytes"] / (sc_graph * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        }
+    if cfg.select in ("global", "layers"):
+        entry["budget"] = r["budget"]
+    if cfg.select == "layers":
+        entry["vs_global_top_b"] = rounds.compare_with_global(st)
+    if cfg.page_draw:
+        P, Kp = cfg.n // cfg.page_size, cfg.K // cfg.page_size
+        entry["pages_evicted_per_round"] = cfg.groups * (P - Kp)
+        entry["table_bytes_per_round"] = cfg.groups * (P * 4 * 2 + (P - Kp) * 4)
+    if r["survival"] is not None:
+        entry["survival"] = r["survival"]
+    if args.profile_workload is None:
+        if name in ("tiny", "global") and not args.no_cpu_baseline:
+            print(f"# cpu baseline on one thread (oracle): {name}", file=sys.stderr, flush=True)
+            entry["cpu_baseline_1_thread"] = cpu_single_thread(torch, cfg, st)
+        if headline:
+            entry["dtod_copy"] = dtod_copy(torch, r["kv_bytes"], achieved)
+            if not args.no_cpu_baseline:
+                print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+                entry["cpu"] = cpu_baseline(torch, cfg, st, args.cpu_seconds)
+        if cfg.layout == "paged" and not (cfg.inplace or cfg.page_draw):
+            # last: the copy overwrites the round's destination pages
+            entry["page_copy_ceiling"] = paged_copy_ceiling(torch, binding, st, cfg, achieved)
+    del r["state"], st
+    r.clear()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return cfg, entry
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(every list is independent, so throughput at N GPUs is N x the one-GPU value "
@@ -442,80 +653,25 @@ def main():
     from kv_cache_eviction_05_amd import binding, configs, rounds
 
     binding.load()
+    if args.profile_workload is not None:
+        _, e = measure(torch, binding, configs, rounds, args.profile_workload, args, False)
+        print(json.dumps({"workload": args.profile_workload, "kernel_ms": e["kernel_ms"],
+                          "roofline": e.get("roofline")}), flush=True)
+        return
     names = [w for w in args.workloads.split(",") if w]
     if names == ["all"]:
-        names = ["batch", "tiny", "paged", "paged_shared", "global", "global_fused", "longgen",
-                 "layers",
-                 "paged_shared_max", "keydiff", "paged_inplace", "longgen_inplace",
-                 "paged_fused", "longgen_fused", "paged_pages", "paged_single"]
-    if "batch" not in names:
-        names = ["batch"] + names
+        names = list(ALL_WORKLOADS)
+    names = ["batch"] + [n for n in names if n != "batch"]
     head = None
     extra = {}
     for name in names:
-        cfg = configs.ALL[name]
-        print(f"# timing {name}", file=sys.stderr, flush=True)
-        steps = args.steps if cfg.rounds == 1 else min(args.steps, cfg.rounds)
-        r = time_workload(torch, rounds, cfg, steps, args.warmup)
-        main_phase = "pages" if cfg.page_draw else "fused" if cfg.fused else "compact"
-        comp_ms = r["kernels_ms"][main_phase]
-        achieved = r["kv_bytes"] / (comp_ms * 1e-3) / 1e9
-        entry = {
-            "workload": describe(cfg),
-            "rounds_per_s": 1e3 / r["ms_per_step"],
-            "ms_per_round": r["ms_per_step"],
-            "kernel_ms": {k: round(v, 4) for k, v in r["kernels_ms"].items()},
-            "kv_bytes_per_round": r["kv_bytes"],
-            "kv_gbps_round": r["kv_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
-            "compact_gbps": achieved if not cfg.page_draw else None,
-            "compact_frac_of_peak": achieved / PEAK_HBM_GBPS if not cfg.page_draw else None,
-            "round_ms_p10_p50_p90": [round(r["round_ms_dist"][q], 4) for q in ("p10", "p50", "p90")],
-            "algorithmic_bytes_per_round": r["algorithmic_bytes"],
-            "applied_rounds": r["applied_rounds"],
-            "bad_rows": r["errors"],
-        }
-        if r["ms_per_step"] < 1.0 and not (cfg.inplace or cfg.page_draw or cfg.rounds > 1):
-            # latency-bound rounds: also replayed from a HIP graph
-            g_ms = graph_replay_ms(torch, rounds, r["state"], max(steps, 10 * GRAPH_ROUNDS))
-            entry["graph_ms_per_round"] = g_ms
-            entry["graph_rounds_per_s"] = 1e3 / g_ms
-        if (cfg.rounds == 1 and not (cfg.inplace or cfg.page_draw or cfg.fused or cfg.fuse_score)
-                and any(p in ("select", "draw_select") for p, _ in rounds.phases(cfg))):
-            sc_eager, sc_graph = select_compact_ms(torch, rounds, r["state"], max(steps, 20))
-            entry["select_compact"] = {
-                "ms": round(sc_eager, 4), "graph_ms": round(sc_graph, 4),
-                "kv_gbps": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9,
-                "frac_of_peak": r["kv_bytes"] / (sc_eager * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                "frac_of_peak_graph": r["kv_bytes"] / (sc_graph * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-            }
-        if name in ("tiny", "global") and not args.no_cpu_baseline:
-            print(f"# cpu baseline on one thread (oracle): {name}", file=sys.stderr, flush=True)
-            entry["cpu_baseline_1_thread"] = cpu_single_thread(torch, cfg, r["state"])
-        if cfg.select in ("global", "layers"):
-            entry["budget"] = r["budget"]
-        if cfg.select == "layers":
-            entry["vs_global_top_b"] = rounds.compare_with_global(r["state"])
-        if cfg.page_draw:
-            P, Kp = cfg.n // cfg.page_size, cfg.K // cfg.page_size
-            entry["pages_evicted_per_round"] = cfg.groups * (P - Kp)
-            entry["table_bytes_per_round"] = cfg.groups * (P * 4 * 2 + (P - Kp) * 4)
-        if r["survival"] is not None:
-            entry["survival"] = r["survival"]
+        cfg, entry = measure(torch, binding, configs, rounds, name, args, name == "batch")
         if name == "batch":
-            entry["dtod_copy"] = dtod_copy(torch, r["kv_bytes"], achieved)
-            head = (cfg, r, entry)
-            if not args.no_cpu_baseline:
-                print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-                head[2]["cpu"] = cpu_baseline(torch, cfg, r["state"], args.cpu_seconds)
+            head = (cfg, entry)
         else:
             extra[name] = entry
-        del r["state"]
-        r.clear()
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
 
-    cfg, r, e = head
-    comp_ms = e["kernel_ms"]["compact"]
+    cfg, e = head
     line = {
         "metric": METRIC,
         "value": e["rounds_per_s"],
@@ -533,16 +689,7 @@ def main():
                    "prot": cfg.prot, "head_dim": cfg.D},
         "kv_gbps": e["kv_gbps_round"],
         "kernel_ms": e["kernel_ms"],
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "compact (K/V gather)",
-            "achieved": e["compact_gbps"],
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": e["compact_gbps"] / PEAK_HBM_GBPS,
-            "traffic": traffic_for(e["kv_bytes_per_round"]),
-            "algorithmic_bytes": e["kv_bytes_per_round"],
-        },
+        "roofline": e["roofline"],
         "round_ms_p10_p50_p90": e["round_ms_p10_p50_p90"],
         "select_compact": e.get("select_compact"),
         "algorithmic_bytes_per_round": e["algorithmic_bytes_per_round"],

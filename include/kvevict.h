@@ -342,6 +342,28 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
                                hipStream_t stream);
 
 /*
+ * Whole-page copy between page pools (GateSight Sec. 4.3: the cache is a pool
+ * of fixed-size blocks behind per-layer block tables; a block moves as a unit).
+ *
+ * For i < count:  K_dst page dst_ids[i] = K_src page src_ids[i], and the same
+ * for V, a page being page_bytes bytes at byte offset id*page_bytes of its
+ * pool.  It is the paged gather with every slot of each page kept in order and
+ * no per-row index: over the same tables it is the copy ceiling of
+ * kvevict_compact on paged stores.
+ * k_src, v_src   device pools of src_pages pages;  k_dst, v_dst  of dst_pages.
+ * src_ids, dst_ids  device int32 [count]; a pair with an id outside its pool
+ *                is skipped and adds 1 to *errors (optional device uint32).
+ * Requires page_bytes > 0 and a multiple of 16 (KVEVICT_ERR_ALIGNMENT), 16-byte
+ * aligned pools, and no destination byte in either source pool nor in the
+ * other destination pool (KVEVICT_ERR_INVALID_ARG).  Destination pages listed
+ * twice race.
+ */
+kvevict_status kvevict_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,
+                                  const int32_t* src_ids, void* k_dst, void* v_dst,
+                                  int64_t dst_pages, const int32_t* dst_ids, int64_t count,
+                                  int64_t page_bytes, uint32_t* errors, hipStream_t stream);
+
+/*
  * In-place chronological compaction with a free-page list (GateSight Sec. 4.3
  * and Appendix G: each layer moves the entries it keeps to the front of its
  * own pages, and the freed tail blocks return to the pool, which releases

@@ -32,6 +32,7 @@ EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_top
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
            "kvevict_evict_pages_random", "kvevict_select_random", "kvevict_score_select_global",
            "kvevict_select_global", "kvevict_select_global_noalloc", "kvevict_compact",
+           "kvevict_copy_pages",
            "kvevict_status_string", "kvevict_abi_version")
 
 # size of the static workspace array behind kvevict_select_global_noalloc (kvevict.h)
@@ -97,6 +98,7 @@ def load():
     lib.kvevict_evict_random_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _i64, _i32, _i32,
                                                  _i32, _i32, _u64, _u32, _i32, _p, _i64, _p, _p,
                                                  _p, _p]
+    lib.kvevict_copy_pages.argtypes = [_p, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _p, _p]
     lib.kvevict_compact_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _p, _i64, _p, _i32,
                                             _i32, _i64, _i32, _p, _p, _p, _p]
     for name in ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_topk",
@@ -104,7 +106,8 @@ def load():
                  "kvevict_reduce_max_heads", "kvevict_score_keydiff", "kvevict_select_global",
                  "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
                  "kvevict_evict_pages_random", "kvevict_select_random",
-                 "kvevict_score_select_global", "kvevict_select_global_noalloc"):
+                 "kvevict_score_select_global", "kvevict_select_global_noalloc",
+                 "kvevict_copy_pages"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -350,6 +353,26 @@ def kvevict_compact(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_i
 
 def kvevict_abi_version() -> int:
     return int(load().kvevict_abi_version())
+
+
+def kvevict_copy_pages(k_src, v_src, src_ids, k_dst, v_dst, dst_ids, page_bytes, errors=None,
+                       stream=None):
+    """Whole pages of the K and V pools from src_ids to dst_ids (pools as flat tensors)."""
+    count = int(src_ids.numel())
+    for t, what in ((k_src, "k_src"), (v_src, "v_src"), (k_dst, "k_dst"), (v_dst, "v_dst")):
+        _need(t, None, 1, what)
+    _need(dst_ids, torch.int32, count, "dst_ids")
+    _need(src_ids, torch.int32, count, "src_ids")
+    src_pages = k_src.numel() * k_src.element_size() // page_bytes
+    dst_pages = k_dst.numel() * k_dst.element_size() // page_bytes
+    for t, pages, what in ((v_src, src_pages, "v_src"), (v_dst, dst_pages, "v_dst")):
+        if t.numel() * t.element_size() < pages * page_bytes:
+            raise ValueError(f"{what}: smaller than its K pool")
+    _need(errors, torch.int32, 1, "errors")
+    _check(load().kvevict_copy_pages(_ptr(k_src), _ptr(v_src), src_pages, _ptr(src_ids),
+                                     _ptr(k_dst), _ptr(v_dst), dst_pages, _ptr(dst_ids), count,
+                                     page_bytes, _ptr(errors), _stream(stream)),
+           "kvevict_copy_pages")
 
 
 def kvevict_compact_inplace(store: KvDesc, k, v, kept_idx, kept_ld, kept_count, K, n, num_groups,

@@ -424,6 +424,29 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
                                             idx_lists_per_group, errors, stream));
 }
 
+kvevict_status kvevict_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,
+                                  const int32_t* src_ids, void* k_dst, void* v_dst,
+                                  int64_t dst_pages, const int32_t* dst_ids, int64_t count,
+                                  int64_t page_bytes, uint32_t* errors, hipStream_t stream) {
+  if (count < 0 || src_pages < 0 || dst_pages < 0) return KVEVICT_ERR_INVALID_ARG;
+  if (page_bytes <= 0) return KVEVICT_ERR_INVALID_ARG;
+  if (page_bytes % 16 != 0) return KVEVICT_ERR_ALIGNMENT;
+  if (count == 0) return KVEVICT_OK;
+  if (!k_src || !v_src || !k_dst || !v_dst || !src_ids || !dst_ids) return KVEVICT_ERR_INVALID_ARG;
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_dst) || !aligned16(v_dst))
+    return KVEVICT_ERR_ALIGNMENT;
+  if (!prod_le(src_pages, page_bytes, INT64_MAX) || !prod_le(dst_pages, page_bytes, INT64_MAX))
+    return KVEVICT_ERR_INVALID_ARG;
+  const u128 se = (u128)src_pages * (u128)page_bytes, de = (u128)dst_pages * (u128)page_bytes;
+  if (ranges_overlap(k_dst, de, k_src, se) || ranges_overlap(k_dst, de, v_src, se) ||
+      ranges_overlap(v_dst, de, k_src, se) || ranges_overlap(v_dst, de, v_src, se) ||
+      ranges_overlap(k_dst, de, v_dst, de))
+    return KVEVICT_ERR_INVALID_ARG;
+  return hip_status(kvevict::launch_copy_pages(k_src, v_src, src_pages, src_ids, k_dst, v_dst,
+                                               dst_pages, dst_ids, count, page_bytes, errors,
+                                               stream));
+}
+
 kvevict_status kvevict_compact_inplace(const kvevict_kv_desc* store, void* k, void* v,
                                        const int32_t* kept_idx, int64_t kept_ld,
                                        const int32_t* kept_count, int32_t K, int32_t n,

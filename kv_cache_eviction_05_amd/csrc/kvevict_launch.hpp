@@ -64,6 +64,12 @@ hipError_t launch_select_global_init(int32_t* kept_idx, int64_t kept_ld, int32_t
 uint32_t* select_global_first_level_bins(int64_t num_lists, int32_t n, int32_t prot,
                                          int64_t budget, void* workspace);
 
+// Whole pages of K and V from src_ids to dst_ids (page_bytes a multiple of 16).
+hipError_t launch_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,
+                             const int32_t* src_ids, void* k_dst, void* v_dst, int64_t dst_pages,
+                             const int32_t* dst_ids, int64_t count, int64_t page_bytes,
+                             uint32_t* errors, hipStream_t stream);
+
 // One K/V store as the compaction kernels see it (units: 16-byte vectors).
 struct StoreView {
   int32_t paged;

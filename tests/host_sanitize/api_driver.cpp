@@ -234,6 +234,25 @@ int main() {
   CHECK(kvevict_score_keydiff(sc, 1088, &keys96, ks, 16, 1088, 128, nullptr), UNSUP, false);
   CHECK(kvevict_score_keydiff(sc, 1088, &keys, ks, huge, 1088, 128, nullptr), INV, false);
 
+  // whole-page copies
+  {
+    const int32_t* ids = fake<const int32_t>(13);
+    CHECK(kvevict_copy_pages(ks, vs, 304128, ids, kd, vd, 294912, ids, 294912, 32768, nullptr,
+                             nullptr), OK, true);
+    CHECK(kvevict_copy_pages(ks, vs, 304128, ids, kd, vd, 294912, ids, 0, 32768, nullptr,
+                             nullptr), OK, false);  // nothing to copy
+    CHECK(kvevict_copy_pages(ks, vs, 304128, ids, kd, vd, 294912, ids, 10, 24, nullptr, nullptr),
+          ALIGN, false);
+    CHECK(kvevict_copy_pages(ks, vs, 304128, ids, fake<uint8_t>(6) + 4096, vd, 294912, ids, 10,
+                             32768, nullptr, nullptr), INV, false);  // K dst inside K src
+    CHECK(kvevict_copy_pages(ks, vs, 304128, ids, kd, kd, 294912, ids, 10, 32768, nullptr,
+                             nullptr), INV, false);  // the destinations alias
+    CHECK(kvevict_copy_pages(ks, vs, 1LL << 62, ids, kd, vd, 294912, ids, 10, 1024, nullptr,
+                             nullptr), INV, false);  // pool size overflows
+    CHECK(kvevict_copy_pages(ks, vs, 30, ids, fake<uint8_t>(6) + 30 * 32768, vd, 30, ids, 10,
+                             32768, nullptr, nullptr), OK, true);  // pools that touch
+  }
+
   // in place
   uint32_t* fc = fake<uint32_t>(11);
   int32_t* fp = fake<int32_t>(12);

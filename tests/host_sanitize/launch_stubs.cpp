@@ -72,6 +72,16 @@ hipError_t launch_select_global(int32_t*, int64_t kept_ld, int32_t*, const float
   return launched();
 }
 
+hipError_t launch_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,
+                             const int32_t* src_ids, void* k_dst, void* v_dst, int64_t dst_pages,
+                             const int32_t* dst_ids, int64_t count, int64_t page_bytes,
+                             uint32_t*, hipStream_t) {
+  need(count > 0 && src_pages >= 0 && dst_pages >= 0 && page_bytes > 0 && page_bytes % 16 == 0 &&
+           k_src && v_src && k_dst && v_dst && src_ids && dst_ids,
+       "copy_pages sizes");
+  return launched();
+}
+
 hipError_t select_global_scratch(void** ptr, size_t* bytes) {
   alignas(256) static unsigned char stand_in[256];  // a stand-in address, never dereferenced
   *ptr = &stand_in;

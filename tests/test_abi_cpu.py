@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "kvevict_evict_pages_random", "kvevict_select_random",
                           "kvevict_score_select_global",
                           "kvevict_select_global", "kvevict_select_global_noalloc",
-                          "kvevict_compact",
+                          "kvevict_compact", "kvevict_copy_pages",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
@@ -194,6 +194,31 @@ def test_compact_validation():
     assert call(src, small) == B.KVEVICT_ERR_INVALID_ARG  # 63 pages x 16 < K = 1024
     weird = B.KvDesc(7, D, H, 16, 100, 0, FAKE, 63)
     assert call(weird, dst) == B.KVEVICT_ERR_INVALID_ARG
+
+
+def test_copy_pages_validation():
+    """Page sizes, counts, pointers, alignment and pool overlaps are rejected on the host."""
+    INV, ALIGN = B.KVEVICT_ERR_INVALID_ARG, B.KVEVICT_ERR_ALIGNMENT
+    page = 32768
+    pool = 1000 * page
+
+    def call(ks=FAKE, vs=FAKE * 2, sp=1000, sid=FAKE * 5, kd=FAKE * 3, vd=FAKE * 4, dp=1000,
+             did=FAKE * 6, count=500, pb=page):
+        return status("kvevict_copy_pages", ks, vs, sp, sid, kd, vd, dp, did, count, pb, None,
+                      None)
+
+    assert call(count=0) == B.KVEVICT_OK                  # nothing to copy: nothing launched
+    assert call(count=-1) == INV
+    assert call(pb=0) == INV
+    assert call(pb=24) == ALIGN                            # pages of whole 16-byte vectors
+    assert call(sp=-1) == INV
+    assert call(ks=None) == INV and call(did=None) == INV
+    assert call(kd=FAKE * 3 + 8) == ALIGN
+    assert call(kd=FAKE + pool - 16) == INV               # K dst starts in K src's last page
+    assert call(vd=FAKE * 2 + 4096) == INV                # V dst inside V src
+    assert call(vd=FAKE * 3 + pool - 16) == INV           # V dst in K dst's last page
+    assert call(kd=FAKE * 2 - pool + 16) == INV           # K dst runs into V src
+    assert call(sp=1 << 62, pb=1 << 10) == INV            # pool size overflows
 
 
 def test_compact_rejects_overlapping_stores():

@@ -953,3 +953,42 @@ def test_evict_random_inplace_tiny_lists():
     assert np.array_equal(to_np(got), kept)
     check_inplace("contig", ks, vs, k, v, np.ascontiguousarray(kept), None, groups, H, H, pt, 16, n,
                   K, D, None, torch.zeros(1, dtype=torch.int32, device=DEV))
+
+
+# ---------------------------------------------------------------------------
+# whole-page copies (the paged gather's copy ceiling)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("page_bytes,src_pages,dst_pages,count", [
+    (32768, 300, 200, 150),    # 16-token pages of 8 heads x D = 128
+    (4096, 50, 64, 64),        # small pages: one step of the workgroup covers several
+    (81920, 7, 9, 9),          # a page of 5 workgroup steps
+    (16, 40, 40, 40),          # one vector per page
+])
+def test_copy_pages(page_bytes, src_pages, dst_pages, count):
+    say(f"copy_pages page_bytes={page_bytes} pools={src_pages}/{dst_pages} count={count}")
+    rng = np.random.default_rng(page_bytes + count)
+    ks = rng.integers(0, 1 << 16, (src_pages, page_bytes // 2), dtype=np.uint16)
+    vs = rng.integers(0, 1 << 16, (src_pages, page_bytes // 2), dtype=np.uint16)
+    src_ids = rng.integers(0, src_pages, count).astype(np.int32)
+    dst_ids = rng.permutation(dst_pages)[:count].astype(np.int32)
+    bad = count // 3
+    src_ids[bad] = src_pages          # outside the source pool: skipped and counted
+    dst_ids[bad + 1] = -1             # outside the destination pool
+    kd = np.full((dst_pages, page_bytes // 2), 0x7777, np.uint16)
+    vd = kd.copy()
+    want_k, want_v = kd.copy(), vd.copy()
+    for i in range(count):
+        if i in (bad, bad + 1):
+            continue
+        want_k[dst_ids[i]] = ks[src_ids[i]]
+        want_v[dst_ids[i]] = vs[src_ids[i]]
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).to(DEV)
+    k_dst, v_dst = dev(kd), dev(vd)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_copy_pages(dev(ks), dev(vs), torch.from_numpy(src_ids).to(DEV), k_dst, v_dst,
+                         torch.from_numpy(dst_ids).to(DEV), page_bytes, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    assert np.array_equal(k_dst.cpu().numpy().view(np.uint16), want_k)
+    assert np.array_equal(v_dst.cpu().numpy().view(np.uint16), want_v)
