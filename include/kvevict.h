@@ -364,6 +364,38 @@ kvevict_status kvevict_copy_pages(const void* k_src, const void* v_src, int64_t 
                                   int64_t page_bytes, uint32_t* errors, hipStream_t stream);
 
 /*
+ * kvevict_compact with a workspace: the same result, bit for bit, for callers
+ * that can provide device scratch.  With a paged destination whose pages the
+ * gather writes whole (16-token pages of H*D = 1024 elements, D = 128 and
+ * H = 8 among others) and a pool at most four times the pages written, the
+ * gather visits the destination pages in increasing physical order, each of
+ * the GPU's eight dies (XCDs) walking one contiguous range of the pool,
+ * instead of in page-table order: with the tables scattered over the pool, as
+ * freshly allocated pages can be (GateSight Sec. 4.3, block tables over a
+ * shared pool), this keeps the writes of the workgroups in flight close
+ * together.  The order comes from two small kernels that write each page's
+ * work item into its slot of the workspace; a page id outside the pool, or
+ * one that two items name, makes the gather fall back to table order (such a
+ * call is invalid anyway: its rows are skipped and counted as in
+ * kvevict_compact).  Other stores take kvevict_compact's path.
+ *
+ * workspace  device scratch, 256-byte aligned, apart from the four stores.
+ *            Two-phase protocol: with workspace == NULL the call writes the
+ *            size it needs (dst->capacity*4 bytes plus 256, rounded up to 256;
+ *            0 for a contiguous destination) to *workspace_bytes and returns
+ *            KVEVICT_OK; otherwise *workspace_bytes must hold at least that
+ *            size (KVEVICT_ERR_WORKSPACE).  Overwritten by each call.
+ * Other arguments, requirements and errors as kvevict_compact.
+ */
+kvevict_status kvevict_compact_ordered(const kvevict_kv_desc* src, const void* k_src,
+                                       const void* v_src, const kvevict_kv_desc* dst,
+                                       void* k_dst, void* v_dst, const int32_t* kept_idx,
+                                       int64_t kept_ld, const int32_t* kept_count, int32_t K,
+                                       int64_t num_groups, int32_t idx_lists_per_group,
+                                       uint32_t* errors, void* workspace,
+                                       size_t* workspace_bytes, hipStream_t stream);
+
+/*
  * In-place chronological compaction with a free-page list (GateSight Sec. 4.3
  * and Appendix G: each layer moves the entries it keeps to the front of its
  * own pages, and the freed tail blocks return to the pool, which releases

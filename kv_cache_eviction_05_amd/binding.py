@@ -32,7 +32,7 @@ EXPORTS = ("kvevict_score_random", "kvevict_score_weighted", "kvevict_select_top
            "kvevict_score_keydiff", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
            "kvevict_evict_pages_random", "kvevict_select_random", "kvevict_score_select_global",
            "kvevict_select_global", "kvevict_select_global_noalloc", "kvevict_compact",
-           "kvevict_copy_pages",
+           "kvevict_copy_pages", "kvevict_compact_ordered",
            "kvevict_status_string", "kvevict_abi_version")
 
 # size of the static workspace array behind kvevict_select_global_noalloc (kvevict.h)
@@ -98,6 +98,9 @@ def load():
     lib.kvevict_evict_random_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _i64, _i32, _i32,
                                                  _i32, _i32, _u64, _u32, _i32, _p, _i64, _p, _p,
                                                  _p, _p]
+    lib.kvevict_compact_ordered.argtypes = [ctypes.POINTER(KvDesc), _p, _p, ctypes.POINTER(KvDesc),
+                                            _p, _p, _p, _i64, _p, _i32, _i64, _i32, _p, _p,
+                                            ctypes.POINTER(_sz), _p]
     lib.kvevict_copy_pages.argtypes = [_p, _p, _i64, _p, _p, _p, _i64, _p, _i64, _i64, _p, _p]
     lib.kvevict_compact_inplace.argtypes = [ctypes.POINTER(KvDesc), _p, _p, _p, _i64, _p, _i32,
                                             _i32, _i64, _i32, _p, _p, _p, _p]
@@ -107,7 +110,7 @@ def load():
                  "kvevict_compact", "kvevict_compact_inplace", "kvevict_evict_random_inplace",
                  "kvevict_evict_pages_random", "kvevict_select_random",
                  "kvevict_score_select_global", "kvevict_select_global_noalloc",
-                 "kvevict_copy_pages"):
+                 "kvevict_copy_pages", "kvevict_compact_ordered"):
         getattr(lib, name).restype = _i32
     lib.kvevict_status_string.argtypes = [_i32]
     lib.kvevict_status_string.restype = ctypes.c_char_p
@@ -326,8 +329,8 @@ def kvevict_select_global_noalloc(kept_idx, kept_ld, kept_count, scores, ld, num
     return budget.value
 
 
-def kvevict_compact(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_idx, kept_ld,
-                    kept_count, K, num_groups, idx_lists_per_group, errors=None, stream=None):
+def _compact_guards(src, k_src, v_src, dst, k_dst, v_dst, kept_idx, kept_ld, kept_count, K,
+                    num_groups, idx_lists_per_group, errors):
     _need(k_src, torch.bfloat16, _store_elems(src, num_groups), "k_src")
     _need(v_src, torch.bfloat16, _store_elems(src, num_groups), "v_src")
     _need(k_dst, torch.bfloat16, _store_elems(dst, num_groups), "k_dst")
@@ -344,11 +347,41 @@ def kvevict_compact(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_i
         _need(src._pt, torch.int32, num_groups * src.pt_ld, "src page table")
     if dst.layout == LAYOUT_PAGED and num_groups > 0:
         _need(dst._pt, torch.int32, num_groups * dst.pt_ld, "dst page table")
+
+
+def kvevict_compact(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_idx, kept_ld,
+                    kept_count, K, num_groups, idx_lists_per_group, errors=None, stream=None):
+    _compact_guards(src, k_src, v_src, dst, k_dst, v_dst, kept_idx, kept_ld, kept_count, K,
+                    num_groups, idx_lists_per_group, errors)
     _check(load().kvevict_compact(ctypes.byref(src), _ptr(k_src), _ptr(v_src), ctypes.byref(dst),
                                   _ptr(k_dst), _ptr(v_dst), _ptr(kept_idx), kept_ld,
                                   _ptr(kept_count), K, num_groups, idx_lists_per_group,
                                   _ptr(errors), _stream(stream)),
            "kvevict_compact")
+
+
+def kvevict_compact_ordered_workspace(dst: KvDesc) -> int:
+    """Workspace bytes of kvevict_compact_ordered for this destination (0 if contiguous)."""
+    size = _sz(0)
+    _check(load().kvevict_compact_ordered(None, None, None, ctypes.byref(dst), None, None, None, 0,
+                                          None, 0, 0, 1, None, None, ctypes.byref(size), None),
+           "kvevict_compact_ordered (workspace query)")
+    return size.value
+
+
+def kvevict_compact_ordered(src: KvDesc, k_src, v_src, dst: KvDesc, k_dst, v_dst, kept_idx,
+                            kept_ld, kept_count, K, num_groups, idx_lists_per_group, workspace,
+                            workspace_bytes, errors=None, stream=None):
+    _compact_guards(src, k_src, v_src, dst, k_dst, v_dst, kept_idx, kept_ld, kept_count, K,
+                    num_groups, idx_lists_per_group, errors)
+    _need(workspace, None, workspace_bytes // max(workspace.element_size(), 1), "workspace")
+    size = _sz(workspace_bytes)
+    _check(load().kvevict_compact_ordered(ctypes.byref(src), _ptr(k_src), _ptr(v_src),
+                                          ctypes.byref(dst), _ptr(k_dst), _ptr(v_dst),
+                                          _ptr(kept_idx), kept_ld, _ptr(kept_count), K,
+                                          num_groups, idx_lists_per_group, _ptr(errors),
+                                          _ptr(workspace), ctypes.byref(size), _stream(stream)),
+           "kvevict_compact_ordered")
 
 
 def kvevict_abi_version() -> int:

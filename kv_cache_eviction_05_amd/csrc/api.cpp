@@ -388,30 +388,30 @@ kvevict_status kvevict_score_select_global(
                                                   true));
 }
 
-kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,
-                               const kvevict_kv_desc* dst, void* k_dst, void* v_dst,
-                               const int32_t* kept_idx, int64_t kept_ld,
-                               const int32_t* kept_count, int32_t K, int64_t num_groups,
-                               int32_t idx_lists_per_group, uint32_t* errors,
-                               hipStream_t stream) {
+// Arguments of an out-of-place compaction: the two stores' views, K within
+// the destination, and no destination byte inside a source or the other
+// destination (the sources are only read and may overlap).
+static kvevict_status check_compact(const kvevict_kv_desc* src, const void* k_src,
+                                    const void* v_src, const kvevict_kv_desc* dst,
+                                    const void* k_dst, const void* v_dst,
+                                    const int32_t* kept_idx, int64_t kept_ld, int32_t K,
+                                    int64_t num_groups, int32_t idx_lists_per_group,
+                                    kvevict::StoreView* sv, kvevict::StoreView* dv) {
   if (!src || !dst) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups < 0 || K < 0 || kept_ld < K) return KVEVICT_ERR_INVALID_ARG;
   if (src->head_dim != dst->head_dim || src->heads != dst->heads) return KVEVICT_ERR_INVALID_ARG;
   const int32_t H = src->heads;
   if (idx_lists_per_group != 1 && idx_lists_per_group != H) return KVEVICT_ERR_INVALID_ARG;
-  kvevict::StoreView sv, dv;
-  kvevict_status st = check_store(src, k_src, v_src, num_groups, &sv);
+  kvevict_status st = check_store(src, k_src, v_src, num_groups, sv);
   if (st != KVEVICT_OK) return st;
-  st = check_store(dst, k_dst, v_dst, num_groups, &dv);
+  st = check_store(dst, k_dst, v_dst, num_groups, dv);
   if (st != KVEVICT_OK) return st;
-  if (K > dv.max_rows) return KVEVICT_ERR_INVALID_ARG;
+  if (K > dv->max_rows) return KVEVICT_ERR_INVALID_ARG;
   if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
   if (num_groups > 0 && K > 0 && !kept_idx) return KVEVICT_ERR_INVALID_ARG;
   const int32_t D = src->head_dim;
   if ((int64_t)H * D > (1 << 26)) return KVEVICT_ERR_INVALID_ARG;  // one token row of all heads
   if (num_groups > 0 && K > 0) {
-    // out of place: no destination byte may lie in a source store or in the
-    // other destination store (the sources are only read and may overlap)
     const int64_t lists = num_groups * H;
     const u128 se = store_extent_bytes(src, lists), de = store_extent_bytes(dst, lists);
     if (ranges_overlap(k_dst, de, k_src, se) || ranges_overlap(k_dst, de, v_src, se) ||
@@ -419,9 +419,66 @@ kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, co
         ranges_overlap(k_dst, de, v_dst, de))
       return KVEVICT_ERR_INVALID_ARG;
   }
-  return hip_status(kvevict::launch_compact(sv, k_src, v_src, dv, k_dst, v_dst, D, H, kept_idx,
-                                            kept_ld, kept_count, K, num_groups,
-                                            idx_lists_per_group, errors, stream));
+  return KVEVICT_OK;
+}
+
+kvevict_status kvevict_compact(const kvevict_kv_desc* src, const void* k_src, const void* v_src,
+                               const kvevict_kv_desc* dst, void* k_dst, void* v_dst,
+                               const int32_t* kept_idx, int64_t kept_ld,
+                               const int32_t* kept_count, int32_t K, int64_t num_groups,
+                               int32_t idx_lists_per_group, uint32_t* errors,
+                               hipStream_t stream) {
+  kvevict::StoreView sv, dv;
+  const kvevict_status st = check_compact(src, k_src, v_src, dst, k_dst, v_dst, kept_idx, kept_ld,
+                                          K, num_groups, idx_lists_per_group, &sv, &dv);
+  if (st != KVEVICT_OK) return st;
+  return hip_status(kvevict::launch_compact(sv, k_src, v_src, dv, k_dst, v_dst, src->head_dim,
+                                            src->heads, kept_idx, kept_ld, kept_count, K,
+                                            num_groups, idx_lists_per_group, errors, stream));
+}
+
+kvevict_status kvevict_compact_ordered(const kvevict_kv_desc* src, const void* k_src,
+                                       const void* v_src, const kvevict_kv_desc* dst,
+                                       void* k_dst, void* v_dst, const int32_t* kept_idx,
+                                       int64_t kept_ld, const int32_t* kept_count, int32_t K,
+                                       int64_t num_groups, int32_t idx_lists_per_group,
+                                       uint32_t* errors, void* workspace,
+                                       size_t* workspace_bytes, hipStream_t stream) {
+  if (!workspace_bytes) return KVEVICT_ERR_INVALID_ARG;
+  if (!dst) return KVEVICT_ERR_INVALID_ARG;
+  if (!workspace) {  // size query: the destination pool's pages as int32 slots, and a flag
+    if (dst->layout == KVEVICT_LAYOUT_PAGED) {
+      if (dst->capacity < 0 || dst->capacity > (INT64_MAX - 512) / 4) return KVEVICT_ERR_INVALID_ARG;
+      kvevict::StoreView dv{};
+      dv.capacity = dst->capacity;
+      *workspace_bytes = kvevict::compact_order_workspace_bytes(dv);
+    } else {
+      *workspace_bytes = 0;
+    }
+    return KVEVICT_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return KVEVICT_ERR_ALIGNMENT;
+  if (dst->layout == KVEVICT_LAYOUT_PAGED) {
+    kvevict::StoreView dv{};
+    dv.capacity = dst->capacity < 0 ? 0 : dst->capacity;
+    if (*workspace_bytes < kvevict::compact_order_workspace_bytes(dv)) return KVEVICT_ERR_WORKSPACE;
+  }
+  kvevict::StoreView sv, dv;
+  const kvevict_status st = check_compact(src, k_src, v_src, dst, k_dst, v_dst, kept_idx, kept_ld,
+                                          K, num_groups, idx_lists_per_group, &sv, &dv);
+  if (st != KVEVICT_OK) return st;
+  if (dv.paged && num_groups > 0 && K > 0) {  // the workspace is written: apart from the stores
+    const int64_t lists = num_groups * src->heads;
+    const u128 wext = (u128)kvevict::compact_order_workspace_bytes(dv);
+    const u128 se = store_extent_bytes(src, lists), de = store_extent_bytes(dst, lists);
+    if (ranges_overlap(workspace, wext, k_src, se) || ranges_overlap(workspace, wext, v_src, se) ||
+        ranges_overlap(workspace, wext, k_dst, de) || ranges_overlap(workspace, wext, v_dst, de))
+      return KVEVICT_ERR_INVALID_ARG;
+  }
+  return hip_status(kvevict::launch_compact(sv, k_src, v_src, dv, k_dst, v_dst, src->head_dim,
+                                            src->heads, kept_idx, kept_ld, kept_count, K,
+                                            num_groups, idx_lists_per_group, errors, stream,
+                                            dv.paged ? workspace : nullptr));
 }
 
 kvevict_status kvevict_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,

@@ -33,6 +33,8 @@
 //
 // Every indirect index (kept index, page id) is checked against its store
 // before it is used; a row that fails is skipped and counted in *errors.
+#include <algorithm>
+
 #include "kvevict_device.hpp"
 #include "kvevict_launch.hpp"
 
@@ -43,7 +45,9 @@ constexpr int kListThreads = 256;
 constexpr int kListVecs = 1024;   // 16-byte vectors of K (or of V) per list item: 16 KiB
 constexpr int kGroupThreads = 256;
 constexpr int kGroupVecs = 2048;  // vectors of K and of V per group item: 32 KiB each
-constexpr int64_t kMaxGrid = 1 << 23;  // workgroups per launch: 256-thread groups stay below 2^31 work-items
+constexpr int kXcds = 8;  // accelerator dies of an MI355X, each with its own L2
+constexpr int64_t kMaxGrid = 1 << 23;  // workgroups per launch (a multiple of kXcds): 256-thread groups stay below 2^31 work-items
+static_assert(kMaxGrid % kXcds == 0, "the ordered walk keeps each workgroup on one XCD");
 static_assert(kMaxGrid * kListThreads < (1LL << 32) && kMaxGrid * kGroupThreads < (1LL << 32),
               "a launch stays below 2^32 work-items");
 // Chunks a workgroup pair walks at most with per-list counts (same-process A/B on
@@ -68,6 +72,12 @@ struct CompactArgs {
   int64_t items;          // group items, or list workgroup pairs
   int32_t vpr;                    // 16-byte vectors per row
   uint32_t* errors;
+  // group kernel, destination-ordered walk: slot s of the pool holds the item
+  // whose destination page is s (or -1); *order_bad is set when some item's
+  // page is outside the pool or shared, and the walk is then in item order
+  const int32_t* order;
+  const uint32_t* order_bad;
+  int64_t order_len;
 };
 
 // Vector offset of row t of (group g, head h) in a store, or -1 if t or its
@@ -161,7 +171,21 @@ __global__ __launch_bounds__(kGroupThreads) void compact_group_kernel(CompactArg
   const vec4u* __restrict__ vs = a.v_src;
   vec4u* __restrict__ kd = a.k_dst;
   vec4u* __restrict__ vd = a.v_dst;
-  for (int64_t item = blockIdx.x; item < a.items; item += gridDim.x) {
+  const bool ordered = a.order && *a.order_bad == 0u;
+  // ordered: slots [0, kXcds * per_xcd) map one to one onto the pool's pages
+  // (and past its end, where they idle); workgroup b runs on XCD b % 8
+  // (round-robin dispatch, and the grid is a multiple of 8), so XCD x walks
+  // the x-th eighth of the pool's pages in increasing order
+  const int64_t per_xcd = (a.order_len + kXcds - 1) / kXcds;
+  const int64_t slots = ordered ? per_xcd * kXcds : a.items;
+  for (int64_t slot = blockIdx.x; slot < slots; slot += gridDim.x) {
+    int64_t item = slot;
+    if (ordered) {
+      const int64_t s2 = (slot % kXcds) * per_xcd + slot / kXcds;
+      if (s2 >= a.order_len) continue;
+      item = a.order[s2];
+      if (item < 0 || item >= a.items) continue;
+    }
     const int64_t g = item / a.chunks;
     const int32_t chunk = (int32_t)(item - g * a.chunks);
     const int32_t r0 = chunk * a.rows_per_item;
@@ -213,6 +237,31 @@ __global__ __launch_bounds__(kGroupThreads) void compact_group_kernel(CompactArg
   }
 }
 
+// Destination-ordered walk of the group kernel: the pool's slots are cleared,
+// then every item writes its index into the slot of its destination page (one
+// whole page per item).  A page outside the pool, or one that two items name,
+// sets *bad, and the gather then walks the items in their own order.
+__global__ __launch_bounds__(256) void order_clear_kernel(int32_t* order, int64_t len,
+                                                          uint32_t* bad) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < len; i += (int64_t)gridDim.x * 256)
+    order[i] = -1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *bad = 0u;
+}
+
+__global__ __launch_bounds__(256) void order_scatter_kernel(const int32_t* page_table, int64_t pt_ld,
+                                                            int32_t page_shift, int32_t rows_per_item,
+                                                            int32_t chunks, int64_t items,
+                                                            int32_t* order, int64_t len,
+                                                            uint32_t* bad) {
+  const int64_t item = blockIdx.x * 256ll + threadIdx.x;
+  if (item >= items) return;
+  const int64_t g = item / chunks;
+  const int32_t chunk = (int32_t)(item - g * chunks);
+  const int32_t page = page_table[g * pt_ld + (((int64_t)chunk * rows_per_item) >> page_shift)];
+  if (page < 0 || (int64_t)page >= len || atomicCAS(order + page, -1, (int32_t)item) != -1)
+    atomicOr(bad, 1u);
+}
+
 struct Plan {
   bool group;
   int32_t rows_per_item, chunks, team;
@@ -247,11 +296,23 @@ Plan plan_compact(const StoreView& src, const StoreView& dst, int32_t D, int32_t
 
 }  // namespace
 
+bool compact_orders_pages(const StoreView& src, const StoreView& dst, int32_t D, int32_t H,
+                          int32_t K, int64_t num_groups) {
+  if (!dst.paged || num_groups == 0 || K == 0) return false;
+  const Plan p = plan_compact(src, dst, D, H, K, num_groups, false);
+  // one destination page per item, and a pool not much larger than the pages written
+  return p.group && p.rows_per_item == (1 << dst.page_shift) && dst.capacity <= 4 * p.items;
+}
+
+size_t compact_order_workspace_bytes(const StoreView& dst) {
+  return (size_t)(dst.capacity * 4 + 256 + 255) / 256 * 256;
+}
+
 hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v_src,
                           const StoreView& dst, void* k_dst, void* v_dst, int32_t D, int32_t H,
                           const int32_t* kept_idx, int64_t kept_ld, const int32_t* kept_count,
                           int32_t K, int64_t num_groups, int32_t ipg, uint32_t* errors,
-                          hipStream_t stream) {
+                          hipStream_t stream, void* order_ws) {
   if (num_groups == 0 || K == 0) return hipSuccess;
   const Plan p = plan_compact(src, dst, D, H, K, num_groups, kept_count != nullptr);
   CompactArgs a;
@@ -273,8 +334,35 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
   a.items = p.items;
   a.vpr = D / 8;
   a.errors = errors;
+  a.order = nullptr;
+  a.order_bad = nullptr;
+  a.order_len = 0;
   if (p.group) {
-    hipLaunchKernelGGL(compact_group_kernel, dim3((unsigned)p.grid), dim3(kGroupThreads), 0,
+    int64_t grid = p.grid;
+    if (order_ws && compact_orders_pages(src, dst, D, H, K, num_groups)) {
+      int32_t* order = static_cast<int32_t*>(order_ws);
+      const int64_t len = dst.capacity;
+      uint32_t* bad = reinterpret_cast<uint32_t*>(static_cast<char*>(order_ws) +
+                                                  (len * 4 + 255) / 256 * 256);
+      const int64_t clear_grid = std::min<int64_t>((len + 255) / 256, 1 << 16);
+      hipLaunchKernelGGL(order_clear_kernel, dim3((unsigned)std::max<int64_t>(clear_grid, 1)),
+                         dim3(256), 0, stream, order, len, bad);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(order_scatter_kernel, dim3((unsigned)((p.items + 255) / 256)), dim3(256),
+                         0, stream, dst.page_table, dst.pt_ld, dst.page_shift, p.rows_per_item,
+                         p.chunks, p.items, order, len, bad);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      a.order = order;
+      a.order_bad = bad;
+      a.order_len = len;
+      // enough workgroups for the larger of the walks (the pool's pages rounded up to a
+      // multiple of the XCDs, or the items); kMaxGrid is a multiple of 8 as well
+      const int64_t span = (len + kXcds - 1) / kXcds * kXcds;
+      const int64_t slots = std::max<int64_t>(span, p.items);
+      grid = slots < kMaxGrid ? slots : kMaxGrid;
+    }
+    hipLaunchKernelGGL(compact_group_kernel, dim3((unsigned)grid), dim3(kGroupThreads), 0,
                        stream, a);
     return hipGetLastError();
   }

@@ -85,7 +85,14 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
                           const StoreView& dst, void* k_dst, void* v_dst, int32_t D, int32_t H,
                           const int32_t* kept_idx, int64_t kept_ld, const int32_t* kept_count,
                           int32_t K, int64_t num_groups, int32_t ipg, uint32_t* errors,
-                          hipStream_t stream);
+                          hipStream_t stream, void* order_ws = nullptr);
+
+// The paged destination-ordered gather: whether it applies (a paged
+// destination, one destination page per work item of the group kernel), and
+// the workspace it takes (the pool's pages as int32 slots, and a flag).
+bool compact_orders_pages(const StoreView& src, const StoreView& dst, int32_t D, int32_t H,
+                          int32_t K, int64_t num_groups);
+size_t compact_order_workspace_bytes(const StoreView& dst);
 
 // KeyDiff scores of num_lists lists of n keys (D a power of two in [8, 512]).
 hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys, const void* k,

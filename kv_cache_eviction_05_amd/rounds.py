@@ -62,6 +62,8 @@ class RoundState:
     freed: torch.Tensor | None = None        # in place, paged: the free-page list
     freed_count: torch.Tensor | None = None
     pt_pristine: torch.Tensor | None = None  # page draw, one round: the table before the round
+    order_ws: torch.Tensor | None = None     # paged destination: the ordered gather's workspace
+    order_ws_bytes: int = 0
 
     @property
     def idx_lists(self) -> int:
@@ -179,6 +181,11 @@ def make_state(cfg: RoundConfig, device="cuda", kv_seed: int = synth.SEED_KV) ->
             st.freed_count = torch.zeros(1, dtype=torch.int32, device=device)
         if cfg.page_draw:
             st.pt_pristine = spt.clone()
+    if cfg.layout == "paged" and not cfg.inplace:
+        # the gather visits the fresh destination pages in physical order
+        st.order_ws_bytes = max(B.kvevict_compact_ordered_workspace(st.dst_desc),
+                                B.kvevict_compact_ordered_workspace(st.src_desc))  # after a swap
+        st.order_ws = torch.empty(max(st.order_ws_bytes, 256), dtype=torch.uint8, device=device)
     if cfg.select == "layers":
         st.kept_count = torch.zeros(lists, dtype=torch.int32, device=device)
         st.layer_budget = B.kvevict_layer_power_budget(synth.layer_gates(cfg.L, synth.SEED_GATES),
@@ -258,6 +265,11 @@ def compact(st: RoundState, stream=None):
         B.kvevict_compact_inplace(st.src_desc, st.k_src, st.v_src, st.kept, st.kept.shape[1], count,
                                   K, st.n, c.groups, ipg, st.freed, st.freed_count, st.errors,
                                   stream)
+        return
+    if st.order_ws is not None:
+        B.kvevict_compact_ordered(st.src_desc, st.k_src, st.v_src, st.dst_desc, st.k_dst,
+                                  st.v_dst, st.kept, st.kept.shape[1], count, K, c.groups, ipg,
+                                  st.order_ws, st.order_ws_bytes, st.errors, stream)
         return
     B.kvevict_compact(st.src_desc, st.k_src, st.v_src, st.dst_desc, st.k_dst, st.v_dst, st.kept,
                       st.kept.shape[1], count, K, c.groups, ipg, st.errors, stream)

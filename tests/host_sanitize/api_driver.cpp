@@ -234,6 +234,28 @@ int main() {
   CHECK(kvevict_score_keydiff(sc, 1088, &keys96, ks, 16, 1088, 128, nullptr), UNSUP, false);
   CHECK(kvevict_score_keydiff(sc, 1088, &keys, ks, huge, 1088, 128, nullptr), INV, false);
 
+  // ordered compaction into a paged destination: workspace protocol and checks
+  {
+    kvevict_kv_desc ps2 = paged(128, 8, 16, 304128, pt, 132), pd2 = paged(128, 8, 16, 294912, pt, 128);
+    size_t ob = 0;
+    CHECK(kvevict_compact_ordered(&ps2, ks, vs, &pd2, kd, vd, idx, 2048, nullptr, 2048, 2304, 8,
+                                  nullptr, nullptr, &ob, nullptr), OK, false);  // size query
+    if (ob != (294912 * 4 + 256 + 255) / 256 * 256) {
+      std::fprintf(stderr, "ordered workspace %zu\n", ob);
+      ++failures;
+    }
+    void* ows = fake<void>(14);
+    CHECK(kvevict_compact_ordered(&ps2, ks, vs, &pd2, kd, vd, idx, 2048, nullptr, 2048, 2304, 8,
+                                  nullptr, ows, &ob, nullptr), OK, true);
+    size_t small = ob - 1;
+    CHECK(kvevict_compact_ordered(&ps2, ks, vs, &pd2, kd, vd, idx, 2048, nullptr, 2048, 2304, 8,
+                                  nullptr, ows, &small, nullptr), WS, false);
+    CHECK(kvevict_compact_ordered(&ps2, ks, vs, &pd2, kd, vd, idx, 2048, nullptr, 2048, 2304, 8,
+                                  nullptr, fake<uint8_t>(8) + 4096, &ob, nullptr), INV, false);
+    CHECK(kvevict_compact_ordered(&ps2, ks, vs, &pd2, kd, vd, idx, 2048, nullptr, 2048, 2304, 8,
+                                  nullptr, fake<uint8_t>(14) + 64, &ob, nullptr), ALIGN, false);
+  }
+
   // whole-page copies
   {
     const int32_t* ids = fake<const int32_t>(13);

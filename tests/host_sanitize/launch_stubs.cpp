@@ -72,6 +72,16 @@ hipError_t launch_select_global(int32_t*, int64_t kept_ld, int32_t*, const float
   return launched();
 }
 
+bool compact_orders_pages(const StoreView&, const StoreView& dst, int32_t, int32_t, int32_t K,
+                          int64_t num_groups) {
+  return dst.paged && K > 0 && num_groups > 0;
+}
+
+size_t compact_order_workspace_bytes(const StoreView& dst) {
+  need(dst.capacity >= 0, "order workspace sizes");
+  return (size_t)(dst.capacity * 4 + 256 + 255) / 256 * 256;
+}
+
 hipError_t launch_copy_pages(const void* k_src, const void* v_src, int64_t src_pages,
                              const int32_t* src_ids, void* k_dst, void* v_dst, int64_t dst_pages,
                              const int32_t* dst_ids, int64_t count, int64_t page_bytes,
@@ -102,7 +112,7 @@ uint32_t* select_global_first_level_bins(int64_t, int32_t, int32_t, int64_t, voi
 hipError_t launch_compact(const StoreView& src, const void*, const void*, const StoreView& dst,
                           void*, void*, int32_t D, int32_t H, const int32_t*, int64_t kept_ld,
                           const int32_t*, int32_t K, int64_t num_groups, int32_t ipg, uint32_t*,
-                          hipStream_t) {
+                          hipStream_t, void*) {
   need(D > 0 && D % 8 == 0 && H >= 1 && (ipg == 1 || ipg == H) && K >= 0 && kept_ld >= K &&
            num_groups >= 0 && num_groups * (int64_t)H <= 2147483647 && K <= dst.max_rows &&
            src.max_rows >= 0,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "kvevict_evict_pages_random", "kvevict_select_random",
                           "kvevict_score_select_global",
                           "kvevict_select_global", "kvevict_select_global_noalloc",
-                          "kvevict_compact", "kvevict_copy_pages",
+                          "kvevict_compact", "kvevict_copy_pages", "kvevict_compact_ordered",
                           "kvevict_status_string", "kvevict_abi_version"}
     lib = ctypes.CDLL(B.LIB_PATH)
     for name in names:
@@ -219,6 +219,34 @@ def test_copy_pages_validation():
     assert call(vd=FAKE * 3 + pool - 16) == INV           # V dst in K dst's last page
     assert call(kd=FAKE * 2 - pool + 16) == INV           # K dst runs into V src
     assert call(sp=1 << 62, pb=1 << 10) == INV            # pool size overflows
+
+
+def test_compact_ordered_validation():
+    """The ordered compaction's workspace protocol and checks, on the host (no launch)."""
+    D, H, groups = 128, 8, 4
+    src = B.contig_desc(D, H, 1088)
+    pool = B.KvDesc(B.LAYOUT_PAGED, D, H, 16, 1000, 0, FAKE * 9, 64)
+    assert B.kvevict_compact_ordered_workspace(pool) == (1000 * 4 + 256 + 255) // 256 * 256
+    assert B.kvevict_compact_ordered_workspace(B.contig_desc(D, H, 1024)) == 0
+    need = B.kvevict_compact_ordered_workspace(pool)
+    INV = B.KVEVICT_ERR_INVALID_ARG
+
+    def call(d=pool, ws=FAKE * 7, size=need, K=1024, kd=FAKE * 3, vd=FAKE * 4, nosize=False):
+        sz = ctypes.c_size_t(size)
+        return status("kvevict_compact_ordered", ctypes.byref(src), FAKE, FAKE * 2,
+                      ctypes.byref(d), kd, vd, FAKE, 1024, None, K, groups, H, None, ws,
+                      None if nosize else ctypes.byref(sz), None)
+
+    assert call(nosize=True) == INV                                  # no size
+    assert call(size=need - 1) == B.KVEVICT_ERR_WORKSPACE
+    assert call(ws=FAKE * 7 + 16) == B.KVEVICT_ERR_ALIGNMENT          # 256-byte aligned
+    assert call(ws=FAKE * 3 + 4096) == INV                           # inside the K destination
+    assert call(ws=FAKE + 1024 * 256) == INV                         # inside the K source
+    assert call(K=1025) == INV                                       # K beyond 64 pages x 16
+    assert call(vd=FAKE * 3) == INV                                  # the destinations alias
+    neg = B.KvDesc(B.LAYOUT_PAGED, D, H, 16, -1, 0, FAKE * 9, 64)
+    assert status("kvevict_compact_ordered", None, None, None, ctypes.byref(neg), None, None, None,
+                  0, None, 0, 0, 1, None, None, ctypes.byref(ctypes.c_size_t(0)), None) == INV
 
 
 def test_compact_rejects_overlapping_stores():

@@ -992,3 +992,77 @@ def test_copy_pages(page_bytes, src_pages, dst_pages, count):
     assert int(err.item()) == 2
     assert np.array_equal(k_dst.cpu().numpy().view(np.uint16), want_k)
     assert np.array_equal(v_dst.cpu().numpy().view(np.uint16), want_v)
+
+
+# ---------------------------------------------------------------------------
+# compaction visiting the destination pages in physical order
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["per_head", "shared", "counts", "bad_page", "big_pool",
+                                  "contig_dst", "d64"])
+def test_compact_ordered(case):
+    """kvevict_compact_ordered equals kvevict_compact bit for bit (rows, untouched rows, error
+    count): the destination-ordered walk (16-token pages of 8 heads x D = 128), its fallbacks
+    (a page id outside the pool: table order; a pool over four times the pages written, two
+    pages per work item at D = 64, a contiguous destination: kvevict_compact's path), two calls
+    in a row on one workspace, and the oracle's rows."""
+    say(f"compact_ordered {case}")
+    groups, H, D, ps, n, K, prot = 7, 8, 128, 16, 2112 - 37, 2048 - 40, 1000
+    if case == "d64":
+        D = 64
+    rng = np.random.default_rng(len(case) * 101 + ord(case[0]))
+    src_pages, dst_pages = -(-n // ps), -(-K // ps)
+    pool_src = groups * src_pages + 7
+    pool_dst = groups * dst_pages * (5 if case == "big_pool" else 1) + 3
+    pt_src = rng.permutation(pool_src)[:groups * src_pages].reshape(groups, src_pages).astype(np.int32)
+    pt_dst = rng.permutation(pool_dst)[:groups * dst_pages].reshape(groups, dst_pages).astype(np.int32)
+    if case == "bad_page":
+        pt_dst[3, 5] = pool_dst + 2  # outside the pool: its rows are skipped and counted
+    shared = case == "shared"
+    idx_lists = groups if shared else groups * H
+    kept = oracle.select_topk(rng.random((idx_lists, n), dtype=np.float32), K, prot)
+    counts = None
+    if case == "counts":
+        counts = rng.integers(prot, K + 1, idx_lists).astype(np.int32)
+    ks = rand_bits((pool_src, ps, H, D), 40)
+    vs = rand_bits(ks.shape, 41)
+    sdesc = B.paged_desc(D, H, ps, pool_src, torch.from_numpy(pt_src).to(DEV))
+    if case == "contig_dst":
+        kd0 = rand_bits((groups * H, K, D), 42)
+        ddesc, do = B.contig_desc(D, H, K), {"list_stride": K * D}
+    else:
+        kd0 = rand_bits((pool_dst, ps, H, D), 42)
+        ddesc = B.paged_desc(D, H, ps, pool_dst, torch.from_numpy(pt_dst).to(DEV))
+        do = {"paged": True, "page_table": pt_dst}
+    vd0 = rand_bits(kd0.shape, 43)
+    ipg = 1 if shared else H
+    kept_t = torch.from_numpy(kept).to(DEV)
+    count_t = torch.from_numpy(counts).to(DEV) if counts is not None else None
+    wsb = B.kvevict_compact_ordered_workspace(ddesc)
+    if case == "contig_dst":
+        assert wsb == 0
+    else:
+        assert wsb == (pool_dst * 4 + 256 + 255) // 256 * 256
+    ws = torch.full((max(wsb, 256),), 0x7E, dtype=torch.uint8, device=DEV)
+    outs = []
+    for variant in ("plain", "ordered", "ordered again"):
+        k_dst, v_dst = bf16_from_bits(kd0), bf16_from_bits(vd0)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        args = (sdesc, bf16_from_bits(ks), bf16_from_bits(vs), ddesc, k_dst, v_dst, kept_t, K,
+                count_t, K, groups, ipg)
+        if variant == "plain":
+            B.kvevict_compact(*args, err)
+        else:
+            B.kvevict_compact_ordered(*args, ws, wsb, err)
+        torch.cuda.synchronize()
+        outs.append((u16(k_dst), u16(v_dst), int(err.item())))
+    for k, v, e in outs[1:]:
+        assert np.array_equal(k, outs[0][0]) and np.array_equal(v, outs[0][1]) and e == outs[0][2]
+    if case == "bad_page":  # skipped rows are counted (and the rest equals the plain call)
+        assert outs[0][2] > 0
+        return
+    assert outs[0][2] == 0
+    kd, vd = kd0.copy(), vd0.copy()
+    oracle.compact({"paged": True, "page_table": pt_src}, ks, vs, do, kd, vd, kept, K, D, H, 0,
+                   groups, ipg=ipg, kept_count=counts, page_size=ps)
+    assert np.array_equal(outs[1][0], kd) and np.array_equal(outs[1][1], vd)
