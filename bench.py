@@ -601,6 +601,16 @@ def measure(torch, binding, configs, rounds, name, args, headline):
                                    "achieved": sg, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                    "frac": sg / PEAK_HBM_GBPS, "algorithmic_bytes": sb,
                                    "ms": round(r["kernels_ms"]["score"], 4)}
+    if cfg.scorer == "keydiff" and "score" in r["kernels_ms"]:
+        # the KeyDiff scorer: every key read once, scores written once (the rows it reads
+        # a second time are not algorithmic bytes; the round's score bytes count the
+        # select's read as well)
+        sb = r["algorithmic_bytes"]["inputs"] + r["algorithmic_bytes"]["scores"] // 2
+        sg = sb / (r["kernels_ms"]["score"] * 1e-3) / 1e9
+        entry["roofline_score"] = {"bound": "hbm", "kernel": "score_keydiff_kernel",
+                                   "achieved": sg, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                   "frac": sg / PEAK_HBM_GBPS, "algorithmic_bytes": sb,
+                                   "ms": round(r["kernels_ms"]["score"], 4)}
     st = r["state"]
     if r["ms_per_step"] < 1.0 and not (cfg.inplace or cfg.page_draw or cfg.rounds > 1):
         # latency-bound rounds: also replayed from a HIP graph

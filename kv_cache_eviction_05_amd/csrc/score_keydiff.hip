@@ -6,25 +6,27 @@
 //   score[list][i] = -cos(k_i, mean_j k_j)   (mean over all n keys of the list),
 //   +inf for i < prot; a zero norm gives cos = 0; zero is written as +0.
 //
-// The mean needs every key before any cosine, and a list (1088 keys of 256 B
-// at D = 128: 278 KB) is larger than a CU's share of L2 and of the Infinity
-// Cache, so a second pass over the keys goes back to HBM.  One workgroup of
-// 512 threads per list keeps the list's first rows on chip between the two
-// passes: a row of D bf16 is VPR = D/8 16-byte vectors, thread t owns vector
-// column t % VPR of rows t / VPR + k * (512 / VPR); its first 10 such rows
-// stay in registers and the next 7 or 8 in LDS (64 KB), which at D = 128 holds
-// 576 of 1088 rows; the rest are read twice.  Two such workgroups fit a CU, so
-// one list's loads overlap the other's binary64 work: measured against one
-// 1024-thread workgroup per CU holding 1024 rows (1.04x traffic, no overlap),
-// 14% faster at ~1.5x traffic.  Ten register rows (118 VGPRs) beat eight by 2%;
-// a ninth LDS row, or twelve register rows (132 VGPRs, 3 waves per SIMD), do not.
+// The mean needs every key before any cosine.  One workgroup of 512 threads
+// per list, two per CU: a row of D bf16 is VPR = D/8 16-byte vectors, thread t
+// owns vector column t % VPR of rows t / VPR + k * (512 / VPR); its first 10
+// such rows stay in registers and the next 9 (D <= 128), 8 or 7 in LDS, which
+// at D = 128 holds 608 of 1088 rows between the two passes.  The other rows
+// are read a second time soon after the first, and those reads mostly hit the
+// Infinity Cache: measured on the 36,864-list batch, a plain read of every row
+// once and of the streamed rows again takes 1.22x the time of one read;
+// twelve register rows gained nothing, and one 1024-thread workgroup per CU
+// holding 1024 rows (1.04x the bytes) was 14% slower, since two workgroups per
+// CU let one list's reads overlap the other's arithmetic.
 // Pass 1 accumulates the column sums in binary64 in a fixed order (lanes of a
 // column with shuffles, then the waves in a tree through LDS) into the mean
 // and its squared norm.  Pass 2 forms each row's dot product with the mean and
-// its squared norm in binary64, adds the VPR partials of a row with DPP lane
-// moves, and rounds -dot / (sqrt(|k|^2) * sqrt(|mean|^2)) once to fp32, with
-// IEEE binary64 square roots and division.  The sums run in another order than
-// a plain loop's, so the binary64 cosine may differ from it by a few units of
+// its squared norm in binary64 and adds the VPR partials of a row with DPP lane
+// moves; the binary64 work bounds the kernel as much as the reads do, so the
+// lanes of a group collect VPR rows' sums before the square root and division,
+// which then run once per row (not once per lane group), and the result
+// -dot / (sqrt(|k|^2) * sqrt(|mean|^2)) is rounded once to fp32, with IEEE
+// binary64 square roots and division.  The sums run in another order than a
+// plain loop's, so the binary64 cosine may differ from it by a few units of
 // 2^-53 times (D + n * |sum of |k_i|| / |sum of k_i|); the fp32 score then
 // equals the plain loop's rounding except where that cosine lies within this
 // bound of a midpoint between two fp32 values, where it may be the other
@@ -40,11 +42,12 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kReg = 10;    // rows per thread held in registers
-constexpr int kUnroll = 2;  // rows per thread in flight for the streamed tail
+constexpr int kUnroll = 8;  // rows per thread in flight for the streamed tail
 
-// rows per thread held in LDS: 16 KB each, next to 8*D + D doubles of sums
+// rows per thread held in LDS: 8 KB each, next to 4*D + D doubles of sums, so that
+// two workgroups fit the 160 KB of a CU
 template <int VPR>
-constexpr int lds_rows() { return VPR >= 64 ? 7 : 8; }
+constexpr int lds_rows() { return VPR >= 64 ? 7 : VPR >= 32 ? 8 : 9; }
 
 typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
 
@@ -108,15 +111,15 @@ __device__ __forceinline__ double group_sum(double v) {
     const uint64_t b = __double_as_longlong(x);
     const int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
     int rlo, rhi;
-    switch (ctrl) {  // the DPP control must be a constant
-      case 0: rlo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, false);
-              rhi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, false); break;
-      case 1: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, false);
-              rhi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, false); break;
-      case 2: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, false);
-              rhi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, false); break;
-      default: rlo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, false);
-               rhi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, false); break;
+    switch (ctrl) {  // the DPP control must be a constant; every lane's source is valid
+      case 0: rlo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, true);
+              rhi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, true); break;
+      case 1: rlo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, true);
+              rhi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, true); break;
+      case 2: rlo = __builtin_amdgcn_mov_dpp(lo, 0x141, 0xF, 0xF, true);
+              rhi = __builtin_amdgcn_mov_dpp(hi, 0x141, 0xF, 0xF, true); break;
+      default: rlo = __builtin_amdgcn_mov_dpp(lo, 0x140, 0xF, 0xF, true);
+               rhi = __builtin_amdgcn_mov_dpp(hi, 0x140, 0xF, 0xF, true); break;
     }
     return __longlong_as_double((int64_t)(((uint64_t)(uint32_t)rhi << 32) | (uint32_t)rlo));
   };
@@ -201,13 +204,23 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
       }
     }
   }
-  for (int32_t base = kCap + r0; base < n; base += rpi * kUnroll) {  // streamed tail
+  // streamed tail: whole steps of kUnroll rows per thread without bounds checks, then
+  // the last partial step checked (the same rows in the same order either way)
+  int32_t b0 = kCap;
+  for (; b0 + rpi * kUnroll <= n; b0 += rpi * kUnroll) {
     vec4u v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int32_t t = base + u * rpi;
-      v[u] = load_row<VPR, kPaged>(a, lb, list, t, n, col);
+      const int32_t t = b0 + r0 + u * rpi;
+      v[u] = kPaged ? load_key<true>(a, list, t, VPR, col) : lb[t * VPR + col];
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) add(v[u]);
+  }
+  if (b0 < n) {
+    vec4u v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_row<VPR, kPaged>(a, lb, list, b0 + r0 + u * rpi, n, col);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) add(v[u]);
   }
@@ -257,15 +270,26 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
   for (int e = 0; e < 8; ++e) mu[e] = s_mean[col * 8 + e];
 
   // --- pass 2: per-row dot with the mean and squared norm ------------------------
-  auto finish = [&](int32_t t, double dot, double kk) {
-    // add the VPR partials of the row (consecutive lanes, VPR a power of two <= 64)
+  // Each row's sums end in all VPR lanes of its group; lane `col` keeps those of
+  // the group's row of step kb + col, and every VPR steps (and at the end) each
+  // lane finishes its kept row, so the binary64 square root and division run
+  // once per row rather than once per lane group.
+  double bdot = 0.0, bkk = 0.0;
+  auto keep = [&](int32_t k, double dot, double kk) {
     dot = group_sum<VPR>(dot);
     kk = group_sum<VPR>(kk);
-    if (col == 0 && t < n) {
+    const bool mine = col == (k & (VPR - 1));
+    bdot = mine ? dot : bdot;
+    bkk = mine ? kk : bkk;
+  };
+  auto flush = [&](int32_t k) {  // steps k - k % VPR .. k are kept
+    const int32_t kb = k & ~(VPR - 1);
+    const int32_t t = r0 + (kb + col) * rpi;
+    if (kb + col <= k && t < n) {
       float sc = INFINITY;
       if (t >= a.prot) {
-        const double den = sqrt(kk) * mnorm;
-        sc = (den > 0.0) ? (float)(-(dot / den)) : 0.0f;
+        const double den = sqrt(bkk) * mnorm;
+        sc = (den > 0.0) ? (float)(-(bdot / den)) : 0.0f;
         if (sc == 0.0f) sc = 0.0f;  // -0 written as +0
       }
       out[t] = sc;
@@ -276,30 +300,45 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
   for (int k = 0; k < kReg; ++k) {
     double dot, kk;
     dot_norm(reg[k], mu, dot, kk);
-    finish(r0 + k * rpi, dot, kk);
+    keep(k, dot, kk);
+    if ((k & (VPR - 1)) == VPR - 1) flush(k);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int k = 0; k < kLds; ++k) {
     double dot, kk;
     dot_norm(s_keys[k][tid], mu, dot, kk);
-    finish(r0 + (kReg + k) * rpi, dot, kk);
+    keep(kReg + k, dot, kk);
+    if (((kReg + k) & (VPR - 1)) == VPR - 1) flush(kReg + k);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int32_t b0 = kCap; b0 < n; b0 += rpi * kUnroll) {  // the streamed tail again
+  int32_t k = kReg + kLds;
+  auto step = [&](const vec4u* v) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u, ++k) {
+      double dot, kk;
+      dot_norm(v[u], mu, dot, kk);
+      keep(k, dot, kk);
+      if ((k & (VPR - 1)) == VPR - 1) flush(k);
+    }
+  };
+  int32_t c0 = kCap;
+  for (; c0 + rpi * kUnroll <= n; c0 += rpi * kUnroll) {  // the streamed tail again
     vec4u v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int32_t t = b0 + r0 + u * rpi;
-      v[u] = load_row<VPR, kPaged>(a, lb, list, t, n, col);
+      const int32_t t = c0 + r0 + u * rpi;
+      v[u] = kPaged ? load_key<true>(a, list, t, VPR, col) : lb[t * VPR + col];
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      double dot, kk;
-      dot_norm(v[u], mu, dot, kk);
-      finish(b0 + r0 + u * rpi, dot, kk);
-    }
+    step(v);
   }
+  if (c0 < n) {
+    vec4u v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load_row<VPR, kPaged>(a, lb, list, c0 + r0 + u * rpi, n, col);
+    step(v);
+  }
+  if ((k & (VPR - 1)) != 0) flush(k - 1);
 }
 
 }  // namespace

@@ -646,6 +646,10 @@ def assert_keydiff_close(got, keys, prot):
     (2, 2, 3000, 8, 3, 3000),       # D = 8: every row on chip
     (1, 3, 5000, 128, 0, 5000),     # a long streamed tail
     (2, 2, 300, 32, 17, 310),
+    (1, 2, 1024, 128, 0, 1024),     # 32 steps of 32 rows: the last batch of 16 rows ends exactly
+    (1, 2, 513, 128, 1, 513),       # 17 steps: a last batch of one row
+    (1, 2, 608, 128, 4, 608),       # every row on chip, no streamed tail
+    (1, 2, 609, 128, 4, 640),       # one streamed row: a partial step only
 ])
 def test_score_keydiff_contig(groups, H, n, D, prot, cap):
     say(f"score_keydiff contig groups={groups} H={H} n={n} D={D} prot={prot}")
