@@ -27,6 +27,11 @@
 // the GDN layer and pass offsets.  The log table holds {ln c, 1/c} pairs, so a
 // log makes one 16-byte LDS read.
 //
+// Signals in the usual layout (48 heads per 16-byte aligned token row, unit
+// head stride) take a second kernel with the same arithmetic in the same
+// order, whose tiles go from HBM straight into LDS (see
+// score_weighted_lds_kernel below); other layouts take this one.
+//
 // Precision: the product beta*|v| of two floats is exact in binary64; its
 // natural log is taken in binary64 (table-driven reduction to [-2^-9, 2^-9]
 // and a degree-6 series, within a few binary64 ulps; zero, infinities, NaN
@@ -403,6 +408,279 @@ __global__ __launch_bounds__(kThreads) void score_weighted_kernel(WeightedArgs a
   }
 }
 
+// The same scores for signals laid out with 48 GDN heads per token row, 16-byte
+// aligned rows and unit head stride (the usual [G, n, 48] layout): one pass
+// per GDN layer, and the tiles travel from HBM straight into LDS
+// (global_load_lds_dwordx4), so no register holds a tile in flight and the
+// next layer's tile is requested right after a step's barrier, streaming in
+// while the whole step (logs and fold) runs.  A stage holds the tile of beta
+// and of |v| as 16-byte chunks of four heads, each token row padded to 13
+// chunks so that 64 lanes reading one chunk of 64 consecutive tokens hit
+// distinct LDS banks; each wave takes the logs of its own six heads straight
+// from the stage (no transposed copy), in the same order as above, so both
+// kernels give identical bits.  The two stages are separate LDS arrays and the
+// step loop is unrolled by two, so that the compiler sees that reads of one
+// stage do not depend on the loads in flight into the other.
+constexpr int kQuads = kJPass / 4;                    // chunks of four heads per token row
+constexpr int kRowChunks = kQuads + 1;                // + one pad chunk per row
+constexpr int kStageChunks = kTok * kRowChunks;       // 832 chunks per signal per stage
+constexpr int kSigLoads = kStageChunks / kWave;       // 13 wave loads per signal per stage
+constexpr int kSigWaves = kWaves / 2;                 // waves loading one signal
+constexpr int kLoadsPerWave = (kSigLoads + kSigWaves - 1) / kSigWaves;
+static_assert(kStageChunks % kWave == 0, "a stage is whole wave loads");
+static_assert(kJPass % 4 == 0 && kJW % 2 == 0, "heads in whole chunks, pairs per wave");
+static_assert(kWRow % (kJPass * kHB) == 0 && (kJPass * kHB) % kWave == 0,
+              "a weight slot is whole waves");
+static_assert(kSlots == 2, "the window-end branch names both slots");
+static_assert(kFirstLevelBins * 4 <= kStageChunks * 16, "the bins fit a stage");
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A workgroup barrier that orders LDS accesses only: it does not wait for the
+// tile loads in flight, as a full barrier (with its memory fence) would.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(kThreads) void score_weighted_lds_kernel(
+    WeightedArgs a, const float* __restrict__ wts, const float* __restrict__ beta,
+    const float* __restrict__ vnorm, float* __restrict__ scores) {
+  __shared__ v4f s_b0[kStageChunks], s_v0[kStageChunks];  // stage 0: beta, |v|
+  __shared__ v4f s_b1[kStageChunks], s_v1[kStageChunks];  // stage 1
+  __shared__ double s_w0[kWRow], s_w1[kWRow];
+  __shared__ double2 s_tab[kLnTable];
+  __shared__ double s_red[kWaves][kHB][kTok];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int32_t t0 = blockIdx.x * kTok;
+  const int32_t t = t0 + lane;
+
+  auto store = [&](int q, int hh, int32_t tt, double v) {
+    if (hh < a.hb && tt < a.n)
+      scores[((int64_t)a.layer[q] * a.H + a.h0 + hh) * a.ld + tt] =
+          (tt < a.prot) ? INFINITY : (float)v;
+  };
+  const bool tile_in_prompt = (t0 + kTok <= a.prot);
+  if (wave < kHB) {
+    for (int q = 0; q < a.nl; ++q)
+      if (tile_in_prompt || ((a.empty_mask >> q) & 1u)) store(q, wave, t, 0.0);
+  }
+  if (tile_in_prompt) return;
+  if (a.g_hi > a.g_lo) {
+    if (tid < kLnTable) {
+      const double c = 1.0 + ((double)tid + 0.5) * (1.0 / kLnTable);
+      s_tab[tid] = make_double2(log(c), 1.0 / c);
+    }
+    const int32_t steps = a.g_hi - a.g_lo;
+    double acc[kHB][kSlots];
+#pragma unroll
+    for (int hh = 0; hh < kHB; ++hh)
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) acc[hh][s] = 0.0;
+
+    // Waves [0, 4) load beta, [4, 8) |v|: wave load i of a signal fills stage chunks
+    // [64 i, 64 i + 64), chunk c = token * 13 + quad.  This lane's offsets within a GDN
+    // layer (-1: a pad chunk or a token past n, not loaded; its stale slot only feeds
+    // that token, whose scores are not stored).
+    const int sw = wave % kSigWaves;
+    const bool loads_v = wave >= kSigWaves;
+    int64_t off[kLoadsPerWave];
+#pragma unroll
+    for (int k = 0; k < kLoadsPerWave; ++k) {
+      const int i = sw + k * kSigWaves;
+      const int32_t c = i * kWave + lane;
+      const int32_t tok = c / kRowChunks, q = c % kRowChunks;
+      off[k] = (i < kSigLoads && q < kQuads && t0 + tok < a.n)
+                   ? (int64_t)(t0 + tok) * a.st + 4 * q : -1;
+    }
+    auto issue_into = [&](v4f* stage_sig, const float* sig, int32_t g) __attribute__((always_inline)) {
+      const float* src = sig + (int64_t)g * a.sg;
+#pragma unroll
+      for (int k = 0; k < kLoadsPerWave; ++k) {
+        const int i = sw + k * kSigWaves;
+        if (i >= kSigLoads) break;
+        if (off[k] >= 0)
+          __builtin_amdgcn_global_load_lds(src + off[k], (lds_void*)(stage_sig + i * kWave), 16,
+                                           0, 0);
+      }
+    };
+    auto issue = [&](auto stage, int32_t g) __attribute__((always_inline)) {
+      if constexpr (decltype(stage)::value == 0) {
+        if (loads_v) issue_into(s_v0, vnorm, g);
+        else issue_into(s_b0, beta, g);
+      } else {
+        if (loads_v) issue_into(s_v1, vnorm, g);
+        else issue_into(s_b1, beta, g);
+      }
+    };
+    // one weight of the (GDN layer) per thread of waves [0, 6): slot wave / 3
+    const int32_t w_slot = wave / (kHB * kJPass / kWave);
+    auto load_w = [&](int32_t g) {
+      float w = 0.0f;
+      if (w_slot < kSlots) {
+        const int32_t hh = (tid / kJPass) % kHB;
+        const int32_t j = tid % kJPass;
+        const int64_t wo = a.woff[g - a.g_lo][w_slot];
+        if (wo >= 0 && hh < a.hb) w = wts[wo + (int64_t)hh * a.w_slots * a.Hg + j];
+      }
+      return w;
+    };
+    issue(std::integral_constant<int, 0>{}, a.g_lo);
+    float wnext = load_w(a.g_lo);
+    if (tid < kWRow) s_w0[tid] = (double)wnext;
+
+    int32_t pending = -1, pending_step = -2;
+    // the waves' partial sums of a finished window, added in wave order; read in one
+    // block that waits for its own reads (the tile loads in flight go elsewhere)
+    auto reduce_store = [&](int32_t q) __attribute__((always_inline)) {
+      if (tid < kHB * kTok) {
+        const int hh = tid / kTok;
+        const uint32_t ar = (uint32_t)reinterpret_cast<uintptr_t>(&s_red[0][hh][lane]);
+        double r0, r1, r2, r3, r4, r5, r6, r7;
+        static_assert(kWaves == 8 && kHB * kTok * 8 == 2048, "offsets below");
+        asm volatile(
+            "ds_read_b64 %0, %8\n\t"
+            "ds_read_b64 %1, %8 offset:2048\n\t"
+            "ds_read_b64 %2, %8 offset:4096\n\t"
+            "ds_read_b64 %3, %8 offset:6144\n\t"
+            "ds_read_b64 %4, %8 offset:8192\n\t"
+            "ds_read_b64 %5, %8 offset:10240\n\t"
+            "ds_read_b64 %6, %8 offset:12288\n\t"
+            "ds_read_b64 %7, %8 offset:14336\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+              "=&v"(r7)
+            : "v"(ar)
+            : "memory");
+        double v = 0.0;
+        v += r0;
+        v += r1;
+        v += r2;
+        v += r3;
+        v += r4;
+        v += r5;
+        v += r6;
+        v += r7;
+        store(q, hh, t, v);
+      }
+    };
+    const int32_t jb = wave * kJW;  // this wave's heads [jb, jb + 6)
+    auto body = [&](auto stage, int32_t step) __attribute__((always_inline)) {
+      constexpr int kCur = decltype(stage)::value;
+      const v4f* sb = kCur == 0 ? s_b0 : s_b1;
+      const v4f* sv = kCur == 0 ? s_v0 : s_v1;
+      const double* w = kCur == 0 ? s_w0 : s_w1;
+      double* w_next = kCur == 0 ? s_w1 : s_w0;
+      const int32_t g = a.g_lo + step;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the stage
+      __syncthreads();  // the whole stage is in LDS, and the other one was read
+      if (step + 1 < steps) {  // the next layer streams in during this step
+        wnext = load_w(g + 1);
+        issue(std::integral_constant<int, 1 - kCur>{}, g + 1);
+      }
+      if (pending >= 0) {
+        reduce_store(pending);
+        pending = -1;
+        pending_step = step;
+      }
+      // this wave's six heads for token `lane`, read in one block that waits for its own
+      // reads (the compiler cannot tell these addresses from the loads in flight)
+      const uint32_t ab = (uint32_t)reinterpret_cast<uintptr_t>(sb + lane * kRowChunks) + jb * 4;
+      const uint32_t av = (uint32_t)reinterpret_cast<uintptr_t>(sv + lane * kRowChunks) + jb * 4;
+      uint64_t rb0, rb1, rb2, rv0, rv1, rv2;
+      asm volatile(
+          "ds_read_b64 %0, %6\n\t"
+          "ds_read_b64 %1, %6 offset:8\n\t"
+          "ds_read_b64 %2, %6 offset:16\n\t"
+          "ds_read_b64 %3, %7\n\t"
+          "ds_read_b64 %4, %7 offset:8\n\t"
+          "ds_read_b64 %5, %7 offset:16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(rb0), "=&v"(rb1), "=&v"(rb2), "=&v"(rv0), "=&v"(rv1), "=&v"(rv2)
+          : "v"(ab), "v"(av)
+          : "memory");
+      const uint64_t rb[3] = {rb0, rb1, rb2}, rv[3] = {rv0, rv1, rv2};
+      float bv[kJW], vv[kJW];
+#pragma unroll
+      for (int k = 0; k < kJW / 2; ++k) {
+        bv[2 * k] = __uint_as_float((uint32_t)rb[k]);
+        bv[2 * k + 1] = __uint_as_float((uint32_t)(rb[k] >> 32));
+        vv[2 * k] = __uint_as_float((uint32_t)rv[k]);
+        vv[2 * k + 1] = __uint_as_float((uint32_t)(rv[k] >> 32));
+      }
+      double xv[kJW];
+      bool any_special = false;
+#pragma unroll
+      for (int k = 0; k < kJW; ++k) {
+        bool sp;
+        xv[k] = ln_fast((double)bv[k] * (double)vv[k], s_tab, &sp);
+        any_special |= sp;
+      }
+      if (any_special) {
+#pragma unroll
+        for (int k = 0; k < kJW; ++k) {
+          const double xp = (double)bv[k] * (double)vv[k];
+          const uint32_t ex = (uint32_t)__double2hiint(xp) >> 20;
+          if (ex - 1u >= 0x7feu) xv[k] = ln_special(xp);
+        }
+      }
+      const int32_t gi = g - a.g_lo;
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        if (a.woff[gi][s] < 0) continue;
+#pragma unroll
+        for (int hh = 0; hh < kHB; ++hh) {
+          const double* wr = w + (s * kHB + hh) * kJPass + jb;
+          double v = acc[hh][s];
+#pragma unroll
+          for (int k = 0; k < kJW; ++k) v = fma(wr[k], xv[k], v);
+          acc[hh][s] = v;
+        }
+      }
+      // the next layer's weights (that row was last read in step - 1)
+      if (step + 1 < steps && tid < kWRow) w_next[tid] = (double)wnext;
+
+      uint32_t ends = a.end_mask[gi];
+      while (ends) {
+        const int32_t q = __builtin_ctz(ends);
+        ends &= ends - 1u;
+        const int32_t s_q = a.slot[q];
+        if (pending >= 0) {
+          lds_barrier();
+          reduce_store(pending);
+          pending = -1;
+          pending_step = step;
+        }
+        if (pending_step == step) lds_barrier();
+        // selects of values (no branch per slot), so that acc stays in registers
+        const bool first = s_q == 0;
+#pragma unroll
+        for (int hh = 0; hh < kHB; ++hh) {
+          const double x0 = acc[hh][0], x1 = acc[hh][1];
+          s_red[wave][hh][lane] = first ? x0 : x1;
+          acc[hh][0] = first ? 0.0 : x0;
+          acc[hh][1] = first ? x1 : 0.0;
+        }
+        pending = q;
+      }
+    };
+    for (int32_t step = 0; step < steps; step += 2) {
+      body(std::integral_constant<int, 0>{}, step);
+      if (step + 1 < steps) body(std::integral_constant<int, 1>{}, step + 1);
+    }
+    if (pending >= 0) {
+      __syncthreads();
+      reduce_store(pending);
+    }
+  }
+  if (a.hist0) {
+    __syncthreads();
+    add_first_level_bins(a, scores, t0, reinterpret_cast<uint32_t*>(&s_b0[0]));
+  }
+}
+
 static_assert(kThreads >= kHB * kTok, "one thread per (head, token) in the reduction");
 static_assert(kFirstLevelBins * 4 <= 2 * kJPass * kXStride * 8, "the bins fit the LDS tiles");
 static_assert(kWaves >= kHB, "one wave per head for the direct stores");
@@ -419,6 +697,9 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
   const bool vec = sj == 1 && sg % 2 == 0 && st % 2 == 0 && Hg % 2 == 0 &&
                    (reinterpret_cast<uintptr_t>(beta) & 7u) == 0 &&
                    (reinterpret_cast<uintptr_t>(vnorm) & 7u) == 0;
+  const bool lds_path = Hg == kJPass && sj == 1 && st % 4 == 0 && sg % 4 == 0 &&
+                        (reinterpret_cast<uintptr_t>(beta) & 15u) == 0 &&
+                        (reinterpret_cast<uintptr_t>(vnorm) & 15u) == 0;
   // Greedy grouping of layers into launches: a layer joins the current launch
   // in the first slot whose layers' windows it does not overlap; when no slot
   // is free, the launch is full or its GDN range would pass kPlanLayers, a
@@ -481,7 +762,10 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
               (((int64_t)a.layer[q] * H + h0) * w_slots + (g - begin[q])) * Hg;
         a.end_mask[end[q] - 1 - lo] |= 1u << q;
       }
-      if (vec)
+      if (lds_path)
+        hipLaunchKernelGGL(score_weighted_lds_kernel, dim3(tiles), dim3(kThreads), 0, stream, a,
+                           w, beta, vnorm, scores);
+      else if (vec)
         hipLaunchKernelGGL(score_weighted_kernel<2>, dim3(tiles), dim3(kThreads), 0, stream, a, w,
                            beta, vnorm, scores);
       else

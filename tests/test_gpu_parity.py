@@ -402,6 +402,44 @@ def test_score_weighted(G, L, H, Hg, n, prot, width):
     say(f"  bit-identical fraction {same:.6f}")
 
 
+@pytest.mark.parametrize("G,L,H,n,prot,windows", [
+    (48, 16, 4, 1000, 256, None),   # the GateSight windows
+    (12, 5, 6, 130, 0, None),       # six KV heads: two launches; a ragged last tile
+    (9, 4, 3, 64, 63, "custom"),    # one tile; two windows end together, one is empty
+    (70, 20, 2, 333, 5, None),      # more than 16 attention layers: several launches
+    (6, 2, 4, 40, 0, None),         # fewer tokens than one tile
+    (15, 6, 4, 700, 640, None),     # the first ten tiles inside the prompt
+])
+def test_score_weighted_layouts_identical(G, L, H, n, prot, windows):
+    """[G, n, 48] signals at a 16-byte aligned base take the kernel that streams tiles into
+    LDS; the same values 8 bytes further on take the register-tile kernel.  Both compute
+    the same sums in the same order: every score bit-identical, and within the oracle's
+    bound."""
+    Hg, width = 48, 6
+    say(f"score_weighted layouts G={G} L={L} H={H} n={n} prot={prot} windows={windows}")
+    beta, vnorm, w, begins, counts = weighted_case(G, L, H, Hg, n, prot, width, seed=G * L + n)
+    if windows == "custom":
+        begins, counts = [0, 2, 2, 5], [4, 2, 3, 0]
+    dw = torch.from_numpy(w).to(DEV)
+    outs = []
+    for shift in (0, 2):  # floats past the allocation's (256-byte aligned) start
+        db = torch.zeros(beta.size + shift, dtype=torch.float32, device=DEV)
+        dv = torch.zeros(vnorm.size + shift, dtype=torch.float32, device=DEV)
+        db[shift:] = torch.from_numpy(beta.ravel()).to(DEV)
+        dv[shift:] = torch.from_numpy(vnorm.ravel()).to(DEV)
+        assert (db[shift:].data_ptr() % 16 == 0) == (shift == 0)
+        s = torch.full((L * H, n), float("nan"), dtype=torch.float32, device=DEV)
+        B.kvevict_score_weighted(s, n, db[shift:], dv[shift:], n * Hg, Hg, 1, dw, width, begins,
+                                 counts, L, H, G, Hg, n, prot)
+        torch.cuda.synchronize()
+        outs.append(to_np(s))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ob, oc = (begins, counts) if windows == "custom" else oracle.gdn_windows(L, G, width)
+    want = oracle.score_weighted(beta, vnorm, w, ob, oc, prot)
+    same = assert_weighted_close(outs[0], want, prot)
+    say(f"  bit-identical fraction {same:.6f}")
+
+
 @pytest.mark.parametrize("tied", [4096, 4097])
 def test_select_global_tied_bucket_list_capacity(tied):
     """`tied` candidates share the threshold value exactly, spread over all lists, and the
