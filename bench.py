@@ -292,25 +292,6 @@ def select_compact_ms(torch, rounds, st, steps):
     return eager, e0.elapsed_time(e1) / (reps * GRAPH_ROUNDS)
 
 
-def score_alone_ms(torch, rounds, st, steps):
-    """The scorer alone, `steps` calls back to back between two events.  Inside a round the
-    scorer follows the previous round's gather, whose last written lines are still being
-    written back from the caches while it runs; alone, it shows its own rate."""
-    fns = [fn for name, fn in rounds.phases(st.cfg) if name == "score"]
-    for s in range(2):
-        for fn in fns:
-            fn(st, s)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s in range(steps):
-        for fn in fns:
-            fn(st, s)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
-
-
 GATHER_KERNELS = ("compact_list_kernel", "compact_group_kernel")
 
 
@@ -612,24 +593,21 @@ def measure(torch, binding, configs, rounds, name, args, headline):
     if not cfg.page_draw:
         entry["roofline"] = roofline(name, cfg, r["kv_bytes"], comp_ms)
     if cfg.scorer in ("weighted", "keydiff") and "score" in r["kernels_ms"]:
-        # the scorer: its inputs (GDN signals, or the keys) read once and the scores
-        # written once (the keys KeyDiff reads a second time are not algorithmic bytes;
-        # the round's score bytes count the select's read as well), timed alone and as
-        # it runs inside the round
+        # the scorer as it runs in the round: its inputs (GDN signals, or the keys) read
+        # once and the scores written once (the keys KeyDiff reads a second time are not
+        # algorithmic bytes; the round's score bytes count the select's read as well)
         lists = cfg.L * cfg.H * cfg.R
         sb = r["algorithmic_bytes"]["inputs"] + (
             lists * r["state"].n * 4 if cfg.scorer == "weighted"
             else r["algorithmic_bytes"]["scores"] // 2)
-        alone = score_alone_ms(torch, rounds, r["state"], max(steps, 10))
-        sg = sb / (alone * 1e-3) / 1e9
+        ms = r["kernels_ms"]["score"]
+        sg = sb / (ms * 1e-3) / 1e9
         entry["roofline_score"] = {
             "bound": "hbm",
             "kernel": ("score_weighted_lds_kernel" if cfg.scorer == "weighted"
                        else "score_keydiff_kernel"),
             "achieved": sg, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": sg / PEAK_HBM_GBPS,
-            "algorithmic_bytes": sb, "ms": round(alone, 4),
-            "in_round_ms": round(r["kernels_ms"]["score"], 4),
-            "in_round_frac": sb / (r["kernels_ms"]["score"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+            "algorithmic_bytes": sb, "ms": round(ms, 4)}
     st = r["state"]
     if r["ms_per_step"] < 1.0 and not (cfg.inplace or cfg.page_draw or cfg.rounds > 1):
         # latency-bound rounds: also replayed from a HIP graph
