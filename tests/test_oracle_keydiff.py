@@ -1,5 +1,6 @@
-"""Oracle pins for the KeyDiff key score (GateSight Sec. 5.1 baselines paragraph: cosine
-similarity of each cached key to the unnormalised mean key of its head, least similar kept)."""
+"""Oracle pins for the KeyDiff key score (GateSight Sec. 5.1, baselines paragraph): a key
+scores minus its cosine to the plain average of its head's keys, so a per-head top-K keeps
+the keys that point away from that average."""
 
 import math
 
