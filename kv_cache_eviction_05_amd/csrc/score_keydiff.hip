@@ -9,21 +9,25 @@
 // The mean needs every key before any cosine.  One workgroup of 512 threads
 // per list, two per CU: a row of D bf16 is VPR = D/8 16-byte vectors, thread t
 // owns vector column t % VPR of rows t / VPR + k * (512 / VPR); its first 10
-// such rows stay in registers and the next 9 (D <= 128), 8 or 7 in LDS, which
-// at D = 128 holds 608 of 1088 rows between the two passes.  The other rows
-// are read a second time soon after the first, and those reads mostly hit the
-// Infinity Cache: measured on the 36,864-list batch, a plain read of every row
-// once and of the streamed rows again takes 1.22x the time of one read;
-// twelve register rows gained nothing, and one 1024-thread workgroup per CU
-// holding 1024 rows (1.04x the bytes) was 14% slower, since two workgroups per
-// CU let one list's reads overlap the other's arithmetic.
+// such rows (11 at D = 128) stay in registers and the next 9 (D <= 128), 8 or 7
+// in LDS, which at D = 128 holds 640 of 1088 rows between the two passes.  The
+// other rows are read a second time soon after the first, and those reads
+// mostly hit the Infinity Cache: measured on the 36,864-list batch, a plain
+// read of every row once and of the streamed rows again takes 1.22x the time
+// of one read; twelve register rows gained nothing, and one 1024-thread
+// workgroup per CU holding 1024 rows (1.04x the bytes) was 14% slower, since
+// two workgroups per CU let one list's reads overlap the other's arithmetic.
 // Pass 1 accumulates the column sums in binary64 in a fixed order (lanes of a
 // column with shuffles, then the waves in a tree through LDS) into the mean
 // and its squared norm.  Pass 2 forms each row's dot product with the mean and
 // its squared norm in binary64 and adds the VPR partials of a row with DPP lane
 // moves; the binary64 work bounds the kernel as much as the reads do, so the
 // lanes of a group collect VPR rows' sums before the square root and division,
-// which then run once per row (not once per lane group), and the result
+// which then run once per row (not once per lane group).  At D = 128 in a
+// contiguous store two rows go through the lane reduction together (one
+// exchange, then three levels that serve both), and the streamed rows come
+// through buffer loads from a per-step base, whose range check reads rows past
+// n as zeros (no per-row bounds checks).  The result
 // -dot / (sqrt(|k|^2) * sqrt(|mean|^2)) is rounded once to fp32, with IEEE
 // binary64 square roots and division.  The sums run in another order than a
 // plain loop's, so the binary64 cosine may differ from it by a few units of
@@ -41,7 +45,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kReg = 10;    // rows per thread held in registers
+constexpr int kReg0 = 10;   // rows per thread held in registers
 constexpr int kUnroll = 8;  // rows per thread in flight for the streamed tail
 
 // rows per thread held in LDS: 8 KB each, next to 4*D + D doubles of sums, so that
@@ -132,6 +136,36 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
+// A binary64 DPP move (each half separately), every lane's source valid.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, kCtrl, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), kCtrl, 0xF, 0xF, true);
+  return __longlong_as_double((int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// The sums of two rows' partials over each aligned group of 16 lanes, the first row's
+// in the even lanes and the second's in the odd ones: even lanes swap their second-row
+// partial for the odd neighbour's first-row one (lanes i, i^1), then the lanes of one
+// parity add within quads (i, i^2) and across quads by rotations of 4 and 8 within the
+// 16-lane row, which keep the parity.
+__device__ __forceinline__ double pair_sum16(double a, double b, bool odd) {
+  const double send = odd ? a : b;
+  double v = (odd ? b : a) + dpp_f64<0xB1>(send);  // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);                           // quad_perm [2,3,0,1]
+  v += dpp_f64<0x124>(v);                          // row_ror:4
+  v += dpp_f64<0x128>(v);                          // row_ror:8
+  return v;
+}
+
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+// A raw buffer over `bytes` bytes from p: loads at or past the end read as zeros.
+__device__ __forceinline__ buf_rsrc rows_rsrc(const void* p, int64_t bytes) {
+  const int32_t nb = bytes > 0 ? (bytes < 0x7fffffff ? (int32_t)bytes : 0x7fffffff) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nb, 0x00020000);
+}
+
 // Partial dot with the mean and squared norm of one 16-byte vector.
 __device__ __forceinline__ void dot_norm(vec4u v, const double* mu, double& dot, double& kk) {
   double x[8];
@@ -145,11 +179,16 @@ __device__ __forceinline__ void dot_norm(vec4u v, const double* mu, double& dot,
   }
 }
 
-template <int VPR, bool kPaged>
+template <int VPR, bool kPaged, bool kPairOk>
 __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) {
   constexpr int32_t rpi = kThreads / VPR;  // rows per iteration
   constexpr int32_t D = VPR * 8;
+  // D = 128 in a contiguous store: rows two at a time through pass 2, the streamed
+  // rows through buffer loads (rows past n read as zeros)
+  constexpr bool kPair = VPR == 16 && !kPaged && kPairOk;
   constexpr int kLds = lds_rows<VPR>();
+  constexpr int kReg = kPair ? 11 : kReg0;
+  static_assert(!kPair || (kReg + kLds) % 2 == 0, "pairs of on-chip steps");
   constexpr int32_t kCap = (kReg + kLds) * rpi;  // rows held on chip
   __shared__ vec4u s_keys[kLds][kThreads];
   __shared__ double s_part[kWaves / 2][D];   // column sums of the upper half of the waves
@@ -204,9 +243,22 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
       }
     }
   }
+  const uint32_t row_off = (uint32_t)(r0 * VPR + col) * 16u;  // this thread's vector in a step
+  if constexpr (kPair) {
+    // streamed tail through a buffer starting at the step's first row
+    for (int32_t b0 = kCap; b0 < n; b0 += rpi * kUnroll) {
+      const buf_rsrc rs = rows_rsrc(lb + (int64_t)b0 * VPR, (int64_t)(n - b0) * VPR * 16);
+      vec4u v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + u * rpi * VPR * 16, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) add(v[u]);
+    }
+  }
   // streamed tail: whole steps of kUnroll rows per thread without bounds checks, then
   // the last partial step checked (the same rows in the same order either way)
-  int32_t b0 = kCap;
+  int32_t b0 = kPair ? n : kCap;
   for (; b0 + rpi * kUnroll <= n; b0 += rpi * kUnroll) {
     vec4u v[kUnroll];
 #pragma unroll
@@ -270,6 +322,59 @@ __global__ __launch_bounds__(kThreads) void score_keydiff_kernel(KeydiffArgs a) 
   for (int e = 0; e < 8; ++e) mu[e] = s_mean[col * 8 + e];
 
   // --- pass 2: per-row dot with the mean and squared norm ------------------------
+  if constexpr (kPair) {
+    // Two steps at a time: after pair_sum16 the even lanes of a 16-lane group hold the
+    // sums of the first step's row, the odd lanes the second's; lane col keeps those of
+    // step kb + col, and every 16 steps (and at the end) each lane finishes its kept row.
+    const bool odd = (col & 1) != 0;
+    double bdot = 0.0, bkk = 0.0;
+    auto keep2 = [&](int32_t k, vec4u v0, vec4u v1) __attribute__((always_inline)) {
+      double d0, q0, d1, q1;
+      dot_norm(v0, mu, d0, q0);
+      dot_norm(v1, mu, d1, q1);
+      const double d = pair_sum16(d0, d1, odd);
+      const double q = pair_sum16(q0, q1, odd);
+      const bool mine = (col >> 1) == ((k >> 1) & 7);
+      bdot = mine ? d : bdot;
+      bkk = mine ? q : bkk;
+    };
+    auto flush = [&](int32_t k) __attribute__((always_inline)) {  // steps k - k % 16 .. k
+      const int32_t kb = k & ~15;
+      const int32_t t = r0 + (kb + col) * rpi;
+      if (kb + col <= k && t < n) {
+        float sc = INFINITY;
+        if (t >= a.prot) {
+          const double den = sqrt(bkk) * mnorm;
+          sc = (den > 0.0) ? (float)(-(bdot / den)) : 0.0f;
+          if (sc == 0.0f) sc = 0.0f;  // -0 written as +0
+        }
+        out[t] = sc;
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < kReg + kLds; k += 2) {
+      const vec4u v0 = k < kReg ? reg[k] : s_keys[k - kReg][tid];
+      const vec4u v1 = k + 1 < kReg ? reg[k + 1] : s_keys[k + 1 - kReg][tid];
+      keep2(k, v0, v1);
+      if (((k + 1) & 15) == 15) flush(k + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    int32_t k = kReg + kLds;
+    for (int32_t c0 = kCap; c0 < n; c0 += rpi * kUnroll) {  // the streamed tail again
+      const buf_rsrc rs = rows_rsrc(lb + (int64_t)c0 * VPR, (int64_t)(n - c0) * VPR * 16);
+      vec4u v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + u * rpi * VPR * 16, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kUnroll; u += 2, k += 2) {
+        keep2(k, v[u], v[u + 1]);
+        if (((k + 1) & 15) == 15) flush(k + 1);
+      }
+    }
+    if ((k & 15) != 0) flush(k - 1);
+    return;
+  }
   // Each row's sums end in all VPR lanes of its group; lane `col` keeps those of
   // the group's row of step kb + col, and every VPR steps (and at the end) each
   // lane finishes its kept row, so the binary64 square root and division run
@@ -357,12 +462,16 @@ hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys
   a.prot = prot;
   a.vpr = D / 8;
   const dim3 grid((unsigned)num_lists), block(kThreads);
-#define KVEVICT_KEYDIFF_CASE(V)                                                       \
-  case V:                                                                             \
-    if (keys.paged)                                                                   \
-      hipLaunchKernelGGL((score_keydiff_kernel<V, true>), grid, block, 0, stream, a);  \
-    else                                                                              \
-      hipLaunchKernelGGL((score_keydiff_kernel<V, false>), grid, block, 0, stream, a); \
+  // buffer loads address a list's streamed rows with 32-bit byte counts
+  const bool pair_ok = (int64_t)n * D * 2 <= 0x7fffffff;
+#define KVEVICT_KEYDIFF_CASE(V)                                                              \
+  case V:                                                                                    \
+    if (keys.paged)                                                                          \
+      hipLaunchKernelGGL((score_keydiff_kernel<V, true, false>), grid, block, 0, stream, a);  \
+    else if (pair_ok)                                                                        \
+      hipLaunchKernelGGL((score_keydiff_kernel<V, false, true>), grid, block, 0, stream, a);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((score_keydiff_kernel<V, false, false>), grid, block, 0, stream, a); \
     break;
   switch (a.vpr) {
     KVEVICT_KEYDIFF_CASE(1)
