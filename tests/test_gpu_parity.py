@@ -826,6 +826,32 @@ def test_compact_inplace(layout, shared, variable, D):
                   n, K, D, freed, fcount)
 
 
+@pytest.mark.parametrize("layout,shared,variable", [
+    ("contig", False, True),
+    ("paged", False, False),
+    ("paged", True, True),
+])
+def test_compact_inplace_long_lists(layout, shared, variable):
+    """Lists of 13,000 rows keeping 12,800 (per-list counts, per-head and shared, contiguous
+    and paged): every moved row equals the oracle's, the rest untouched, the freed pages
+    exact."""
+    groups, H, ps, n, K, prot, D = 2, 2, 16, 13000, 12800, 37, 64
+    say(f"compact_inplace long lists {layout} shared={shared} variable={variable} K={K}")
+    ipg = 1 if shared else H
+    kept, counts = keep_sets(groups * ipg, n, K, prot, seed=K, variable=variable)
+    desc, pt, ks, vs, k, v = make_store(layout, groups, H, D, n, ps, seed=6)
+    freed = torch.full((groups * (n // ps + 1),), -5, dtype=torch.int32, device=DEV)
+    fcount = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.kvevict_compact_inplace(desc, k, v, torch.from_numpy(kept).to(DEV), K,
+                              torch.from_numpy(counts).to(DEV) if variable else None, K, n,
+                              groups, ipg, freed, fcount, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_inplace(layout, ks, vs, k, v, kept, counts if variable else None, groups, H, ipg, pt, ps,
+                  n, K, D, freed, fcount)
+
+
 @pytest.mark.parametrize("layout,shared,D,n,K,prot", [
     ("contig", False, 128, 300, 240, 37),
     ("contig", True, 40, 300, 240, 0),
