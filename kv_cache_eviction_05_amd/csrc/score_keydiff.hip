@@ -160,7 +160,10 @@ __device__ __forceinline__ double pair_sum16(double a, double b, bool odd) {
 }
 
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
-// A raw buffer over `bytes` bytes from p: loads at or past the end read as zeros.
+// A raw buffer over `bytes` bytes from p: loads at or past the end read as zeros.  Stride 0
+// makes the record count a byte count; the last word's 0x00020000 sets the data format
+// field to 32-bit elements, with no swizzle and no added thread id (the raw-buffer setting
+// of this GPU family).
 __device__ __forceinline__ buf_rsrc rows_rsrc(const void* p, int64_t bytes) {
   const int32_t nb = bytes > 0 ? (bytes < 0x7fffffff ? (int32_t)bytes : 0x7fffffff) : 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nb, 0x00020000);
