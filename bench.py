@@ -594,8 +594,10 @@ def measure(torch, binding, configs, rounds, name, args, headline):
         entry["roofline"] = roofline(name, cfg, r["kv_bytes"], comp_ms)
     if cfg.scorer in ("weighted", "keydiff") and "score" in r["kernels_ms"]:
         # the scorer as it runs in the round: its inputs (GDN signals, or the keys) read
-        # once and the scores written once (the keys KeyDiff reads a second time are not
-        # algorithmic bytes; the round's score bytes count the select's read as well)
+        # once and the scores written once (keys a KeyDiff kernel reads a second time are
+        # not algorithmic bytes; the round's score bytes count the select's read as well).
+        # KeyDiff lists of at most 1088 keys at D = 128 in a contiguous store are held on
+        # chip whole by their own kernel.
         lists = cfg.L * cfg.H * cfg.R
         sb = r["algorithmic_bytes"]["inputs"] + (
             lists * r["state"].n * 4 if cfg.scorer == "weighted"
@@ -605,6 +607,8 @@ def measure(torch, binding, configs, rounds, name, args, headline):
         entry["roofline_score"] = {
             "bound": "hbm",
             "kernel": ("score_weighted_lds_kernel" if cfg.scorer == "weighted"
+                       else "score_keydiff_resident_kernel"
+                       if cfg.D == 128 and cfg.n <= 1088 and cfg.layout == "contig"
                        else "score_keydiff_kernel"),
             "achieved": sg, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": sg / PEAK_HBM_GBPS,
             "algorithmic_bytes": sb, "ms": round(ms, 4)}

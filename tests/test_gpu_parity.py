@@ -684,10 +684,19 @@ def assert_keydiff_close(got, keys, prot):
     (2, 2, 3000, 8, 3, 3000),       # D = 8: every row on chip
     (1, 3, 5000, 128, 0, 5000),     # a long streamed tail
     (2, 2, 300, 32, 17, 310),
-    (1, 2, 1024, 128, 0, 1024),     # 32 steps of 32 rows: the last batch of 16 rows ends exactly
-    (1, 2, 513, 128, 1, 513),       # 17 steps: a last batch of one row
-    (1, 2, 608, 128, 4, 608),       # every row on chip, no streamed tail
-    (1, 2, 609, 128, 4, 640),       # one streamed row: a partial step only
+    # D = 128, n <= 1088: the whole list on chip (256 threads, 16 rows per step)
+    (1, 2, 1024, 128, 0, 1024),     # 64 whole steps, the last four skipped
+    (1, 2, 513, 128, 1, 513),       # a last step of one row
+    (1, 2, 608, 128, 4, 608),
+    (1, 2, 609, 128, 4, 640),       # padded rows past n in the store
+    (2, 3, 1088, 128, 0, 1100),     # exactly the 68 steps held on chip, padded store
+    (1, 2, 17, 128, 0, 17),         # two steps, one of them a single row
+    (1, 2, 300, 128, 300, 300),     # every slot protected
+    (1, 2, 1000, 128, 999, 1000),   # every slot but the last protected
+    # D = 128, n > 1088: 640 rows on chip, the rest streamed in batches of 256 rows
+    (1, 2, 1089, 128, 2, 1089),     # a streamed tail of 449 rows, its last batch partial
+    (1, 2, 1152, 128, 0, 1152),     # two whole batches, the last one ends exactly
+    (1, 2, 1153, 128, 1, 1153),     # a last batch of one row
 ])
 def test_score_keydiff_contig(groups, H, n, D, prot, cap):
     say(f"score_keydiff contig groups={groups} H={H} n={n} D={D} prot={prot}")
