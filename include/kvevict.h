@@ -39,6 +39,14 @@
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error status nothing has been enqueued and no output is touched.
  *     KVEVICT_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - One launch holds fewer than 2^32 work-items in a grid dimension.  A call
+ *     whose grid would not fit returns KVEVICT_ERR_INVALID_ARG with nothing
+ *     enqueued: from 2^22 lists where a list takes a 1024-thread workgroup
+ *     (the global top-B; per-head top-K and its random form for lists of more
+ *     than 15,360 candidates after the prompt), 2^23 for 512 threads (KeyDiff),
+ *     2^24 for 256 (in-place compaction, the one-launch rounds, the page draw)
+ *     and 2^25 for 128 (per-head top-K of shorter lists), and from 2^29 tokens
+ *     for the weighted scores (a 512-thread workgroup per 64 tokens).
  *   - Empty batches (zero lists or groups) are valid and enqueue nothing.
  */
 #ifndef KVEVICT_H
@@ -151,8 +159,8 @@ kvevict_status kvevict_score_weighted(float* scores, int64_t ld, const float* be
  * A key or a mean of norm zero gives cos = 0; a zero score is written as +0.
  * A paged row whose page id falls outside the pool reads as zeros.
  * Requires D = head_dim in {8, 16, 32, ..., 512}, 0 <= prot <= n <= rows of a
- * list, n * D / 8 < 2^31, ld >= n, num_groups*H < 2^31.  KVEVICT_ERR_UNSUPPORTED
- * for other D.
+ * list, n * D / 8 < 2^31, ld >= n, num_groups*H < 2^23 (one workgroup per list,
+ * fewer than 2^32 work-items per launch).  KVEVICT_ERR_UNSUPPORTED for other D.
  */
 kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv_desc* keys,
                                      const void* k_cache, int64_t num_groups, int32_t n,

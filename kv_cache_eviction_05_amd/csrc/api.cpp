@@ -24,7 +24,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // product that could overflow.
 bool prod_le(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
-kvevict_status hip_status(hipError_t e) { return e == hipSuccess ? KVEVICT_OK : KVEVICT_ERR_HIP; }
+// A launcher returns hipErrorInvalidConfiguration, before it enqueues anything, for a call too
+// large for one grid (2^32 or more work-items in a dimension): a size out of its range.
+kvevict_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVEVICT_OK;
+  return e == hipErrorInvalidConfiguration ? KVEVICT_ERR_INVALID_ARG : KVEVICT_ERR_HIP;
+}
 
 int log2_exact(int32_t v) {
   if (v <= 0 || (v & (v - 1)) != 0) return -1;
@@ -172,7 +177,8 @@ kvevict_status kvevict_score_keydiff(float* scores, int64_t ld, const kvevict_kv
   if (vpr > 64 || (vpr & (vpr - 1)) != 0) return KVEVICT_ERR_UNSUPPORTED;  // D in {8, 16, ..., 512}
   if (n > sv.max_rows) return KVEVICT_ERR_INVALID_ARG;
   if ((int64_t)n * vpr > kInt32Max) return KVEVICT_ERR_INVALID_ARG;  // 32-bit row offsets
-  if (!prod_le(num_groups, H, kInt32Max)) return KVEVICT_ERR_INVALID_ARG;
+  // one workgroup of up to 512 threads per list, fewer than 2^32 work-items per launch
+  if (!prod_le(num_groups, H, (1LL << 23) - 1)) return KVEVICT_ERR_INVALID_ARG;
   const int64_t lists = num_groups * H;
   if (lists > 0 && n > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
   return hip_status(kvevict::launch_score_keydiff(scores, ld, sv, k_cache, D, H, lists, n, prot,
@@ -373,6 +379,11 @@ kvevict_status kvevict_score_select_global(
                     workspace_bytes, &budget, &launch);
   if (st != KVEVICT_OK || !launch) return st;
   if (budget_out) *budget_out = budget;
+  // every launch of the call fits its grid before the first is enqueued
+  if (num_lists > kvevict::max_workgroups(kvevict::kGlobalThreads) ||
+      (n + kvevict::kWeightedTile - 1) / kvevict::kWeightedTile >
+          kvevict::max_workgroups(kvevict::kWeightedThreads))
+    return KVEVICT_ERR_INVALID_ARG;
   // prompts and cleared workspace, then the scores with the first radix level
   // added by the scorer, then the rest of the select
   hipError_t e = kvevict::launch_select_global_init(kept_idx, kept_ld, kept_count, num_lists, n,

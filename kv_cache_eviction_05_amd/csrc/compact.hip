@@ -315,6 +315,8 @@ hipError_t launch_compact(const StoreView& src, const void* k_src, const void* v
                           hipStream_t stream, void* order_ws) {
   if (num_groups == 0 || K == 0) return hipSuccess;
   const Plan p = plan_compact(src, dst, D, H, K, num_groups, kept_count != nullptr);
+  // one thread per item in the page-order scatter
+  if ((p.items + 255) / 256 > max_workgroups(256)) return hipErrorInvalidConfiguration;
   CompactArgs a;
   a.src = src;
   a.dst = dst;

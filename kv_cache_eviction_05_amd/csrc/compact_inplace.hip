@@ -227,6 +227,7 @@ hipError_t launch_compact_inplace(const StoreView& st, void* k, void* v, int32_t
   if (num_groups == 0 || H == 0) return hipSuccess;
   if (num_groups * H > 0x7fffffffLL || (int64_t)n * (D / 8) > (1LL << 30))
     return hipErrorInvalidValue;
+  if (num_groups * H > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   InplaceArgs a;
   a.st = st;
   a.k = static_cast<vec4u*>(k);

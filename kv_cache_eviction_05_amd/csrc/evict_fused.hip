@@ -218,6 +218,7 @@ hipError_t launch_evict_random_inplace(const StoreView& st, void* k, void* v, in
                                        int32_t* freed, uint32_t* freed_count, uint32_t* errors,
                                        hipStream_t stream) {
   if (num_groups == 0 || H == 0) return hipSuccess;
+  if (num_groups * H > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   FusedArgs a;
   a.st = st;
   a.k = static_cast<vec4u*>(k);

@@ -107,6 +107,7 @@ hipError_t launch_evict_pages(int32_t* page_table, int64_t pt_ld, int32_t page_s
                               uint64_t seed, uint32_t round, int32_t* kept_pages, int64_t kept_ld,
                               int32_t* freed, uint32_t* freed_count, hipStream_t stream) {
   if (num_groups == 0) return hipSuccess;
+  if (num_groups > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   PagesArgs a;
   a.pt = page_table;
   a.pt_ld = pt_ld;

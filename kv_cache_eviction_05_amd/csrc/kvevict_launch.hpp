@@ -8,6 +8,16 @@
 
 namespace kvevict {
 
+// A launch holds fewer than 2^32 work-items in each grid dimension: the most workgroups of
+// `threads` threads that one dimension takes.  A launcher whose grid would not fit returns
+// hipErrorInvalidConfiguration before it enqueues anything.
+constexpr int64_t max_workgroups(int threads) { return 0xffffffffLL / threads; }
+// Workgroup sizes of launches whose grid grows with the lists or tokens of a call (the
+// kernels assert that they match), for callers that check a whole call before its first launch.
+constexpr int kGlobalThreads = 1024;   // global top-B: one workgroup per list (init) or item
+constexpr int kWeightedThreads = 512;  // weighted scores: one workgroup per tile of tokens
+constexpr int kWeightedTile = 64;      // tokens per tile
+
 hipError_t launch_score_random(float* scores, int64_t ld, int64_t num_lists, int32_t L, int32_t H,
                                int32_t n, int32_t prot, uint64_t seed, uint32_t round,
                                bool shared_draw, hipStream_t stream);

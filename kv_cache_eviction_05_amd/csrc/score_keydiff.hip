@@ -611,6 +611,7 @@ hipError_t launch_score_keydiff(float* scores, int64_t ld, const StoreView& keys
                                 int32_t D, int32_t H, int64_t num_lists, int32_t n, int32_t prot,
                                 hipStream_t stream) {
   if (num_lists == 0 || n == 0) return hipSuccess;
+  if (num_lists > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   KeydiffArgs a;
   a.scores = scores;
   a.ld = ld;

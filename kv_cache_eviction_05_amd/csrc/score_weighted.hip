@@ -49,6 +49,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTok = 64;                    // tokens per tile (= lanes)
+static_assert(kThreads == kWeightedThreads && kTok == kWeightedTile, "the grid checks");
 constexpr int kJW = 6;                      // GDN heads per wave per pass
 constexpr int kJPass = kWaves * kJW;        // GDN heads per pass
 constexpr int kHB = 4;                      // KV heads per launch
@@ -693,6 +694,7 @@ hipError_t launch_score_weighted(float* scores, int64_t ld, const float* beta, c
                                  int32_t Hg, int32_t n, int32_t prot, hipStream_t stream,
                                  uint32_t* hist0) {
   if (n == 0 || L == 0 || H == 0) return hipSuccess;
+  if ((n + kTok - 1) / kTok > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   const unsigned tiles = (unsigned)((n + kTok - 1) / kTok);
   const bool vec = sj == 1 && sg % 2 == 0 && st % 2 == 0 && Hg % 2 == 0 &&
                    (reinterpret_cast<uintptr_t>(beta) & 7u) == 0 &&

@@ -47,6 +47,7 @@ namespace kvevict {
 namespace {
 
 constexpr int kThreads = 1024;
+static_assert(kThreads == kGlobalThreads, "the grid checks of the fused call");
 constexpr int kBinsPerThread = 2048 / kThreads;
 static_assert(kBinsPerThread >= 1 && 2048 % kThreads == 0 && 1024 % kThreads == 0,
               "resolve: whole bins per thread");
@@ -730,6 +731,7 @@ hipError_t launch_select_global_init(int32_t* kept_idx, int64_t kept_ld, int32_t
                                      int64_t num_lists, int32_t n, int32_t prot, int64_t budget,
                                      void* workspace, hipStream_t stream) {
   if (num_lists == 0) return hipSuccess;
+  if (num_lists > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   const GlobalArgs a = global_args(kept_idx, kept_ld, kept_count, nullptr, n, num_lists, n, prot,
                                    budget, workspace);
   hipLaunchKernelGGL(global_init_kernel, dim3((unsigned)num_lists), dim3(kThreads), 0, stream, a);
@@ -741,6 +743,7 @@ hipError_t launch_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t* kep
                                 int32_t prot, int64_t budget, void* workspace,
                                 hipStream_t stream, bool first_level_done) {
   if (num_lists == 0) return hipSuccess;
+  if (num_lists > max_workgroups(kThreads)) return hipErrorInvalidConfiguration;
   const GlobalArgs a = global_args(kept_idx, kept_ld, kept_count, scores, ld, num_lists, n, prot,
                                    budget, workspace);
   hipError_t e;

@@ -108,6 +108,8 @@ hipError_t launch_select_topk(int32_t* kept_idx, int64_t kept_ld, int32_t* kept_
   a.H = H;
   for (int32_t l = 0; l < kMaxBudgetLayers; ++l) a.kk[l] = (layer_kk && l < L) ? layer_kk[l] : 0;
   const int32_t m = n - prot;
+  if (num_lists > max_workgroups(m <= kMaxLdsKeys ? kShortThreads : kBigThreads))
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);
@@ -227,6 +229,8 @@ hipError_t launch_draw_select(int32_t* kept_idx, int64_t kept_ld, int64_t num_li
   a.seed = seed;
   a.round = round;
   const int32_t m = n - prot;
+  if (num_lists > max_workgroups(m <= kMaxLdsKeys ? kShortThreads : kBigThreads))
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)num_lists);
   if (m <= kMaxLdsKeys) {
     const size_t lds = (size_t)(m > 0 ? m : 1) * sizeof(uint32_t);

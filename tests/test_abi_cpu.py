@@ -354,6 +354,8 @@ def test_score_keydiff_validation():
     assert st(d, 1088, 4, 1088, 1089) == B.KVEVICT_ERR_INVALID_ARG     # prot > n
     assert st(d, 1088, -1, 1088, 0) == B.KVEVICT_ERR_INVALID_ARG
     assert status("kvevict_score_keydiff", FAKE, 1088, None, FAKE, 4, 1088, 0, None) == B.KVEVICT_ERR_INVALID_ARG
+    d1 = B.contig_desc(128, 1, 1088)
+    assert st(d1, 1088, 1 << 23, 1088, 0) == B.KVEVICT_ERR_INVALID_ARG  # 2^23 lists: 2^32 work-items
 
 
 def test_compact_inplace_validation():
@@ -483,3 +485,46 @@ def test_sizes_whose_products_overflow_are_rejected():
     wrap = B.KvDesc(B.LAYOUT_CONTIG, D, H, 0, 1 << 60, 1 << 20, None, 0)
     assert status("kvevict_compact", ctypes.byref(wrap), FAKE, FAKE * 2, ctypes.byref(dst),
                   FAKE * 3, FAKE * 4, FAKE, 1024, None, 1024, 1, H, None, None) == INV
+
+
+def test_calls_too_large_for_one_grid_are_rejected():
+    """A launch holds fewer than 2^32 work-items per grid dimension.  Calls whose per-list or
+    per-tile grid would not fit are rejected with KVEVICT_ERR_INVALID_ARG before anything is
+    enqueued (the launcher returns before its first HIP call), each at the first size past its
+    limit: 2^25 lists of 128-thread workgroups, 2^22 of 1024, 2^24 of 256, 2^23 tiles of 512."""
+    INV = B.KVEVICT_ERR_INVALID_ARG
+    # per-head top-K: short lists take 128 threads, lists above 15,360 candidates 1024
+    assert status("kvevict_select_topk", FAKE, 16, FAKE, 16, 1 << 25, 16, 16, 0, None) == INV
+    assert status("kvevict_select_topk", FAKE, 16, FAKE, 20000, 1 << 22, 20000, 16, 0,
+                  None) == INV
+    # random draw + top-K: 2^25 short lists
+    assert status("kvevict_select_random", FAKE, 16, 1 << 25, 1, 1, 16, 16, 0, 0, 0, 0,
+                  None) == INV
+    # in-place compaction: 2^24 lists of 256 threads (K and V 1 TiB apart, 69 GB each)
+    c = B.contig_desc(128, 8, 16)
+    assert status("kvevict_compact_inplace", ctypes.byref(c), FAKE, FAKE * 2, FAKE * 3, 16, None,
+                  16, 16, 1 << 21, 8, None, None, None, None) == INV
+    # one-launch random round: 2^18 requests x 8 layers x 8 heads = 2^24 lists
+    assert status("kvevict_evict_random_inplace", ctypes.byref(c), FAKE, FAKE * 2, 1 << 18, 8, 16,
+                  16, 0, 0, 0, 0, FAKE * 5, 16, None, None, None, None) == INV
+    # page draw: 2^24 groups of 256 threads, one freed page each
+    assert status("kvevict_evict_pages_random", FAKE, 2, 16, 1 << 18, 64, 32, 16, 0, 0, 0, FAKE * 2,
+                  1, FAKE * 3, FAKE * 4, None) == INV
+    # weighted scores: 2^29 tokens make 2^23 tiles of 64 tokens, 512 threads each
+    n = 1 << 29
+    wb = (ctypes.c_int32 * 1)(0)
+    wc = (ctypes.c_int32 * 1)(6)
+    assert status("kvevict_score_weighted", FAKE, n, FAKE, FAKE, n * 4, 4, 1, FAKE, 6, wb, wc,
+                  1, 1, 12, 4, n, 0, None) == INV
+    size = ctypes.c_size_t(0)
+    assert status("kvevict_score_select_global", FAKE, n, FAKE, None, FAKE, n, FAKE, FAKE, n * 4,
+                  4, 1, FAKE, 6, wb, wc, 1, 1, 12, 4, n, 0, 0.25, None, ctypes.byref(size),
+                  None) == B.KVEVICT_OK  # the workspace query
+    assert status("kvevict_score_select_global", FAKE, n, FAKE, None, FAKE, n, FAKE, FAKE, n * 4,
+                  4, 1, FAKE, 6, wb, wc, 1, 1, 12, 4, n, 0, 0.25, FAKE, ctypes.byref(size),
+                  None) == INV
+    # global top-B: 2^22 lists of 256 candidates, one 1024-thread workgroup per list to start
+    lists = 1 << 22
+    size = ctypes.c_size_t(B.kvevict_select_global_workspace(lists, 256, 0, p=0.25))
+    assert status("kvevict_select_global", FAKE, 256, FAKE, None, FAKE, 256, lists, 256, 0, 0.25,
+                  FAKE, ctypes.byref(size), None) == INV
