@@ -10,8 +10,8 @@
 // Kept indices are strictly increasing, so idx[j] >= j: a row only moves
 // towards the front, and the unchanged prefix (idx[j] == j: the prompt and the
 // rows before the first eviction) is never touched.  Heads own disjoint
-// memory in both layouts, so one workgroup per (group, head) walks that head's
-// destination rows in increasing chunks.  Within a chunk a source row may also
+// memory in both layouts, so one workgroup per (group, head), head-major, walks
+// that head's destination rows in increasing chunks.  Within a chunk a source row may also
 // be a destination of the same chunk, so every thread waits for its loads
 // before a workgroup barrier and only then stores; a later chunk reads only
 // rows at or beyond its own first destination row, which no earlier chunk
@@ -92,9 +92,14 @@ __device__ int32_t first_moved(const int32_t* __restrict__ idx, int32_t c, int32
 template <bool kPaged>
 __global__ __launch_bounds__(kThreads) void compact_inplace_kernel(InplaceArgs a) {
   __shared__ int32_t s_min[kWaves];
+  // consecutive workgroups take one head of consecutive groups (head-major), so the
+  // workgroups in flight do not all move rows of the same groups' pages at once
+  // (same-process A/B against group-major: paged 3.917 -> 3.856 ms, the 30-round
+  // shape in one round 15.86 -> 15.62 ms)
   const int32_t H = a.H;
-  const int64_t g = blockIdx.x / H;
-  const int32_t h = (int32_t)(blockIdx.x - g * H);
+  const int64_t G = gridDim.x / H;
+  const int32_t h = (int32_t)(blockIdx.x / G);
+  const int64_t g = blockIdx.x - (int64_t)h * G;
   const int32_t tid = threadIdx.x;
   const int64_t il = g * a.ipg + (a.ipg == 1 ? 0 : h);
   const int32_t* __restrict__ idx = a.kept_idx + il * a.kept_ld;
