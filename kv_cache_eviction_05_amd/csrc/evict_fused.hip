@@ -5,7 +5,7 @@
 // Appendix G: kept entries move to the front of their own pages and the freed
 // tail blocks return to the pool).
 //
-// One 256-thread workgroup per (group, head).  It draws the n - prot
+// One 256-thread workgroup per (group, head), head-major.  It draws the n - prot
 // candidate scores of its list with the same Philox stream as the standalone
 // scorer straight into LDS keys, selects the K - prot largest (ties to the
 // lower position), writes the kept indices in increasing order into LDS (and,
@@ -48,8 +48,11 @@ __global__ __launch_bounds__(kThreads) void evict_random_inplace_kernel(FusedArg
   __shared__ SelectShared<kThreads> sh;
   __shared__ int32_t s_min[kWaves];
   const int32_t H = a.H, n = a.n, K = a.K, prot = a.prot;
-  const int64_t g = blockIdx.x / H;
-  const int32_t h = (int32_t)(blockIdx.x - g * H);
+  // head-major, as the standalone in-place compaction (same-process A/B against
+  // group-major: paged 3.895 -> 3.838 ms, the 30-round shape in one round 15.86 -> 15.57 ms)
+  const int64_t G = gridDim.x / H;
+  const int32_t h = (int32_t)(blockIdx.x / G);
+  const int64_t g = blockIdx.x - (int64_t)h * G;
   const int32_t tid = threadIdx.x;
   const int32_t m = n - prot, kk = K - prot;
   uint32_t* s_keys = s_dyn;
