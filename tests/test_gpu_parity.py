@@ -675,6 +675,38 @@ def assert_keydiff_close(got, keys, prot):
     return float(np.mean(same[fin])) if fin.any() else 1.0
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # the oracle's inf - inf
+@pytest.mark.parametrize("n,D,cap", [
+    (300, 128, 300),    # the whole list on chip
+    (1500, 128, 1500),  # 640 rows on chip, the rest streamed twice
+    (300, 64, 320),     # the generic lane reduction
+])
+def test_score_keydiff_non_finite(n, D, cap):
+    """Non-finite keys follow the oracle's binary64 arithmetic: a NaN element makes the list's
+    mean NaN and every cosine 0 (den > 0 fails), so every score is +0; an infinite element
+    makes the mean infinite and the scores NaN, except a zero key's (+0); +inf and -inf in one
+    column make the mean NaN again.  NaN positions must match the oracle's exactly."""
+    say(f"score_keydiff non-finite n={n} D={D}")
+    H, prot = 4, 3
+    keys = rand_keys((H, cap, D), seed=n + D)
+    keys[0, 17, 5] = 0x7FC0                          # NaN
+    keys[1, 9, 3] = 0x7F80                           # +inf
+    keys[1, 11] = 0                                  # a zero key next to it
+    keys[2, 20, 7], keys[2, 40, 7] = 0x7F80, 0xFF80  # +inf and -inf in one column
+    ld = n + 1
+    s = torch.full((H, ld), 7.0, dtype=torch.float32, device=DEV)
+    B.kvevict_score_keydiff(s, ld, B.contig_desc(D, H, cap), bf16_from_bits(keys), 1, n, prot)
+    torch.cuda.synchronize()
+    got = to_np(s)[:, :n]
+    want = oracle.score_keydiff(np.ascontiguousarray(keys[:, :n]), prot)
+    assert np.all(np.isposinf(got[:, :prot]))
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.all(got[0, prot:] == 0) and not np.signbit(got[0, prot:]).any()
+    assert np.isnan(got[1, prot:]).sum() == n - prot - 1 and got[1, 11] == 0
+    assert np.all(got[2, prot:] == 0)
+    assert_keydiff_close(got[3:], keys[3:, :n], prot)  # the ordinary list
+
+
 @pytest.mark.parametrize("groups,H,n,D,prot,cap", [
     (3, 4, 1088, 128, 128, 1088),   # the batch shape
     (2, 3, 777, 256, 5, 800),       # ragged, padded rows, D = 256
