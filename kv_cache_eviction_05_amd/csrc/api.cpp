@@ -330,6 +330,7 @@ kvevict_status kvevict_select_global(int32_t* kept_idx, int64_t kept_ld, int32_t
                                          workspace, workspace_bytes, &budget, &launch);
   if (st != KVEVICT_OK || !launch) return st;
   if (num_lists > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
+  if (num_lists > kvevict::max_workgroups(kvevict::kGlobalThreads)) return KVEVICT_ERR_INVALID_ARG;
   if (budget_out) *budget_out = budget;
   return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
                                                   num_lists, n, prot, budget, workspace, stream));
@@ -355,6 +356,7 @@ kvevict_status kvevict_select_global_noalloc(int32_t* kept_idx, int64_t kept_ld,
                     &budget, &launch);
   if (st != KVEVICT_OK || !launch) return st;
   if (num_lists > 0 && !scores) return KVEVICT_ERR_INVALID_ARG;
+  if (num_lists > kvevict::max_workgroups(kvevict::kGlobalThreads)) return KVEVICT_ERR_INVALID_ARG;
   if (budget_out) *budget_out = budget;
   return hip_status(kvevict::launch_select_global(kept_idx, kept_ld, kept_count, scores, ld,
                                                   num_lists, n, prot, budget, ws, stream));
@@ -378,12 +380,13 @@ kvevict_status kvevict_score_select_global(
   st = check_global(kept_idx, kept_ld, kept_count, ld, num_lists, n, prot, p, workspace,
                     workspace_bytes, &budget, &launch);
   if (st != KVEVICT_OK || !launch) return st;
-  if (budget_out) *budget_out = budget;
-  // every launch of the call fits its grid before the first is enqueued
+  // every launch of the call fits its grid before the first is enqueued (and before any
+  // output is written)
   if (num_lists > kvevict::max_workgroups(kvevict::kGlobalThreads) ||
       (n + kvevict::kWeightedTile - 1) / kvevict::kWeightedTile >
           kvevict::max_workgroups(kvevict::kWeightedThreads))
     return KVEVICT_ERR_INVALID_ARG;
+  if (budget_out) *budget_out = budget;
   // prompts and cleared workspace, then the scores with the first radix level
   // added by the scorer, then the rest of the select
   hipError_t e = kvevict::launch_select_global_init(kept_idx, kept_ld, kept_count, num_lists, n,

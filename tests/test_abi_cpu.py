@@ -520,11 +520,14 @@ def test_calls_too_large_for_one_grid_are_rejected():
     assert status("kvevict_score_select_global", FAKE, n, FAKE, None, FAKE, n, FAKE, FAKE, n * 4,
                   4, 1, FAKE, 6, wb, wc, 1, 1, 12, 4, n, 0, 0.25, None, ctypes.byref(size),
                   None) == B.KVEVICT_OK  # the workspace query
-    assert status("kvevict_score_select_global", FAKE, n, FAKE, None, FAKE, n, FAKE, FAKE, n * 4,
-                  4, 1, FAKE, 6, wb, wc, 1, 1, 12, 4, n, 0, 0.25, FAKE, ctypes.byref(size),
-                  None) == INV
+    budget = ctypes.c_int64(-7)  # an output: untouched by a rejected call
+    assert status("kvevict_score_select_global", FAKE, n, FAKE, ctypes.byref(budget), FAKE, n,
+                  FAKE, FAKE, n * 4, 4, 1, FAKE, 6, wb, wc, 1, 1, 12, 4, n, 0, 0.25, FAKE,
+                  ctypes.byref(size), None) == INV
+    assert budget.value == -7
     # global top-B: 2^22 lists of 256 candidates, one 1024-thread workgroup per list to start
     lists = 1 << 22
     size = ctypes.c_size_t(B.kvevict_select_global_workspace(lists, 256, 0, p=0.25))
-    assert status("kvevict_select_global", FAKE, 256, FAKE, None, FAKE, 256, lists, 256, 0, 0.25,
-                  FAKE, ctypes.byref(size), None) == INV
+    assert status("kvevict_select_global", FAKE, 256, FAKE, ctypes.byref(budget), FAKE, 256, lists,
+                  256, 0, 0.25, FAKE, ctypes.byref(size), None) == INV
+    assert budget.value == -7
