@@ -417,6 +417,34 @@ def paged_copy_ceiling(torch, binding, st, cfg, gather_gbps, reps=5):
     return out
 
 
+def contig_copy_ceiling(torch, binding, st, gather_gbps, reps=10):
+    """A plain copy of the gather's bytes between the same K and V stores: the leading
+    kv_bytes / 4 bytes of each source store copied whole to its destination store in 32 KiB
+    pieces with kvevict_copy_pages (identity piece lists), so that reads and writes are
+    contiguous.  The ceiling for a gather of this many bytes, launch ramp and drain included;
+    the gather's scattered rows can approach it but not pass it.  Overwrites the destination."""
+    piece = 32 << 10
+    count = st.kv_bytes_moved() // 4 // piece
+    ids = torch.arange(count, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moved = 4 * count * piece  # K and V, read and written
+    run = lambda: binding.kvevict_copy_pages(st.k_src, st.v_src, ids, st.k_dst, st.v_dst, ids,
+                                             piece, err)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = moved / (ms * 1e-3) / 1e9
+    return {"bytes_moved": moved, "ms": round(ms, 4), "gbps": gbps,
+            "frac_of_peak": gbps / PEAK_HBM_GBPS, "gather_vs_copy": gather_gbps / gbps,
+            "bad_pages": int(err.item())}
+
+
 def cpu_baseline(torch, cfg, st, seconds):
     """The oracle timed on the host cores over a bounded sample of the same workload."""
     import numpy as np
@@ -649,6 +677,11 @@ def measure(torch, binding, configs, rounds, name, args, headline):
         if cfg.layout == "paged" and not (cfg.inplace or cfg.page_draw):
             # last: the copy overwrites the round's destination pages
             entry["page_copy_ceiling"] = paged_copy_ceiling(torch, binding, st, cfg, achieved)
+        if cfg.select in ("global", "layers") and cfg.layout == "contig" and not cfg.inplace:
+            # two same-size copies as the gather's ceiling: torch's device copy, and
+            # (last: it overwrites the round's destination rows) the library's page copy
+            entry["dtod_copy"] = dtod_copy(torch, r["kv_bytes"], achieved)
+            entry["copy_ceiling"] = contig_copy_ceiling(torch, binding, st, achieved)
     del r["state"], st
     r.clear()
     torch.cuda.synchronize()
