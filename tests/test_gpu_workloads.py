@@ -13,6 +13,7 @@ import gc
 import math
 import os
 import sys
+import types
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -70,6 +71,22 @@ def oracle_keep_sets(cfg, round_id, K=None, n=None):
         l1 = min(lists, l0 + step)
         sc = oracle.score_random(cfg.L, cfg.H, n, cfg.prot, cfg.seed, round_id, cfg.shared, l0, l1)
         out[l0:l1] = oracle.select_topk(sc, K, cfg.prot)
+
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        list(ex.map(part, range(0, lists, step)))
+    return out
+
+
+def oracle_select_all(scores, K, prot):
+    """The oracle's top-K int32 [lists][K] of the given scores [lists][n], list ranges spread
+    over the host threads."""
+    lists = scores.shape[0]
+    out = np.empty((lists, K), np.int32)
+    step = max(64, -(-lists // (4 * THREADS)))
+
+    def part(l0):
+        l1 = min(lists, l0 + step)
+        out[l0:l1] = oracle.select_topk(np.ascontiguousarray(scores[l0:l1]), K, prot)
 
     with ThreadPoolExecutor(max_workers=THREADS) as ex:
         list(ex.map(part, range(0, lists, step)))
@@ -399,9 +416,11 @@ def test_longgen_rounds_replayed_by_oracle():
     free()
 
 
-def test_paged_shared_max_round_sampled():
+def test_paged_shared_max_round_full():
     """Paged round with one list per (request, layer) by the max of the per-head scores and a
-    kept count rounded down to a multiple of four: sampled groups against the oracle."""
+    kept count rounded down to a multiple of four: every group's shared scores and keep set
+    against the oracle's, every group's destination pages against a page walk of the source
+    through the oracle's indices."""
     cfg = configs.PAGED_SHARED_MAX
     say("paged shared-max round: allocating")
     st = rounds.make_state(cfg, DEV)
@@ -410,27 +429,26 @@ def test_paged_shared_max_round_sampled():
     assert int(st.errors.item()) == 0
     K4 = cfg.kept_shared
     assert K4 % 4 == 0 and K4 == oracle.shared_kept_count(cfg.K, cfg.prot)
-    check_kept_properties(st.kept, K4, cfg.prot, cfg.n)
-    ps, H, D = cfg.page_size, cfg.H, cfg.D
-    src_pt, dst_pt = st.src_pt.cpu().numpy(), st.dst_pt.cpu().numpy()
-    for g in sample_lists(cfg.groups, 8, seed=5):
-        heads = oracle.score_random(cfg.L, H, cfg.n, cfg.prot, cfg.seed, 5, False, g * H, g * H + H)
+    H, groups = cfg.H, cfg.groups
+    got_s = st.scores[:groups].cpu().numpy()
+    want_k = np.empty((groups, K4), np.int32)
+    bad = []
+    step = max(16, -(-groups // (4 * THREADS)))
+
+    def part(g0):
+        g1 = min(groups, g0 + step)
+        heads = oracle.score_random(cfg.L, H, cfg.n, cfg.prot, cfg.seed, 5, False, g0 * H, g1 * H)
         want_s = oracle.shared_max_scores(heads, H)
-        assert np.array_equal(st.scores[g:g + 1].cpu().numpy(), want_s), g
-        want_k = oracle.select_topk(want_s, K4, cfg.prot)
-        assert np.array_equal(st.kept[g:g + 1, :K4].cpu().numpy(), want_k), g
-        sp = torch.from_numpy(src_pt[g].astype(np.int64)).to(DEV)
-        dp = torch.from_numpy(dst_pt[g].astype(np.int64)).to(DEV)
-        ks, vs = u16(st.k_src[sp]), u16(st.v_src[sp])
-        pt_s = np.arange(len(src_pt[g]), dtype=np.int32)[None, :]
-        pt_d = np.arange(len(dst_pt[g]), dtype=np.int32)[None, :]
-        kd = np.zeros((len(dst_pt[g]), ps, H, D), np.uint16)
-        vd = np.zeros_like(kd)
-        oracle.compact({"paged": True, "page_table": pt_s}, ks, vs,
-                       {"paged": True, "page_table": pt_d}, kd, vd, want_k, K4, D, H, 0, 1,
-                       ipg=1, page_size=ps)
-        assert np.array_equal(u16(st.k_dst[dp]), kd), g
-        assert np.array_equal(u16(st.v_dst[dp]), vd), g
+        if not np.array_equal(got_s[g0:g1], want_s):
+            bad.append(g0)
+        want_k[g0:g1] = oracle.select_topk(want_s, K4, cfg.prot)
+
+    say(f"paged shared-max round: the oracle's scores and keep sets of all {groups} groups")
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        list(ex.map(part, range(0, groups, step)))
+    assert not bad, f"shared scores differ in the group ranges starting at {sorted(bad)[:4]}"
+    assert_keep_sets(st.kept[:, :K4], want_k, cfg.name)
+    check_paged_gather(st, cfg, want_k, K4)
     del st
     free()
 
@@ -483,57 +501,58 @@ def test_layers_round():
     free()
 
 
-def test_keydiff_round_sampled():
-    """The batch round scored by KeyDiff: sampled lists against the oracle's scores (the stated
-    precision: the oracle's fp32 rounding, or its neighbour next to a midpoint), selection given
-    the GPU's scores, and the whole gather."""
+def test_keydiff_round():
+    """The batch round scored by KeyDiff: every list's keep set against the oracle's top-K of
+    the GPU's scores (selection bit-exact given identical scores) and every compacted row
+    against a gather through those oracle indices; the scores themselves on 60 sampled lists
+    against the oracle's (the stated precision: the oracle's fp32 rounding, or its neighbour
+    next to a midpoint), since the oracle's plain per-row loop would take minutes for all."""
     cfg = configs.KEYDIFF
     say("keydiff round: allocating")
     st = rounds.make_state(cfg, DEV)
     rounds.run_round(st)
     torch.cuda.synchronize()
     assert int(st.errors.item()) == 0
-    check_kept_properties(st.kept, cfg.K, cfg.prot, cfg.n)
-    check_contig_gather(st, cfg.K)
     got_s = st.scores.cpu().numpy()
-    for l in sample_lists(cfg.lists, 12, seed=8):
+    say(f"keydiff round: the oracle's top-K of all {cfg.lists} lists' scores")
+    want_k = oracle_select_all(got_s, cfg.K, cfg.prot)
+    assert_keep_sets(st.kept, want_k, cfg.name)
+    check_contig_gather(st, cfg.K, kept=want_k)
+    del want_k
+    say("keydiff round: sampled scores against the oracle's")
+    for l in sample_lists(cfg.lists, 60, seed=8):
         assert_keydiff_close(got_s[l:l + 1], u16(st.k_src[l:l + 1]), cfg.prot)
-        assert np.array_equal(st.kept[l].cpu().numpy(),
-                              oracle.select_topk(got_s[l:l + 1], cfg.K, cfg.prot)[0]), l
     del st
     free()
 
 
 @pytest.mark.parametrize("base", [configs.PAGED_INPLACE, configs.PAGED_FUSED], ids=lambda c: c.name)
-def test_paged_inplace_round_sampled(base):
-    """Paged round compacted in place (three launches, or the one-launch fused round): on
-    sampled groups every head's first K rows are the kept rows of the cache before the round and
-    the rows past K are untouched; every group returns its 4 tail pages (132 -> 128) and the
-    free list holds exactly those pages."""
+def test_paged_inplace_round_full(base):
+    """Paged round compacted in place (three launches, or the one-launch fused round): every
+    keep set against the oracle's; for every group and head, the first K rows walked through
+    the group's own page table equal the rows of the cache before the round at the oracle's
+    indices, and every tail page (rows past K) is untouched; every group returns its 4 tail
+    pages (132 -> 128) and the free list holds exactly those pages."""
     cfg = base
     say(f"{cfg.name} round: allocating")
     st = rounds.make_state(cfg, DEV)
-    ps, H, D, n, K = cfg.page_size, cfg.H, cfg.D, cfg.n, cfg.K
-    pt = st.src_pt.cpu().numpy()
-    samples = sample_lists(cfg.groups, 6, seed=2)
-    before = {g: (u16(st.k_src[torch.from_numpy(pt[g].astype(np.int64)).to(DEV)]),
-                  u16(st.v_src[torch.from_numpy(pt[g].astype(np.int64)).to(DEV)])) for g in samples}
+    ps, n, K = cfg.page_size, cfg.n, cfg.K
+    k0, v0 = st.k_src.clone(), st.v_src.clone()  # the cache before the round
     rounds.run_round(st, round_id=1)
     torch.cuda.synchronize()
     assert int(st.errors.item()) == 0
-    check_kept_properties(st.kept, K, cfg.prot, n)
-    kept = st.kept.cpu().numpy()
-    for g in samples:
-        idx_pages = torch.from_numpy(pt[g].astype(np.int64)).to(DEV)
-        ak, av = u16(st.k_src[idx_pages]), u16(st.v_src[idx_pages])
-        bk, bv = before[g]
-        # [pages][16][H][D] -> [H][rows][D]
-        rows = lambda a: a.reshape(-1, H, D).transpose(1, 0, 2)[:, :n]
-        for h in range(H):
-            idx = kept[g * H + h]
-            assert np.array_equal(rows(ak)[h, :K], rows(bk)[h, idx]), (g, h)
-            assert np.array_equal(rows(av)[h, :K], rows(bv)[h, idx]), (g, h)
-            assert np.array_equal(rows(ak)[h, K:], rows(bk)[h, K:]), (g, h)
+    say(f"{cfg.name} round: the oracle's keep sets of all {cfg.lists} lists")
+    want = oracle_keep_sets(cfg, 1)
+    assert_keep_sets(st.kept, want, cfg.name)
+    say(f"{cfg.name} round: every group's moved rows and tail pages")
+    before = types.SimpleNamespace(k_src=k0, v_src=v0, k_dst=st.k_src, v_dst=st.v_src,
+                                   src_pt=st.src_pt, dst_pt=st.src_pt)
+    check_paged_gather(before, cfg, want, K)
+    del want
+    tail = st.src_pt[:, K // ps:].reshape(-1).long()
+    assert torch.equal(st.k_src[tail], k0[tail]) and torch.equal(st.v_src[tail], v0[tail])
+    del k0, v0, before
+    pt = st.src_pt.cpu().numpy()
     nf = int(st.freed_count.item())
     assert nf == cfg.groups * (-(-n // ps) - K // ps) == cfg.groups * 4
     assert sorted(st.freed[:nf].cpu().tolist()) == sorted(pt[:, K // ps:].reshape(-1).tolist())
