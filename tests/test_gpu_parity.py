@@ -723,6 +723,8 @@ def test_score_keydiff_non_finite(n, D, cap):
     (1, 2, 609, 128, 4, 640),       # padded rows past n in the store
     (2, 3, 1088, 128, 0, 1100),     # exactly the 68 steps held on chip, padded store
     (1, 2, 17, 128, 0, 17),         # two steps, one of them a single row
+    (1, 2, 16, 128, 0, 16),         # exactly one step
+    (2, 2, 5, 128, 2, 9),           # one partial step, padded store
     (1, 2, 300, 128, 300, 300),     # every slot protected
     (1, 2, 1000, 128, 999, 1000),   # every slot but the last protected
     # D = 128, n > 1088: 640 rows on chip, the rest streamed in batches of 256 rows
