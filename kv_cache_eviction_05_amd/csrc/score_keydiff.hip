@@ -40,7 +40,7 @@
 // (score_keydiff_resident_kernel, below) that holds the whole list on chip at two waves
 // per SIMD and so reads every key once: 2.00-2.03 ms against 2.10-2.15 ms on the batch
 // in a same-process A/B, bit-identical scores.  It is bound by binary64 issue as much as
-// by the reads (about 65% VALU busy, 19% of wave time waiting on memory); requesting the
+// by the reads (about 65% VALU busy, 20% of wave time waiting on memory); requesting the
 // next list's rows behind pass 2, in a persistent form, measured the same.
 #include <cmath>
 
