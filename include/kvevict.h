@@ -33,7 +33,9 @@
  * Conventions shared by every entry point:
  *   - Pointers marked "device" are device memory owned by the caller; the
  *     library allocates nothing, frees nothing and keeps no state between
- *     calls.  Host arrays are read during the call only.
+ *     calls, apart from kvevict_select_global_noalloc's static per-GPU array
+ *     and the address of it that the first call on each device looks up.
+ *     Host arrays are read during the call only.
  *   - All work is enqueued on `stream` (NULL = the default stream); nothing is
  *     synchronised; outputs are valid once the stream reaches that point.
  *   - Arguments are validated on the host before anything is enqueued; on an
