@@ -85,3 +85,38 @@ def test_noalloc_rejects_more_than_the_array_holds():
     assert e.value.status == B.KVEVICT_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((kept == -3).all()) and bool((counts == -1).all())
+
+
+def test_noalloc_replays_from_a_graph():
+    """The call recorded in a HIP graph (the use it is for) and replayed three times, each
+    replay after the outputs were cleared and after an eager call on other inputs had left the
+    static array dirty: every replay equals the eager result bit for bit."""
+    lists, n, prot, p = 64, 32768, 256, 0.25
+    s = scores_of("normal", lists, n, prot, seed=91)
+    scores = torch.from_numpy(s).to(DEV)
+    other = torch.from_numpy(scores_of("ties", 5, 9000, 100, seed=92)).to(DEV)
+    o_kept = torch.empty((5, 9000), dtype=torch.int32, device=DEV)
+    o_counts = torch.empty((5,), dtype=torch.int32, device=DEV)
+    say("select_global_noalloc graph: eager reference")
+    kept_e = torch.full((lists, n), -3, dtype=torch.int32, device=DEV)
+    counts_e = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    budget = B.kvevict_select_global_noalloc(kept_e, n, counts_e, scores, n, lists, n, prot, p)
+    torch.cuda.synchronize()
+    kept = torch.full((lists, n), -3, dtype=torch.int32, device=DEV)
+    counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    say("select_global_noalloc graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b = B.kvevict_select_global_noalloc(kept, n, counts, scores, n, lists, n, prot, p)
+    assert b == budget
+    for rep in range(3):
+        say(f"select_global_noalloc graph: replay {rep}")
+        kept.fill_(-3)
+        counts.fill_(-1)
+        B.kvevict_select_global_noalloc(o_kept, 9000, o_counts, other, 9000, 5, 9000, 100, 0.3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(counts, counts_e), rep
+        assert torch.equal(kept, kept_e), rep
+    assert int(counts_e.sum()) == lists * prot + budget
