@@ -112,6 +112,36 @@ def test_random_select_global(case):
         assert np.all(got[l, c:] == -3), l
 
 
+@pytest.mark.parametrize("case", cases(4))
+def test_random_select_global_many_items(case):
+    """Calls of 16 to 768 items (runs of up to 8,192 candidates): the two-level flow up to 256
+    items and the three-level one above, on random lengths, prompts, fractions and scores."""
+    rng = case_rng(case, 13)
+    lists = int(rng.integers(8, 65))
+    n = int(rng.integers(2 * 8192, 12 * 8192))
+    prot = int(rng.integers(0, 300))
+    p = float(rng.choice([0.05, 0.25, 0.5, 0.9]))
+    kind = KINDS[case % len(KINDS)]
+    say(f"random select_global many items case={case} lists={lists} n={n} prot={prot} p={p} "
+        f"kind={kind}")
+    s = make_scores(kind, lists, n, seed=900 + case)
+    kept = torch.full((lists, n), -3, dtype=torch.int32, device=DEV)
+    counts = torch.full((lists,), -1, dtype=torch.int32, device=DEV)
+    wsb = B.kvevict_select_global_workspace(lists, n, prot, p=p)
+    ws = torch.full((max(wsb, 256),), 0x5A, dtype=torch.uint8, device=DEV)
+    budget = B.kvevict_select_global(kept, n, counts, torch.from_numpy(s).to(DEV), n, lists, n,
+                                     prot, p, ws, wsb)
+    torch.cuda.synchronize()
+    want_kept, want_counts, want_B = oracle.select_global(s, prot, p)
+    assert budget == want_B
+    got_counts, got = to_np(counts), to_np(kept)
+    assert np.array_equal(got_counts, want_counts)
+    for l in range(lists):
+        c = want_counts[l]
+        assert np.array_equal(got[l, :c], want_kept[l, :c]), l
+        assert np.all(got[l, c:] == -3), l
+
+
 @pytest.mark.parametrize("case", cases(12))
 def test_random_compact(case):
     rng = case_rng(case, 4)
