@@ -189,6 +189,77 @@ def test_random_compact(case):
     assert int(err.item()) == 0
 
 
+@pytest.mark.parametrize("case", cases(8))
+def test_random_compact_ordered(case):
+    """kvevict_compact_ordered against kvevict_compact (bit for bit, error count included) and
+    the oracle: paged destinations of 16-token pages whose rows hold 1024 elements (the
+    physical-order walk) or not (its fallback), pools from one to five times the pages written,
+    per-head or shared lists, per-list counts, now and then a page id outside the pool."""
+    rng = case_rng(case, 14)
+    ps = 16
+    H, D = [(8, 128), (4, 256), (16, 64), (2, 512), (8, 64), (3, 40)][int(rng.integers(0, 6))]
+    groups = int(rng.integers(1, 13))
+    n = int(rng.integers(1, 2200))
+    prot, K = draw_prot_k(rng, n)
+    K = max(K, 1)
+    src_paged = bool(rng.random() < 0.7)
+    shared = bool(rng.random() < 0.3)
+    variable = bool(rng.random() < 0.4)
+    bad_page = bool(rng.random() < 0.15)
+    slack = float(rng.choice([1.0, 1.5, 2.0, 3.0, 5.0]))
+    ipg = 1 if shared else H
+    idx_lists = groups * ipg
+    say(f"random compact_ordered case={case} groups={groups} H={H} D={D} n={n} K={K} "
+        f"prot={min(prot, K)} src_paged={src_paged} shared={shared} variable={variable} "
+        f"slack={slack} bad_page={bad_page}")
+    kept = oracle.select_topk(rng.random((idx_lists, n), dtype=np.float32), K, min(prot, K))
+    counts = rng.integers(0, K + 1, idx_lists).astype(np.int32) if variable else None
+    if src_paged:
+        sp = -(-n // ps)
+        pool_s = groups * sp + int(rng.integers(0, 5))
+        pt_s = rng.permutation(pool_s)[:groups * sp].reshape(groups, sp).astype(np.int32)
+        ks = rand_bits((pool_s, ps, H, D), 60 + case)
+        sdesc = B.paged_desc(D, H, ps, pool_s, torch.from_numpy(pt_s).to(DEV))
+        so = {"paged": True, "page_table": pt_s}
+    else:
+        ks = rand_bits((groups * H, n, D), 60 + case)
+        sdesc, so = B.contig_desc(D, H, n), {"list_stride": n * D}
+    vs = rand_bits(ks.shape, 61 + case)
+    dp = -(-K // ps)
+    pool_d = int(groups * dp * slack) + int(rng.integers(0, 3))
+    pt_d = rng.permutation(pool_d)[:groups * dp].reshape(groups, dp).astype(np.int32)
+    if bad_page:
+        pt_d[int(rng.integers(0, groups)), int(rng.integers(0, dp))] = pool_d + 1
+    kd0 = rand_bits((pool_d, ps, H, D), 62 + case)
+    vd0 = rand_bits(kd0.shape, 63 + case)
+    ddesc = B.paged_desc(D, H, ps, pool_d, torch.from_numpy(pt_d).to(DEV))
+    kept_t = torch.from_numpy(kept).to(DEV)
+    count_t = torch.from_numpy(counts).to(DEV) if variable else None
+    wsb = B.kvevict_compact_ordered_workspace(ddesc)
+    ws = torch.full((max(wsb, 256),), 0x7E, dtype=torch.uint8, device=DEV)
+    outs = []
+    for ordered in (False, True):
+        k_dst, v_dst = bf16_from_bits(kd0), bf16_from_bits(vd0)
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        args = (sdesc, bf16_from_bits(ks), bf16_from_bits(vs), ddesc, k_dst, v_dst, kept_t, K,
+                count_t, K, groups, ipg)
+        if ordered:
+            B.kvevict_compact_ordered(*args, ws, wsb, err)
+        else:
+            B.kvevict_compact(*args, err)
+        torch.cuda.synchronize()
+        outs.append((u16(k_dst), u16(v_dst), int(err.item())))
+    assert np.array_equal(outs[1][0], outs[0][0]) and np.array_equal(outs[1][1], outs[0][1])
+    assert outs[1][2] == outs[0][2]
+    if bad_page:
+        return
+    assert outs[0][2] == 0
+    kd, vd = kd0.copy(), vd0.copy()
+    oracle.compact(so, ks, vs, {"paged": True, "page_table": pt_d}, kd, vd, kept, K, D, H, 0,
+                   groups, ipg=ipg, kept_count=counts, page_size=ps)
+    assert np.array_equal(outs[1][0], kd) and np.array_equal(outs[1][1], vd)
+
+
 @pytest.mark.parametrize("case", cases(10))
 def test_random_evict_random_inplace(case):
     rng = case_rng(case, 5)
