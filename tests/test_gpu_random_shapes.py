@@ -358,6 +358,29 @@ def test_random_score_keydiff(case):
     assert_keydiff_close(got[:, :n], keys[:, :n], prot)
 
 
+@pytest.mark.parametrize("case", cases(6))
+def test_random_score_keydiff_whole_list(case):
+    """D = 128 and at most 1088 keys in a contiguous store: the kernel that holds the whole
+    list on chip, on random lengths (steps of 16 rows, whole, partial or skipped), padded
+    stores and prompts."""
+    rng = case_rng(case, 15)
+    groups, H = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+    n = int(rng.integers(1, 1089))
+    cap = n + int(rng.integers(0, 40))
+    prot = int(rng.integers(0, n + 1)) if rng.random() < 0.6 else 0
+    lists = groups * H
+    say(f"random score_keydiff whole list case={case} groups={groups} H={H} n={n} cap={cap} "
+        f"prot={prot}")
+    keys = rand_keys((lists, cap, 128), seed=800 + case)
+    s = torch.full((lists, n + 1), float("nan"), dtype=torch.float32, device=DEV)
+    B.kvevict_score_keydiff(s, n + 1, B.contig_desc(128, H, cap), bf16_from_bits(keys), groups,
+                            n, prot)
+    torch.cuda.synchronize()
+    got = to_np(s)
+    assert np.all(np.isnan(got[:, n:]))
+    assert_keydiff_close(got[:, :n], keys[:, :n], prot)
+
+
 @pytest.mark.parametrize("case", cases(8))
 def test_random_select_topk_layers(case):
     rng = case_rng(case, 9)
