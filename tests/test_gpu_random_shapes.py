@@ -19,6 +19,7 @@ import torch
 import oracle
 from kv_cache_eviction_05_amd import binding as B
 from kv_cache_eviction_05_amd.configs import gdn_windows
+from test_gpu_parity import test_score_select_global as fused_score_select_check
 from test_gpu_parity import (assert_keydiff_close, assert_weighted_close, bf16_from_bits,
                              check_inplace, keep_sets, make_scores, make_store, rand_bits,
                              rand_keys, say, to_np, u16)
@@ -140,6 +141,22 @@ def test_random_select_global_many_items(case):
         c = want_counts[l]
         assert np.array_equal(got[l, :c], want_kept[l, :c]), l
         assert np.all(got[l, c:] == -3), l
+
+
+@pytest.mark.parametrize("case", cases(6))
+def test_random_score_select_global(case):
+    """The fused weighted score + global top-B on random model shapes: bit for bit the two
+    calls it replaces, and the oracle's top-B of those scores."""
+    rng = case_rng(case, 16)
+    L = int(rng.integers(1, 21))
+    G = 3 * L
+    H = int(rng.integers(1, 7))
+    Hg = int(rng.choice([4, 8, 16, 48, 70]))
+    n = int(rng.integers(1, max(2, min(40000, 8_000_000 // (G * Hg)))))
+    prot = int(rng.integers(0, min(n, 300) + 1))
+    width = int(rng.choice([4, 6]))
+    p = float(np.round(rng.random(), 3))
+    fused_score_select_check(G, L, H, Hg, n, prot, width, p)
 
 
 @pytest.mark.parametrize("case", cases(12))
