@@ -73,6 +73,27 @@ def test_noalloc_matches_workspace_call(calls):
         assert int(c1.sum()) == lists * prot + b1
 
 
+def test_noalloc_random_sequence():
+    """Twelve calls in a row of random sizes (1 to 96 lists, up to 70,000 candidates, both the
+    two-level and the three-level flow, ties and special values), each equal to the workspace
+    call: whatever the previous call left in the static array, the next one clears what it
+    relies on."""
+    rng = np.random.default_rng(2024)
+    for i in range(12):
+        lists = int(rng.integers(1, 97))
+        n = int(rng.integers(1, max(2, min(70000, 4_000_000 // lists))))
+        prot = int(rng.integers(0, min(n, 400) + 1))
+        p = float(rng.choice([0.0, 0.1, 0.25, 0.5, 0.9, 1.0]))
+        kind = str(rng.choice(["uniform", "ties", "normal"]))
+        say(f"select_global_noalloc random call {i}: lists={lists} n={n} prot={prot} p={p} "
+            f"kind={kind}")
+        s = scores_of(kind, lists, n, prot, seed=3000 + i)
+        (b1, c1, k1), (b2, c2, k2) = both(s, prot, p)
+        assert b1 == b2, i
+        assert np.array_equal(c1, c2), i
+        assert np.array_equal(k1, k2), i
+
+
 def test_noalloc_rejects_more_than_the_array_holds():
     """A call whose workspace would exceed the static array returns KVEVICT_ERR_WORKSPACE and
     leaves its outputs untouched."""
