@@ -43,3 +43,24 @@ def test_global_round_counts_the_kept_rows():
     skew[0] += 5000
     skew[1] -= 5000
     assert credited(cfg, skew) == 1_098_907_648
+
+
+def test_in_place_rounds_count_only_the_rows_that_move():
+    # a row moves when its kept index differs from its slot; the prompt and the unchanged
+    # prefix stay.  One request of the in-place paged shape: 288 lists, K = 2048
+    cfg = configs.PAGED_INPLACE.small(R=1)
+    lists, K, n = cfg.lists, cfg.K, cfg.n
+    g = torch.Generator().manual_seed(5)
+    kept = torch.empty((lists, K), dtype=torch.int32)
+    moved = 0
+    for lst in range(lists):
+        stay = int(torch.randint(cfg.prot, K + 1, (1,), generator=g))  # slots [0, stay) stay
+        tail = torch.randperm(n - stay, generator=g)[:K - stay].sort().values + stay
+        kept[lst, :stay] = torch.arange(stay, dtype=torch.int32)
+        kept[lst, stay:] = tail.to(torch.int32)
+        moved += int((kept[lst] != torch.arange(K, dtype=torch.int32)).sum())
+    st = types.SimpleNamespace(cfg=cfg, kept=kept)
+    assert rounds.RoundState.kv_bytes_moved(st) == moved * 256 * 2 * 2
+    # nothing moves when every list keeps its first K slots
+    st.kept = torch.arange(K, dtype=torch.int32).repeat(lists, 1)
+    assert rounds.RoundState.kv_bytes_moved(st) == 0
