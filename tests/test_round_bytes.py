@@ -64,3 +64,23 @@ def test_in_place_rounds_count_only_the_rows_that_move():
     # nothing moves when every list keeps its first K slots
     st.kept = torch.arange(K, dtype=torch.int32).repeat(lists, 1)
     assert rounds.RoundState.kv_bytes_moved(st) == 0
+
+
+def test_scorer_inputs_and_scores():
+    # the weighted scorer reads beta and |v|, fp32 [48 GDN layers][32768][48 heads] each, once
+    # (0.604 GB) and writes 64 x 32768 fp32 scores, which the select reads once (16.8 MB)
+    cfg = configs.GLOBAL
+    counts = torch.full((64,), 256 + 8128, dtype=torch.int32)
+    st = types.SimpleNamespace(cfg=cfg, kept_count=counts, n=cfg.n,
+                               kv_bytes_moved=lambda: credited(cfg, counts))
+    b = rounds.RoundState.algorithmic_bytes(st)
+    assert b["inputs"] == 2 * 48 * 32768 * 48 * 4 == 603_979_776
+    assert b["scores"] == 64 * 32768 * 4 * 2
+    assert b["inputs"] + b["scores"] // 2 == 612_368_384  # the scorer's own bytes
+    assert b["kv"] == 1_098_907_648
+    # KeyDiff reads every key of the batch once (36,864 lists x 1088 x 128 bf16 = 10.27 GB)
+    cfg = configs.KEYDIFF
+    st = types.SimpleNamespace(cfg=cfg, n=cfg.n, kv_bytes_moved=lambda: credited(cfg))
+    b = rounds.RoundState.algorithmic_bytes(st)
+    assert b["inputs"] == 36_864 * 1088 * 128 * 2 == 10_267_656_192
+    assert b["inputs"] + b["scores"] // 2 == 10_428_088_320  # keys read + scores written
